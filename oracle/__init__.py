@@ -1,0 +1,6 @@
+"""CPU oracle for the fused attention forward (test infrastructure only).
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+never by the GPU library or its Python binding.
+"""
+from .attention import admitted, attention, kv_head_of, modified_scores, pair_count  # noqa: F401

@@ -1,0 +1,151 @@
+"""Oracle: plain, slow, fp64 CPU attention forward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The GPU library never calls it and
+shares no code with it.
+
+What it computes. The fused, tiled method reorganises where the work happens
+but makes "no approximations" and changes no result (Neuron FA4 explainer,
+"Enter Tri Dao and FlashAttention"; "zero loss in accuracy" in its TL;DR). So
+the oracle is the unfused definition of attention written out, comparing every
+query with every key (same page, "What Is Attention, and Why Is It
+Expensive?"), with the score modification and the mask that FlexAttention lets a
+user attach to a (query index, key index) pair applied literally (NextVector
+FlexAttention article, body: a function of q_idx and k_idx modifies the score;
+PyTorch FlexAttention FA4-backend post: "score/mask modifications"):
+
+    s[q, j]  = scale * <Q[b, h, q, :], K[b, kvh(h), j, :]>
+    s'[q, j] = score_mod(s[q, j], b, h, q, j)
+    admitted = { j : mask_mod(b, h, q, j) }
+    O[q]     = sum_{j admitted} exp(s'[q, j]) V[b, kvh(h), j, :] / sum_{j admitted} exp(s'[q, j])
+    LSE[q]   = log sum_{j admitted} exp(s'[q, j])
+
+with a row whose admitted set is empty defined as O = 0, LSE = -inf.
+
+The whole score row is materialised in fp64 (the very N x N matrix the fused
+method keeps out of HBM: NextVector article, "Executive Key Takeaways"), the
+softmax is taken with the row maximum subtracted once (an exact identity, used
+only to keep exp() finite), and nothing is blocked, fused or reordered.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * the scale multiplies the raw dot product before the score modification;
+  * mask and modification see (b, h, q_idx, k_idx); a masked score is -inf after
+    the modification, so the mask always wins;
+  * causal is q_idx >= k_idx, the sliding window is q_idx - k_idx < window, and
+    documents admit a pair iff both positions carry the same document label;
+    several masks compose by AND;
+  * ALiBi adds slope[h] * (k_idx - q_idx) to the scaled score; soft-capping
+    replaces it by c * tanh(s / c);
+  * grouped heads: query head h reads key/value head h // (H // Hkv).
+
+Every function here is pinned by tests that do not reuse it (closed forms,
+invariants, a scalar brute force and a library routine).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["kv_head_of", "admitted", "modified_scores", "attention", "pair_count"]
+
+
+def kv_head_of(h: int, H: int, Hkv: int) -> int:
+    """Grouped heads: H // Hkv consecutive query heads share one K/V head."""
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    return h // (H // Hkv)
+
+
+def admitted(q_idx, k_idx, *, causal: bool = False, window: int | None = None,
+             doc_row=None) -> np.ndarray:
+    """The mask: True where query q_idx may attend to key k_idx.
+
+    `q_idx`, `k_idx` broadcast against each other (e.g. a column and a row of
+    indices); `doc_row` is the document label of every position of one batch
+    row (or None).
+    """
+    q_idx = np.asarray(q_idx, dtype=np.int64)
+    k_idx = np.asarray(k_idx, dtype=np.int64)
+    keep = np.ones(np.broadcast_shapes(q_idx.shape, k_idx.shape), dtype=bool)
+    if causal:
+        keep &= q_idx >= k_idx
+    if window is not None and window > 0:
+        keep &= (q_idx - k_idx) < window
+    if doc_row is not None:
+        doc_row = np.asarray(doc_row)
+        keep &= doc_row[q_idx] == doc_row[k_idx]
+    return keep
+
+
+def modified_scores(s: np.ndarray, h: int, q_idx, k_idx, *, alibi_slopes=None,
+                    softcap: float | None = None) -> np.ndarray:
+    """The score modification applied to already-scaled scores `s`."""
+    if alibi_slopes is not None and softcap is not None:
+        raise ValueError("one score modification at a time")
+    if alibi_slopes is not None:
+        slope = float(np.asarray(alibi_slopes, dtype=np.float64)[h])
+        dist = np.asarray(k_idx, dtype=np.float64) - np.asarray(q_idx, dtype=np.float64)
+        return s + slope * dist
+    if softcap is not None:
+        c = float(softcap)
+        return c * np.tanh(s / c)
+    return s
+
+
+def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None = None,
+              doc_ids=None, alibi_slopes=None, softcap: float | None = None, rows=None,
+              heads=None):
+    """fp64 attention forward, the definition written out.
+
+    q: [B, H, Sq, D], k and v: [B, Hkv, Skv, D] (any real dtype; computed in
+    float64). doc_ids: [B, >= max(Sq, Skv)] document label per position, or
+    None. rows: optional 1-D array of query indices to evaluate (for sampled
+    checks at full size); heads: optional list of query heads to evaluate.
+
+    Returns (O, LSE): O [B, H, len(rows), D] float64 and LSE [B, H, len(rows)]
+    float64 (natural log). Heads not in `heads` are left as NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if (Bk, Dk) != (B, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = range(H) if heads is None else heads
+    keys = np.arange(Skv)
+
+    O = np.full((B, H, rows.size, D), np.nan)
+    LSE = np.full((B, H, rows.size), np.nan)
+    for b in range(B):
+        doc_row = None if doc_ids is None else np.asarray(doc_ids)[b]
+        keep = admitted(rows[:, None], keys[None, :], causal=causal, window=window,
+                        doc_row=doc_row)
+        any_kept = keep.any(axis=1)
+        for h in heads:
+            kh = kv_head_of(h, H, Hkv)
+            s = (q[b, h, rows, :] @ k[b, kh].T) * scale
+            s = modified_scores(s, h, rows[:, None], keys[None, :],
+                                alibi_slopes=alibi_slopes, softcap=softcap)
+            s = np.where(keep, s, -np.inf)
+            m = np.where(any_kept, s.max(axis=1, initial=-np.inf), 0.0)
+            w = np.exp(s - m[:, None])          # exp(-inf) = 0 for masked keys
+            l = w.sum(axis=1)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                o = (w @ v[b, kh]) / l[:, None]
+                lse = m + np.log(l)
+            O[b, h] = np.where(any_kept[:, None], o, 0.0)
+            LSE[b, h] = np.where(any_kept, lse, -np.inf)
+    return O, LSE
+
+
+def pair_count(Sq: int, Skv: int, *, causal: bool = False, window: int | None = None,
+               doc_row=None) -> int:
+    """Number of admitted (query, key) pairs, counted element by element."""
+    total = 0
+    keys = np.arange(Skv)
+    for lo in range(0, Sq, 1024):
+        r = np.arange(lo, min(Sq, lo + 1024))
+        total += int(admitted(r[:, None], keys[None, :], causal=causal,
+                              window=window, doc_row=doc_row).sum())
+    return total

@@ -1,0 +1,48 @@
+"""Scalar pure-Python attention: a second, independent reading of the
+definition, used only to check the vectorised oracle on tiny shapes.
+
+Every score is a Python float computed with explicit loops and math.exp /
+math.tanh; nothing here is shared with the oracle.
+"""
+import math
+
+
+def brute_attention(q, k, v, scale, *, causal=False, window=None, doc_ids=None,
+                    alibi_slopes=None, softcap=None):
+    """q: nested lists [B][H][Sq][D]; k, v: [B][Hkv][Skv][D]. Returns nested
+    lists O [B][H][Sq][D] and LSE [B][H][Sq]."""
+    B, H, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, Skv = len(k[0]), len(k[0][0])
+    O = [[[[0.0] * D for _ in range(Sq)] for _ in range(H)] for _ in range(B)]
+    L = [[[0.0] * Sq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            g = h * Hkv // H          # query heads split into Hkv equal consecutive groups
+            for i in range(Sq):
+                kept = []
+                for j in range(Skv):
+                    if causal and j > i:
+                        continue
+                    if window and i - j >= window:
+                        continue
+                    if doc_ids is not None and doc_ids[b][i] != doc_ids[b][j]:
+                        continue
+                    dot = 0.0
+                    for d in range(D):
+                        dot += q[b][h][i][d] * k[b][g][j][d]
+                    s = dot * scale
+                    if alibi_slopes is not None:
+                        s = s + alibi_slopes[h] * (j - i)
+                    if softcap is not None:
+                        s = softcap * math.tanh(s / softcap)
+                    kept.append((j, s))
+                if not kept:
+                    L[b][h][i] = -math.inf
+                    continue
+                top = max(s for _, s in kept)
+                ws = [(j, math.exp(s - top)) for j, s in kept]
+                tot = sum(w for _, w in ws)
+                for d in range(D):
+                    O[b][h][i][d] = sum(w * v[b][g][j][d] for j, w in ws) / tot
+                L[b][h][i] = top + math.log(tot)
+    return O, L
