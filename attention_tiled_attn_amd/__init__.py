@@ -1,0 +1,136 @@
+"""Fused, tiled attention forward for AMD MI355X (gfx950).
+
+The computation runs entirely in the HIP kernels of libflexattn.so; this
+package only marshals arguments. `flexattn_*` mirror the C ABI of
+include/flexattn.h one to one. `attention()` and `build_block_mask()` are
+conveniences that allocate outputs with torch and call those entry points.
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import (  # noqa: F401
+    BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
+    MOD_SOFTCAP, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
+    flexattn_build_block_mask, flexattn_fwd, flexattn_last_error, flexattn_strerror,
+    flexattn_version, lib,
+)
+
+__all__ = [
+    "flexattn_fwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
+    "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
+    "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError",
+]
+
+_DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
+
+
+@dataclass
+class Variant:
+    """A mask_mod / score_mod selection with its parameters (device tensors)."""
+
+    causal: bool = False
+    window: int = 0                       # > 0: keep keys with q - k < window
+    doc_ids: torch.Tensor | None = None   # int32 [B, >= max(Sq, Skv)] on the device
+    alibi_slopes: torch.Tensor | None = None  # float32 [H] on the device
+    softcap: float | None = None
+
+    @property
+    def mask_kind(self) -> int:
+        return mask_kind_of(self.causal, self.window, self.doc_ids is not None)
+
+    @property
+    def mod_kind(self) -> int:
+        if self.alibi_slopes is not None and self.softcap is not None:
+            raise ValueError("one score modification at a time")
+        if self.alibi_slopes is not None:
+            return MOD_ALIBI
+        if self.softcap is not None:
+            return MOD_SOFTCAP
+        return MOD_NONE
+
+
+def mask_kind_of(causal: bool, window: int, documents: bool) -> int:
+    return ((MASK_CAUSAL if causal else 0) | (MASK_WINDOW if window and window > 0 else 0)
+            | (MASK_DOCUMENT if documents else 0))
+
+
+def make_params(var: Variant, dtype: torch.dtype) -> Params:
+    p = Params()
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported element type {dtype}")
+    p.dtype = _DTYPES[dtype]
+    p.window = int(var.window or 0)
+    p.softcap = float(var.softcap) if var.softcap is not None else 0.0
+    p.alibi_slopes = var.alibi_slopes.data_ptr() if var.alibi_slopes is not None else None
+    if var.doc_ids is not None:
+        if var.doc_ids.dtype != torch.int32 or not var.doc_ids.is_contiguous():
+            raise TypeError("doc_ids must be a contiguous int32 tensor")
+        p.doc_ids = var.doc_ids.data_ptr()
+        p.doc_stride = int(var.doc_ids.shape[-1])
+    return p
+
+
+@dataclass
+class BuiltBlockMask:
+    """A block mask and the device buffer that holds its lists."""
+
+    struct: BlockMask
+    buf: torch.Tensor
+
+    def counts(self) -> torch.Tensor:
+        s = self.struct
+        return self.buf[: s.num_b * s.nq].view(s.num_b, s.nq)
+
+    def lists(self) -> torch.Tensor:
+        s = self.struct
+        return self.buf[s.num_b * s.nq:].view(s.num_b, s.nq, s.nk)
+
+
+def build_block_mask(var: Variant, B: int, Sq: int, Skv: int, device=None,
+                     stream=None) -> BuiltBlockMask:
+    """Allocate the list buffer and enqueue flexattn_build_block_mask."""
+    mk = var.mask_kind
+    nbytes = flexattn_block_mask_bytes(B, Sq, Skv, mk)
+    if nbytes == 0:
+        raise ValueError("invalid sizes or mask kind for a block mask")
+    device = device or (var.doc_ids.device if var.doc_ids is not None else torch.device("cuda"))
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+    out = BlockMask()
+    flexattn_build_block_mask(mk, make_params(var, torch.bfloat16), B, Sq, Skv, buf, nbytes, out,
+                              stream)
+    return BuiltBlockMask(out, buf)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | None = None, *,
+              scale: float | None = None, block_mask: BuiltBlockMask | None | str = "auto",
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+              with_lse: bool = True, stream=None):
+    """O (and LSE) of the attention forward for [B, H, S, D] tensors.
+
+    block_mask: "auto" builds one for the variant; None visits every key tile
+    with the per-element mask; or a BuiltBlockMask from build_block_mask().
+    """
+    var = var or Variant()
+    B, H, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise TypeError("q, k, v must be contiguous device tensors of one dtype")
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if isinstance(block_mask, str):
+        block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
+    flexattn_fwd(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, var.mask_kind, var.mod_kind,
+                 make_params(var, q.dtype), block_mask.struct if block_mask is not None else None,
+                 stream)
+    return out, lse

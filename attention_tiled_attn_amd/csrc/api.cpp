@@ -1,0 +1,191 @@
+// api.cpp - the C ABI declared in include/flexattn.h: argument validation
+// (pure host code, done before any HIP call), dispatch, error reporting.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/flexattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
+                static_cast<int>(e));
+  return FLEXATTN_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0};
+
+// Checks shared by the forward pass and the block-mask builder.
+int check_mask_args(int mask_kind, const flexattn_params* prm, int B, int Sq, int Skv) {
+  if (B < 1 || Sq < 1 || Skv < 1) return FLEXATTN_ERR_SHAPE;
+  if (mask_kind < 0 || mask_kind > 7) return FLEXATTN_ERR_UNSUPPORTED;
+  if ((mask_kind & FLEXATTN_MASK_WINDOW) && prm->window < 1) return FLEXATTN_ERR_ARG;
+  if (mask_kind & FLEXATTN_MASK_DOCUMENT) {
+    if (!prm->doc_ids) return FLEXATTN_ERR_NULLPTR;
+    if (!aligned(prm->doc_ids, 4)) return FLEXATTN_ERR_ALIGN;
+    if (prm->doc_stride < (Sq > Skv ? Sq : Skv)) return FLEXATTN_ERR_ARG;
+    if (static_cast<long long>(B) * prm->doc_stride > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+  }
+  return FLEXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flexattn_version(void) { return FLEXATTN_VERSION; }
+
+const char* flexattn_strerror(int status) {
+  switch (status) {
+    case FLEXATTN_OK: return "success";
+    case FLEXATTN_ERR_NULLPTR: return "a required pointer is NULL";
+    case FLEXATTN_ERR_SHAPE: return "invalid shape (sizes must be >= 1 and H a multiple of Hkv)";
+    case FLEXATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype, mask kind or mod kind";
+    case FLEXATTN_ERR_ALIGN: return "misaligned pointer (Q/K/V/O need 16 bytes, LSE and params 4)";
+    case FLEXATTN_ERR_BLOCKMASK: return "block mask does not match this call";
+    case FLEXATTN_ERR_OVERFLOW: return "sizes exceed the 32-bit index range";
+    case FLEXATTN_ERR_HIP: return "HIP runtime error";
+    case FLEXATTN_ERR_ARG: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+const char* flexattn_last_error(void) { return g_last_error; }
+
+size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind) {
+  if (B < 1 || Sq < 1 || Skv < 1 || mask_kind < 0 || mask_kind > 7) return 0;
+  const size_t nb = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? static_cast<size_t>(B) : 1;
+  const size_t nq = static_cast<size_t>(ceil_div(Sq, FLEXATTN_TILE));
+  const size_t nk = static_cast<size_t>(ceil_div(Skv, FLEXATTN_TILE));
+  return nb * nq * (1 + nk) * sizeof(int);
+}
+
+int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
+                              void* buf, size_t bytes, flexattn_block_mask* out, void* stream) {
+  const flexattn_params* prm = params ? params : &kDefaultParams;
+  if (!buf || !out) return FLEXATTN_ERR_NULLPTR;
+  int st = check_mask_args(mask_kind, prm, B, Sq, Skv);
+  if (st) return st;
+  if (!aligned(buf, 4)) return FLEXATTN_ERR_ALIGN;
+  const size_t need = flexattn_block_mask_bytes(B, Sq, Skv, mask_kind);
+  if (need == 0 || bytes < need) return FLEXATTN_ERR_ARG;
+  const int nb = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? B : 1;
+  const int nq = ceil_div(Sq, FLEXATTN_TILE), nk = ceil_div(Skv, FLEXATTN_TILE);
+  if (static_cast<long long>(nb) * nq * (1LL + nk) > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+
+  int* counts = static_cast<int*>(buf);
+  int* lists = counts + static_cast<size_t>(nb) * nq;
+  fa::MaskLaunch ml{};
+  ml.mask_kind = mask_kind;
+  ml.window = prm->window;
+  ml.doc = prm->doc_ids;
+  ml.doc_stride = prm->doc_stride;
+  ml.B = B;
+  ml.Sq = Sq;
+  ml.Skv = Skv;
+  ml.nq = nq;
+  ml.nk = nk;
+  ml.num_b = nb;
+  ml.kv_count = counts;
+  ml.kv_list = lists;
+  hipError_t e = fa::launch_block_mask(ml, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block-mask launch");
+
+  out->tile_q = FLEXATTN_TILE;
+  out->tile_k = FLEXATTN_TILE;
+  out->nq = nq;
+  out->nk = nk;
+  out->num_b = nb;
+  out->mask_kind = mask_kind;
+  out->Sq = Sq;
+  out->Skv = Skv;
+  out->kv_count = counts;
+  out->kv_list = lists;
+  return FLEXATTN_OK;
+}
+
+int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream) {
+  const flexattn_params* prm = params ? params : &kDefaultParams;
+  if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
+  if (H < 1 || Hkv < 1 || H % Hkv != 0) return FLEXATTN_ERR_SHAPE;
+  int st = check_mask_args(mask_kind, prm, B, Sq, Skv);
+  if (st) return st;
+  if (D != 64 && D != 128) return FLEXATTN_ERR_UNSUPPORTED;
+  if (prm->dtype != FLEXATTN_BF16 && prm->dtype != FLEXATTN_FP32) return FLEXATTN_ERR_UNSUPPORTED;
+  if (mod_kind < FLEXATTN_MOD_NONE || mod_kind > FLEXATTN_MOD_SOFTCAP) return FLEXATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FLEXATTN_ERR_ARG;
+  if (mod_kind == FLEXATTN_MOD_ALIBI) {
+    if (!prm->alibi_slopes) return FLEXATTN_ERR_NULLPTR;
+    if (!aligned(prm->alibi_slopes, 4)) return FLEXATTN_ERR_ALIGN;
+  }
+  if (mod_kind == FLEXATTN_MOD_SOFTCAP && !(prm->softcap > 0.f && std::isfinite(prm->softcap)))
+    return FLEXATTN_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
+
+  // 32-bit limits: in-kernel position arithmetic is int; tensor offsets are size_t.
+  const long long nq = ceil_div(Sq, FLEXATTN_TILE);
+  const long long nk = ceil_div(Skv, FLEXATTN_TILE);
+  if (static_cast<long long>(Sq) + FLEXATTN_TILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
+    return FLEXATTN_ERR_OVERFLOW;
+  if (static_cast<long long>(B) * H * nq + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+
+  if (block_mask) {
+    const flexattn_block_mask* bm = block_mask;
+    if (bm->tile_q != FLEXATTN_TILE || bm->tile_k != FLEXATTN_TILE || bm->nq != nq || bm->nk != nk ||
+        bm->mask_kind != mask_kind || bm->Sq != Sq || bm->Skv != Skv)
+      return FLEXATTN_ERR_BLOCKMASK;
+    const int want_b = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? B : 1;
+    if (bm->num_b != want_b) return FLEXATTN_ERR_BLOCKMASK;
+    if (!bm->kv_count || !bm->kv_list) return FLEXATTN_ERR_BLOCKMASK;
+  }
+
+  fa::FwdLaunch p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = D;
+  p.is_fp32 = prm->dtype == FLEXATTN_FP32;
+  p.mask_kind = mask_kind;
+  p.mod_kind = mod_kind;
+  p.va.c1 = scale * fa::kLog2e;
+  const float cap = mod_kind == FLEXATTN_MOD_SOFTCAP ? prm->softcap : 1.f;
+  p.va.sc_in = 2.f * fa::kLog2e * scale / cap;
+  p.va.sc_out = cap * fa::kLog2e;
+  p.va.window = prm->window;
+  p.va.slopes = prm->alibi_slopes;
+  p.va.doc = prm->doc_ids;
+  p.va.doc_stride = prm->doc_stride;
+  p.kv_count = block_mask ? block_mask->kv_count : nullptr;
+  p.kv_list = block_mask ? block_mask->kv_list : nullptr;
+  p.nq = static_cast<int>(nq);
+  p.nk = static_cast<int>(nk);
+  p.bm_num_b = block_mask ? block_mask->num_b : 1;
+  hipError_t e = fa::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return FLEXATTN_OK;
+}
+
+}  // extern "C"

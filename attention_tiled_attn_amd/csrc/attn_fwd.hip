@@ -1,0 +1,401 @@
+// attn_fwd.hip - fused, tiled attention forward for gfx950 (MI355X, CDNA4).
+//
+// The method: keep the work of attention in on-chip memory instead of writing
+// the score matrix to HBM and reading it back, with no approximation (Neuron FA4
+// explainer, "Enter Tri Dao and FlashAttention"); run the softmax online, one key
+// tile at a time, rescaling the running output when the running maximum grows
+// (same page, "FlashAttention-4: Built for Blackwell", forward-pass fixes); split
+// the work over query tiles (same section, and FlashAttention-2's "better
+// parallelism and work partitioning" in "Enter Tri Dao and FlashAttention").
+//
+// Mapping to CDNA4:
+//  * A workgroup owns one 128-row query tile of one (batch, head): 4 waves of 64
+//    lanes, each wave 32 query rows. Grid ids are remapped so that the query
+//    tiles of one (batch, key/value head) land on the same XCD and share its L2.
+//  * Per 64-key stage each wave computes S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16 (fp32 accumulate). In the accumulator layout a
+//    lane then holds 32 scores of ONE query row, so the row max needs one
+//    permlane32 swap and the running sum stays lane-local until the epilogue.
+//  * O^T += V^T P^T: the S^T accumulators, rounded to bf16, are already the
+//    B operand (P^T) of the second MFMA; V is stored transposed in LDS with the
+//    key order permuted to match, so each A-operand fetch is one 16-byte read.
+//  * K and V^T stages are double-buffered in LDS; the next stage's global loads
+//    are issued before the current stage's math and written to LDS after it.
+//  * Row padding plus an XOR swizzle of 16-byte blocks keep LDS reads free of
+//    bank conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "variants.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kBM = 128;        // query rows per workgroup
+constexpr int kBN = 64;         // keys per pipeline stage
+constexpr int kTile = 128;      // block-mask tile edge
+constexpr int kXcds = 8;
+
+template <int D>
+struct Geo {
+  static constexpr int kStride = D + 8;            // bf16 per K row in LDS
+  static constexpr int vStride = kBN + 8;          // bf16 per V^T row in LDS
+  static constexpr int kElems = kBN * kStride;
+  static constexpr int vElems = D * vStride;
+  static constexpr int stage = kElems + vElems;    // bf16 per buffer
+  static constexpr int kChunks = kBN * D / 8 / kThreads;  // 16B K chunks per thread
+  static constexpr int vCols = kBN * D / (4 * kThreads);  // V columns per thread (4 rows each)
+  static_assert(kChunks >= 1 && vCols >= 2 && (D / vCols) == 16, "tile geometry");
+};
+
+__device__ inline unsigned pack_bf16(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+  return static_cast<unsigned>(__builtin_bit_cast(unsigned short, x)) |
+         (static_cast<unsigned>(__builtin_bit_cast(unsigned short, y)) << 16);
+}
+
+// Exchange with lane ^ 32: the pair returned holds this lane's value and the
+// partner's, in an order that depends on the half; symmetric reductions
+// (max, +) of the two give the 64-lane-pair result on both halves.
+__device__ inline float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Load 8 consecutive elements as bf16x8 (fp32 sources are rounded to nearest even).
+template <bool F32>
+__device__ inline u32x4 load8(const void* base, size_t elem_off) {
+  if constexpr (!F32) {
+    return *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(base) + elem_off);
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem_off);
+    f32x4 a = p[0], b = p[1];
+    u32x4 r;
+    r[0] = pack_bf16(a[0], a[1]);
+    r[1] = pack_bf16(a[2], a[3]);
+    r[2] = pack_bf16(b[0], b[1]);
+    r[3] = pack_bf16(b[2], b[3]);
+    return r;
+  }
+}
+
+// Load N (2 or 4 or 8) consecutive elements as packed bf16 pairs.
+template <bool F32, int N>
+__device__ inline void loadN(const void* base, size_t elem_off, unsigned (&dst)[N / 2]) {
+  if constexpr (N == 8) {
+    u32x4 r = load8<F32>(base, elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = r[i];
+  } else if constexpr (N == 4) {
+    if constexpr (!F32) {
+      u32x2 r = *reinterpret_cast<const u32x2*>(static_cast<const __bf16*>(base) + elem_off);
+      dst[0] = r[0];
+      dst[1] = r[1];
+    } else {
+      f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem_off);
+      dst[0] = pack_bf16(a[0], a[1]);
+      dst[1] = pack_bf16(a[2], a[3]);
+    }
+  }
+}
+
+template <int D, int MOD, bool F32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdLaunch p) {
+  using G = Geo<D>;
+  constexpr int DC = D / 16;          // 16-wide d chunks (QK^T k-steps)
+  constexpr int DB = D / 32;          // 32-wide d blocks of O^T
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * G::stage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;            // lane half
+
+  // ---- workgroup -> (b, h, query tile), XCD-aware and heavy-tiles-first
+  const int nq = (p.Sq + kBM - 1) / kBM;
+  const int total = p.B * p.H * nq;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int wg = blockIdx.x;
+  const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
+  if (lin >= total) return;
+  const int qt = nq - 1 - (lin % nq);
+  const int bh = lin / nq;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int kvh = h / (p.H / p.Hkv);
+
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
+  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
+
+  // ---- this wave's 32 query rows; lane owns row q_row
+  const int q_row = qt * kBM + wave * 32 + l32;
+  const bool q_ok = q_row < p.Sq;
+
+  // Q^T fragments (B operand): 8 consecutive d per lane half per 16-wide chunk
+  bf16x8 qf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (q_ok) r = load8<F32>(p.q, (q_head + q_row) * D + c * 16 + g * 8);
+    qf[c] = __builtin_bit_cast(bf16x8, r);
+  }
+
+  // ---- key-tile schedule
+  const int bm_b = (p.kv_count && p.bm_num_b > 1) ? b : 0;
+  const int* list = p.kv_count ? p.kv_list + (static_cast<size_t>(bm_b) * p.nq + qt) * p.nk : nullptr;
+  const int n_entries = p.kv_count ? p.kv_count[bm_b * p.nq + qt] : p.nk;
+  int n_stages = 2 * n_entries;
+  if (n_entries > 0) {
+    const int last = list ? (list[n_entries - 1] >> 1) : (p.nk - 1);
+    if (last * kTile + kBN >= p.Skv) n_stages -= 1;   // last tile has a single 64-key stage
+  }
+
+  // ---- per-thread global->LDS mapping
+  // K: kChunks 16-byte chunks, row-major; V: rows 4*vr .. 4*vr+3, columns vCols*vc ..
+  const int vc = tid & 15;
+  const int vr = tid >> 4;
+
+  unsigned kreg[G::kChunks][4];
+  unsigned vreg[4][G::vCols / 2];
+
+  auto stage_kv0 = [&](int it, bool& full) -> int {
+    const int e = it >> 1;
+    int kt = e, f = 0;
+    if (list) {
+      const int ent = list[e];
+      kt = ent >> 1;
+      f = ent & 1;
+    }
+    full = f != 0;
+    return kt * kTile + (it & 1) * kBN;
+  };
+
+  auto load_stage = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < G::kChunks; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / (D / 8);
+      const int col = (ci % (D / 8)) * 8;
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (kv0 + row < p.Skv) r = load8<F32>(p.k, (kv_head + kv0 + row) * D + col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kreg[i][j] = r[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kv0 + vr * 4 + i;
+#pragma unroll
+      for (int j = 0; j < G::vCols / 2; ++j) vreg[i][j] = 0u;
+      if (row < p.Skv) loadN<F32, G::vCols>(p.v, (kv_head + row) * D + vc * G::vCols, vreg[i]);
+    }
+  };
+
+  auto store_stage = [&](int buf) {
+    __bf16* ks = smem + buf * G::stage;
+    __bf16* vs = ks + G::kElems;
+#pragma unroll
+    for (int i = 0; i < G::kChunks; ++i) {
+      const int ci = tid + i * kThreads;
+      const int row = ci / (D / 8);
+      const int col = (ci % (D / 8)) * 8;
+      u32x4 r = {kreg[i][0], kreg[i][1], kreg[i][2], kreg[i][3]};
+      *reinterpret_cast<u32x4*>(ks + row * G::kStride + col) = r;
+    }
+    // V^T: keys 4*vr..4*vr+3 of column d go to one 8-byte slot. Within each
+    // 16-key chunk the key groups of 4 are placed in the order 0,2,1,3 so that
+    // the eight keys one lane half needs for an MFMA are contiguous.
+    const int kl = vr * 4;                 // local key (multiple of 4)
+    const int a = (kl >> 2) & 3;
+    const int pos = (kl & ~15) + 4 * (((a & 1) << 1) | (a >> 1));
+    const int blk = pos >> 3, off = pos & 7;
+#pragma unroll
+    for (int c = 0; c < G::vCols; ++c) {
+      const int d = vc * G::vCols + c;
+      const int w = c >> 1, hi = (c & 1) * 16;
+      const unsigned e0 = (vreg[0][w] >> hi) & 0xffffu, e1 = (vreg[1][w] >> hi) & 0xffffu;
+      const unsigned e2 = (vreg[2][w] >> hi) & 0xffffu, e3 = (vreg[3][w] >> hi) & 0xffffu;
+      u32x2 pr = {e0 | (e1 << 16), e2 | (e3 << 16)};
+      const int pblk = blk ^ ((d >> 3) & 7);
+      *reinterpret_cast<u32x2*>(vs + d * G::vStride + pblk * 8 + off) = pr;
+    }
+  };
+
+  // ---- running state: O^T accumulators, row max (log2 units), lane-partial sum
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  using SM = ScoreMod<MOD>;
+  const typename SM::Lane sml = SM::lane(p.va, h, q_row);
+  const int* doc_row = (p.mask_kind & kMaskDocument) ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : nullptr;
+  const int doc_q = (doc_row && q_ok) ? doc_row[q_row] : 0;
+
+  if (n_stages > 0) {
+    bool f;
+    load_stage(stage_kv0(0, f));
+    store_stage(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_stages; ++it) {
+    const int cur = it & 1;
+    bool full;
+    const int kv0 = stage_kv0(it, full);
+    const bool more = it + 1 < n_stages;
+    if (more) {
+      bool f2;
+      load_stage(stage_kv0(it + 1, f2));
+    }
+
+    const __bf16* ks = smem + cur * G::stage;
+    const __bf16* vs = ks + G::kElems;
+
+    // S^T = K Q^T : two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const __bf16* krow = ks + (kb * 32 + l32) * G::kStride + g * 8;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + c * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+
+    // score_mod, mask_mod, running max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float t = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
+        if (!full) {
+          const bool ok = kidx < p.Skv && admit(p.mask_kind, q_row, kidx, p.va.window, doc_row, doc_q);
+          t = ok ? t : -INFINITY;
+        }
+        s[kb][r] = t;
+        mx = fmaxf(mx, t);
+      }
+    }
+    mx = max_pair32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    }
+    m_run = m_new;
+
+    // P = exp2(t - m), rounded to bf16 as the B operand of the second product
+    bf16x8 pf[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int kb = ch >> 1, r0 = (ch & 1) * 8;
+      unsigned w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j] - base);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j + 1] - base);
+        ls += p0 + p1;
+        w[j] = pack_bf16(p0, p1);
+      }
+      u32x4 wv = {w[0], w[1], w[2], w[3]};
+      pf[ch] = __builtin_bit_cast(bf16x8, wv);
+    }
+    l_run += ls;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
+      const __bf16* vrow = vs + d * G::vStride;
+      const int sw = (d >> 3) & 7;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const int blk = (2 * ch + g) ^ sw;
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + blk * 8);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], o[db], 0, 0, 0);
+      }
+    }
+
+    if (more) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, LSE, store
+  const float l_tot = sum_pair32(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (q_ok) {
+    const size_t orow = (q_head + q_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const float x0 = o[db][4 * i] * inv, x1 = o[db][4 * i + 1] * inv;
+        const float x2 = o[db][4 * i + 2] * inv, x3 = o[db][4 * i + 3] * inv;
+        if constexpr (F32) {
+          f32x4 vv = {x0, x1, x2, x3};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d0) = vv;
+        } else {
+          u32x2 vv = {pack_bf16(x0, x1), pack_bf16(x2, x3)};
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.out) + orow + d0) = vv;
+        }
+      }
+    }
+    if (p.lse && g == 0) {
+      p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, int MOD, bool F32>
+hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
+  const int nq = (p.Sq + kBM - 1) / kBM;
+  const long long total = static_cast<long long>(p.B) * p.H * nq;
+  const long long per = (total + kXcds - 1) / kXcds;
+  dim3 grid(static_cast<unsigned>(per * kXcds));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
+  switch (p.mod_kind) {
+    case kModNone: return launch_t<D, kModNone, F32>(p, stream);
+    case kModAlibi: return launch_t<D, kModAlibi, F32>(p, stream);
+    case kModSoftcap: return launch_t<D, kModSoftcap, F32>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream) {
+  if (p.D == 128) return p.is_fp32 ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
+  if (p.D == 64) return p.is_fp32 ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,44 @@
+// launch.h - internal interface between the C ABI (api.cpp) and the HIP kernels.
+// Every launch function assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "variants.h"
+
+namespace fa {
+
+struct FwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;          // may be null
+  int B, H, Hkv, Sq, Skv, D;
+  int is_fp32;         // element type of q/k/v/out
+  int mask_kind;
+  int mod_kind;
+  VariantArgs va;
+  // block mask (kv_count == nullptr: visit every key tile as partial)
+  const int* kv_count;
+  const int* kv_list;
+  int nq, nk, bm_num_b;
+};
+
+hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream);
+
+struct MaskLaunch {
+  int mask_kind;
+  int window;
+  const int* doc;
+  int doc_stride;
+  int B, Sq, Skv;
+  int nq, nk, num_b;
+  int* kv_count;
+  int* kv_list;
+};
+
+hipError_t launch_block_mask(const MaskLaunch& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,92 @@
+// variants.h - score_mod and mask_mod variants of the attention forward, as
+// compile-time functors (device code, gfx950).
+//
+// FlexAttention lets a user attach a function of (q_idx, k_idx) that modifies a
+// score, and mask modifications that drop pairs (NextVector FlexAttention
+// article, body; PyTorch FlexAttention FA4-backend post). The variants named on
+// the pages are sliding window, document packing, ALiBi and soft-capping (Neuron
+// FA4 explainer, "PyTorch Gets the Upgrade Too"; NextVector article, "What
+// Happened?"). Here each is a functor chosen at compile time (score mods) or by a
+// wave-uniform flag word (masks, evaluated only on partial tiles).
+//
+// All score functors return t = s' * log2(e), the modified score in base-2
+// units, because the softmax exponential is evaluated as exp2 (the unit the
+// pages name as the forward-pass wall: Zadouri tweet; Neuron FA4 explainer,
+// "FlashAttention-4: Built for Blackwell").
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum : int { kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 4 };
+enum : int { kModNone = 0, kModAlibi = 1, kModSoftcap = 2 };
+
+// Per-call constants the functors read. Filled on the host.
+struct VariantArgs {
+  float c1;          // scale * log2(e)
+  float sc_in;       // softcap: 2 * log2(e) * scale / cap
+  float sc_out;      // softcap: cap * log2(e)
+  int window;        // sliding window (keys with q - k < window are kept)
+  const float* slopes;  // ALiBi slopes [H]
+  const int* doc;       // document labels [B][doc_stride]
+  int doc_stride;
+};
+
+// ---------------------------------------------------------------- score_mod
+// s: raw dot product q.k accumulated in fp32; q_idx/k_idx: positions.
+template <int MOD>
+struct ScoreMod;
+
+template <>
+struct ScoreMod<kModNone> {
+  struct Lane {};
+  __device__ static Lane lane(const VariantArgs&, int /*h*/, int /*q*/) { return {}; }
+  __device__ static float apply(float s, const VariantArgs& a, const Lane&, int /*dk*/) {
+    return s * a.c1;
+  }
+};
+
+// ALiBi: s' = scale*q.k + slope[h] * (k_idx - q_idx). The per-lane part
+// slope*log2e is prepared once; `dk` is k_idx - q_idx.
+template <>
+struct ScoreMod<kModAlibi> {
+  struct Lane { float sl; };
+  __device__ static Lane lane(const VariantArgs& a, int h, int /*q*/) {
+    return {a.slopes[h] * kLog2e};
+  }
+  __device__ static float apply(float s, const VariantArgs& a, const Lane& L, int dk) {
+    return __builtin_fmaf(s, a.c1, L.sl * static_cast<float>(dk));
+  }
+};
+
+// Soft-capping: s' = cap * tanh(scale*q.k / cap), with
+// tanh(x) = 1 - 2 / (exp(2x) + 1) evaluated through exp2 and a reciprocal;
+// exp2 overflow to +inf gives tanh = 1 and underflow to 0 gives -1.
+template <>
+struct ScoreMod<kModSoftcap> {
+  struct Lane {};
+  __device__ static Lane lane(const VariantArgs&, int, int) { return {}; }
+  __device__ static float apply(float s, const VariantArgs& a, const Lane&, int /*dk*/) {
+    const float e = __builtin_amdgcn_exp2f(s * a.sc_in);
+    const float th = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+    return th * a.sc_out;
+  }
+};
+
+// ---------------------------------------------------------------- mask_mod
+// Per-element predicate for partial tiles: causal q >= k, window q - k < W,
+// document doc[q] == doc[k]; AND-composed by the flag word `kind`.
+// `doc_row` points at this batch row's labels; `doc_q` is doc_row[q].
+__device__ inline bool admit(int kind, int q, int k, int window, const int* doc_row, int doc_q) {
+  bool ok = true;
+  if (kind & kMaskCausal) ok = ok && (q >= k);
+  if (kind & kMaskWindow) ok = ok && (q - k < window);
+  if (kind & kMaskDocument) ok = ok && (doc_row[k] == doc_q);
+  return ok;
+}
+
+}  // namespace fa

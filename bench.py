@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dense] [--no-cpu-baseline]
+
+One step is the whole hot path on one batch: build the block mask for the
+workload's mask, then run the attention forward (both kernels, enqueued on
+torch's current stream). Inputs are seeded synthetic tensors resident in HBM
+before timing starts. The metric is effective TFLOPS counting only admitted
+(unmasked) pairs: 4 * D * pairs * B * H per forward (two products, 2 FLOP per
+multiply-add). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (the published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["attention_tiled_attn_amd/csrc/attn_fwd.hip",
+                  "attention_tiled_attn_amd/csrc/variants.h",
+                  "attention_tiled_attn_amd/csrc/launch.h"]
+
+
+def admitted_pairs(wl, doc_ids) -> int:
+    """Admitted (query, key) pairs per (batch, head), from closed forms: dense
+    S^2, causal S(S+1)/2, documents under causal and window W: per document of
+    length L, L(L+1)/2 if L <= W else W(W+1)/2 + (L - W) W. Returns the total
+    over batch rows (divide by B for one row)."""
+    S = wl.S
+    if wl.documents:
+        import numpy as np
+        tot = 0
+        for b in range(wl.B):
+            lens = np.diff(np.flatnonzero(np.diff(np.r_[-1, doc_ids[b], -2]) != 0))
+            for L in lens.tolist():
+                if not wl.causal:
+                    tot += L * L if not wl.window else _window_noncausal(L, wl.window)
+                elif wl.window and L > wl.window:
+                    W = wl.window
+                    tot += W * (W + 1) // 2 + (L - W) * W
+                else:
+                    tot += L * (L + 1) // 2
+        return tot
+    if wl.causal and wl.window and wl.window < S:
+        W = wl.window
+        return wl.B * (W * (W + 1) // 2 + (S - W) * W)
+    if wl.causal:
+        return wl.B * S * (S + 1) // 2
+    if wl.window:
+        return wl.B * _window_noncausal(S, wl.window)
+    return wl.B * S * S
+
+
+def _window_noncausal(L: int, W: int) -> int:
+    # pairs with q - k < W over an L x L square: all pairs minus those with q - k >= W
+    n = max(L - W, 0)
+    return L * L - n * (n + 1) // 2
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, n_launch_bytes_key="per_launch_bytes"):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get(n_launch_bytes_key)
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """The oracle, as it is, on whole (batch, head) slices of the same workload
+    until the budget is spent; rate in the same unit as the GPU metric."""
+    import numpy as np
+    import oracle
+    from workload import bf16_values
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wl = inp.wl
+    q, k, v = (bf16_values(t) for t in (inp.q[:1], inp.k[:1], inp.v[:1]))
+    kw = dict(causal=wl.causal, window=wl.window or None,
+              doc_ids=None if inp.doc_ids is None else inp.doc_ids[:1],
+              alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
+              softcap=wl.softcap if wl.mod == "softcap" else None)
+    pairs_per_head = admitted_pairs(wl.with_(B=1), None if inp.doc_ids is None else inp.doc_ids[:1])
+    # rows per chunk so that one chunk is a fraction of the budget
+    t0 = time.perf_counter()
+    done_pairs = 0
+    heads_done = 0
+    rows_done = 0
+    chunk = 512
+    h = 0
+    while time.perf_counter() - t0 < budget_s and h < wl.H:
+        for r0 in range(0, wl.Sq, chunk):
+            rows = np.arange(r0, min(wl.Sq, r0 + chunk))
+            oracle.attention(q, k, v, wl.scale, rows=rows, heads=[h], **kw)
+            rows_done += rows.size
+            done_pairs += _pairs_in_rows(wl, rows, None if inp.doc_ids is None else inp.doc_ids[0])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            heads_done += 1
+        h += 1
+    dt = time.perf_counter() - t0
+    tflops = 4.0 * wl.D * done_pairs / dt / 1e12
+    return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows of batch 0 ({heads_done} whole heads of {wl.H}), "
+                      f"{done_pairs} admitted pairs, fp64 numpy, {dt:.1f} s",
+            "pairs_per_head": pairs_per_head}
+
+
+def _pairs_in_rows(wl, rows, doc_row) -> int:
+    import numpy as np
+    import oracle
+    tot = 0
+    keys = np.arange(wl.Skv)
+    for r0 in range(0, rows.size, 256):
+        r = rows[r0:r0 + 256]
+        tot += int(oracle.admitted(r[:, None], keys[None, :], causal=wl.causal,
+                                   window=wl.window or None, doc_row=doc_row).sum())
+    return tot
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; sharding is design-only",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import attention_tiled_attn_amd as fa
+    from workload import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    var = fa.Variant(causal=wl.causal, window=wl.window,
+                     doc_ids=torch.from_numpy(inp.doc_ids).to(dev) if inp.doc_ids is not None else None,
+                     alibi_slopes=torch.from_numpy(inp.slopes).to(dev) if inp.slopes is not None else None,
+                     softcap=wl.softcap if wl.mod == "softcap" else None)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4}), file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv, dev)
+        if ev is not None:
+            ev[0].record(stream)
+        fa.attention(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        return bm
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    pairs = admitted_pairs(wl, inp.doc_ids)            # summed over batch rows
+    flop = 4.0 * wl.D * pairs * wl.H                   # per forward
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kern_avg_ms * 1e-3) / 1e12
+
+    # tile FLOPs: every computed 128x128 tile counts in full
+    bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv, dev)
+    torch.cuda.synchronize()
+    counts = bm.counts().sum().item() * (wl.B if bm.struct.num_b == 1 else 1)
+    tile_flop = 4.0 * wl.D * 128 * 128 * counts * wl.H
+
+    bytes_alg = (q.numel() + k.numel() + v.numel() + out.numel()) * q.element_size() + lse.numel() * 4
+    traffic = traffic_from_profile(wl.name)
+
+    rec = {
+        "metric": "attention fwd effective TFLOPS (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "bf16 (fp32 in/out)",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Hkv": wl.Hkv, "Sq": wl.Sq,
+                   "Skv": wl.Skv, "D": wl.D, "causal": wl.causal, "window": wl.window,
+                   "documents": wl.documents, "mod": wl.mod, "seed": wl.seed},
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "attn_kernel_ms": round(kern_avg_ms, 4),
+        "attn_kernel_ms_min": round(min(kern_ms), 4),
+        "tile_tflops": round(tile_flop / (kern_avg_ms * 1e-3) / 1e12, 2),
+        "admitted_pairs_per_head": pairs // wl.B,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": bytes_alg,
+            "kernel": "attn_fwd_kernel",
+        },
+        "kernel_sha": kernel_sha(),
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * flexattn.h - C ABI of the fused, tiled attention forward for AMD MI355X (gfx950).
+ *
+ * What it computes. For every batch b, query head h and query position q:
+ *
+ *     s[j]   = scale * dot(Q[b,h,q,:], K[b,kvh,j,:])          kvh = h / (H / Hkv)
+ *     s'[j]  = score_mod(s[j], b, h, q, j)
+ *     O[b,h,q,:] = sum_{j : mask_mod(b,h,q,j)} softmax_j(s') V[b,kvh,j,:]
+ *     LSE[b,h,q] = log sum_{j : mask_mod(b,h,q,j)} exp(s'[j])      (natural log)
+ *
+ * A row that admits no key gets O = 0 and LSE = -inf.
+ *
+ * This is softmax attention comparing every query with every key (Neuron FA4
+ * explainer, "What Is Attention, and Why Is It Expensive?"), computed tile by
+ * tile in on-chip memory so that the score matrix is never written to HBM and
+ * with no approximation (same page, "Enter Tri Dao and FlashAttention";
+ * NextVector FlexAttention article, "Executive Key Takeaways"). The score and
+ * mask modifications are the FlexAttention-style variants the pages list
+ * (sliding window, document packing, ALiBi, soft-capping: Neuron FA4
+ * explainer, "PyTorch Gets the Upgrade Too"; NextVector article, "What
+ * Happened?"), selected here by enum and compiled in, rather than generated
+ * at run time (PyTorch FlexAttention FA4-backend post).
+ *
+ * Conventions for every call below:
+ *   - Tensors are caller-owned device memory (e.g. allocated by PyTorch),
+ *     contiguous, row-major in the shapes given. The library allocates
+ *     nothing, keeps no pointer after a call returns and has no mutable
+ *     global state; calls are reentrant.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call returns a negative FLEXATTN_ERR_* code and touches no memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising. A fault inside a kernel
+ *     surfaces at the caller's next synchronisation on that stream.
+ */
+#ifndef FLEXATTN_H
+#define FLEXATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLEXATTN_VERSION 1
+
+/* Tile edge of the block mask, in query rows and in keys. */
+#define FLEXATTN_TILE 128
+
+/* Status codes: 0 on success, negative on failure. */
+enum flexattn_status {
+  FLEXATTN_OK = 0,
+  FLEXATTN_ERR_NULLPTR = -1,     /* a required pointer is NULL                         */
+  FLEXATTN_ERR_SHAPE = -2,       /* B, H, Hkv, Sq, Skv < 1, or H % Hkv != 0            */
+  FLEXATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, mask or mod kind      */
+  FLEXATTN_ERR_ALIGN = -4,       /* Q/K/V/O not 16-byte or LSE/params not 4-byte aligned */
+  FLEXATTN_ERR_BLOCKMASK = -5,   /* block mask does not match the call                 */
+  FLEXATTN_ERR_OVERFLOW = -6,    /* sizes exceed the 32-bit index range                */
+  FLEXATTN_ERR_HIP = -7,         /* a HIP call failed; see flexattn_last_error()       */
+  FLEXATTN_ERR_ARG = -8          /* bad scalar argument (scale, window, softcap, size)  */
+};
+
+/* Element type of Q, K, V and O. LSE is always float32. FP32 inputs are
+ * rounded to bf16 (round-to-nearest-even) when loaded, since both products
+ * run on bf16 matrix cores with float32 accumulation; O is stored as float32. */
+enum flexattn_dtype { FLEXATTN_BF16 = 0, FLEXATTN_FP32 = 1 };
+
+/* mask_mod kinds: bit flags, AND-composed; 0 = every key admitted.
+ *   CAUSAL   : q_idx >= k_idx
+ *   WINDOW   : q_idx - k_idx < params->window       (combine with CAUSAL for a
+ *                                                      causal sliding window)
+ *   DOCUMENT : doc[b][q_idx] == doc[b][k_idx]        (document packing)        */
+enum flexattn_mask_kind {
+  FLEXATTN_MASK_NONE = 0,
+  FLEXATTN_MASK_CAUSAL = 1,
+  FLEXATTN_MASK_WINDOW = 2,
+  FLEXATTN_MASK_DOCUMENT = 4
+};
+
+/* score_mod kinds, applied to the scaled score s = scale * q.k:
+ *   ALIBI   : s + alibi_slopes[h] * (k_idx - q_idx)
+ *   SOFTCAP : softcap * tanh(s / softcap)                                       */
+enum flexattn_mod_kind { FLEXATTN_MOD_NONE = 0, FLEXATTN_MOD_ALIBI = 1, FLEXATTN_MOD_SOFTCAP = 2 };
+
+/* Parameters of the variants. Host struct, read during the call only.
+ * A NULL params pointer means: dtype BF16, no window, no documents, no mods. */
+typedef struct flexattn_params {
+  int dtype;                 /* enum flexattn_dtype                                   */
+  int window;                /* > 0 when the mask has FLEXATTN_MASK_WINDOW            */
+  float softcap;             /* > 0 when mod_kind is FLEXATTN_MOD_SOFTCAP             */
+  const float* alibi_slopes; /* device float32 [H] when mod_kind is FLEXATTN_MOD_ALIBI */
+  const int* doc_ids;        /* device int32 [B][doc_stride] document label per position,
+                                when the mask has FLEXATTN_MASK_DOCUMENT               */
+  int doc_stride;            /* elements per batch row of doc_ids, >= max(Sq, Skv)    */
+} flexattn_params;
+
+/* Block mask: for every query tile of FLEXATTN_TILE rows, the ascending list of
+ * key tiles of FLEXATTN_TILE keys that hold at least one admitted pair, each
+ * flagged full (every pair in range and admitted, so the kernel skips the
+ * per-element mask) or partial. Empty tiles are absent and never computed.
+ * The lists depend on the batch only through DOCUMENT masks (num_b = B then,
+ * else num_b = 1 and row 0 serves every batch); no mask depends on the head.
+ * Filled in by flexattn_build_block_mask; the arrays live in the caller's
+ * buffer. */
+typedef struct flexattn_block_mask {
+  int tile_q, tile_k;   /* both FLEXATTN_TILE                                    */
+  int nq, nk;           /* ceil(Sq / tile_q), ceil(Skv / tile_k)                  */
+  int num_b;            /* 1 or B                                                */
+  int mask_kind;        /* the mask_kind it was built for                        */
+  int Sq, Skv;          /* the sizes it was built for                            */
+  const int* kv_count;  /* device int32 [num_b][nq]: entries in each list        */
+  const int* kv_list;   /* device int32 [num_b][nq][nk]: (kv_tile << 1) | is_full,
+                           ascending; entries past kv_count are unspecified      */
+} flexattn_block_mask;
+
+/* Library version (FLEXATTN_VERSION of the build). */
+int flexattn_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* flexattn_strerror(int status);
+
+/* Detail text of the last FLEXATTN_ERR_HIP returned on this thread ("" if none). */
+const char* flexattn_last_error(void);
+
+/* Bytes of device memory flexattn_build_block_mask needs for these sizes
+ * (int32 counts and lists). Returns 0 for invalid sizes or mask kinds. */
+size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind);
+
+/* Classify every (query tile, key tile) pair of the mask as full, partial or
+ * empty and write the per-query-tile key-tile lists into `buf` (device memory
+ * of at least flexattn_block_mask_bytes(B, Sq, Skv, mask_kind) bytes, 4-byte
+ * aligned). `params` supplies window and doc_ids as for flexattn_fwd (may be
+ * NULL when the mask needs neither). On success fills *out, whose pointers
+ * point into buf, and enqueues the build on `stream`. The classification is
+ * exact: it agrees with the per-element mask on every in-range pair. */
+int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
+                              void* buf, size_t bytes, flexattn_block_mask* out, void* stream);
+
+/* Attention forward.
+ *   q     : device [B][H][Sq][D]    dtype of params (bf16 or float32)
+ *   k, v  : device [B][Hkv][Skv][D] same dtype
+ *   out   : device [B][H][Sq][D]    same dtype; every element is written
+ *   lse   : device float32 [B][H][Sq], or NULL to skip it; every element is written
+ *   D     : 64 or 128; scale: finite (1/sqrt(D) is the usual choice)
+ *   mask_kind, mod_kind, params: the variant (see above)
+ *   block_mask: from flexattn_build_block_mask for the same mask_kind, sizes
+ *           and params, or NULL to visit every key tile with the per-element
+ *           mask (correct for any mask, slower). Results are bitwise equal
+ *           either way.
+ * Query head h reads key/value head h / (H / Hkv). */
+int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXATTN_H */

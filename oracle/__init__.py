@@ -3,4 +3,6 @@
 Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
 never by the GPU library or its Python binding.
 """
-from .attention import admitted, attention, kv_head_of, modified_scores, pair_count  # noqa: F401
+from .attention import (  # noqa: F401
+    admitted, attention, kv_head_of, modified_scores, pair_count, tile_classes,
+)

@@ -45,7 +45,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["kv_head_of", "admitted", "modified_scores", "attention", "pair_count"]
+__all__ = ["kv_head_of", "admitted", "modified_scores", "attention", "pair_count", "tile_classes"]
 
 
 def kv_head_of(h: int, H: int, Hkv: int) -> int:
@@ -149,3 +149,30 @@ def pair_count(Sq: int, Skv: int, *, causal: bool = False, window: int | None = 
         total += int(admitted(r[:, None], keys[None, :], causal=causal,
                               window=window, doc_row=doc_row).sum())
     return total
+
+
+def tile_classes(Sq: int, Skv: int, tile: int, *, causal: bool = False,
+                 window: int | None = None, doc_row=None) -> np.ndarray:
+    """Classify every (query tile, key tile) pair by testing every pair of
+    positions: 0 = empty (no admitted pair), 2 = full (every query row in
+    range admits every key of the tile, and the tile lies inside [0, Skv)),
+    1 = partial otherwise. Query rows past Sq are ignored; keys past Skv never
+    exist, so a tile reaching past Skv is never full.
+
+    Returns int array [ceil(Sq/tile), ceil(Skv/tile)].
+    """
+    nq, nk = -(-Sq // tile), -(-Skv // tile)
+    out = np.zeros((nq, nk), dtype=np.int64)
+    for i in range(nq):
+        rows = np.arange(i * tile, min(Sq, (i + 1) * tile))
+        keep = admitted(rows[:, None], np.arange(Skv)[None, :], causal=causal, window=window,
+                        doc_row=doc_row)
+        for j in range(nk):
+            blk = keep[:, j * tile:(j + 1) * tile]
+            if not blk.any():
+                out[i, j] = 0
+            elif blk.all() and (j + 1) * tile <= Skv:
+                out[i, j] = 2
+            else:
+                out[i, j] = 1
+    return out

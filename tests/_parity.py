@@ -1,0 +1,122 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+run the HIP path through the binding, run the oracle on the values the GPU
+consumed, and compare at the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import attention_tiled_attn_amd as fa
+import oracle
+from workload import Inputs, Workload, bf16_values, make_inputs
+
+# Tolerances: bf16 output against the fp64 oracle.
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_ABS = 1e-3
+
+
+def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
+    wl = inp.wl
+    return fa.Variant(
+        causal=wl.causal,
+        window=wl.window,
+        doc_ids=torch.from_numpy(inp.doc_ids).to(device) if inp.doc_ids is not None else None,
+        alibi_slopes=torch.from_numpy(inp.slopes).to(device) if inp.slopes is not None else None,
+        softcap=wl.softcap if wl.mod == "softcap" else None,
+    )
+
+
+def run_gpu(inp: Inputs, block_mask="auto", var=None, qkv=None):
+    """(O, LSE) device tensors from the HIP path."""
+    q, k, v = qkv if qkv is not None else (t.cuda() for t in (inp.q, inp.k, inp.v))
+    var = var or device_variant(inp)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    fa.attention(q, k, v, var, scale=inp.wl.scale, block_mask=block_mask, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_kwargs(inp: Inputs) -> dict:
+    wl = inp.wl
+    return dict(causal=wl.causal, window=wl.window or None, doc_ids=inp.doc_ids,
+                alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
+                softcap=wl.softcap if wl.mod == "softcap" else None)
+
+
+def run_oracle(inp: Inputs, rows=None, heads=None):
+    """Oracle on exactly the values the GPU consumes (bf16; fp32 inputs are
+    rounded to bf16 on load by the kernel)."""
+    q, k, v = (bf16_values(t) for t in (inp.q, inp.k, inp.v))
+    return oracle.attention(q, k, v, inp.wl.scale, rows=rows, heads=heads, **oracle_kwargs(inp))
+
+
+def compare(O, L, Oref, Lref, what=""):
+    """Assert the GPU result (numpy float64) matches the oracle."""
+    assert not np.isnan(O).any(), f"{what}: NaN in O"
+    assert not np.isnan(L).any(), f"{what}: NaN in LSE"
+    ninf = np.isneginf(Lref)
+    assert np.array_equal(np.isneginf(L), ninf), f"{what}: -inf rows differ"
+    if ninf.any():
+        assert (O[ninf] == 0).all(), f"{what}: fully masked rows must be zero"
+    err = np.abs(O - Oref)
+    lerr = np.abs(L[~ninf] - Lref[~ninf])
+    stats = dict(max_abs=float(err.max(initial=0)), mean_abs=float(err.mean()) if err.size else 0.0,
+                 lse_max=float(lerr.max(initial=0)))
+    assert stats["max_abs"] <= O_MAX_ABS, f"{what}: {stats}"
+    assert stats["mean_abs"] <= O_MEAN_ABS, f"{what}: {stats}"
+    assert stats["lse_max"] <= LSE_ABS, f"{what}: {stats}"
+    return stats
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0) -> np.ndarray:
+    """Query rows for sampled checks at full size: both ends, tile edges, the
+    middle, document boundaries, and seeded random rows."""
+    S = wl.Sq
+    r = {0, 1, 2, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 1}
+    if inp.doc_ids is not None:
+        starts = np.flatnonzero(np.diff(inp.doc_ids[0]) != 0) + 1
+        for s in starts[:6]:
+            r.update({int(s) - 1, int(s), int(s) + 1})
+    r.update(np.random.default_rng(seed).integers(0, S, n_random).tolist())
+    return np.array(sorted(x for x in r if 0 <= x < S))
+
+
+def small(name="t", *, B=1, H=2, Hkv=None, S=200, Sq=None, Skv=None, D=64, dtype="bf16",
+          causal=False, window=0, documents=False, mod="none", softcap=30.0, seed=7,
+          doc_range=(16, 96)) -> Inputs:
+    """Small seeded inputs (Sq and Skv may differ)."""
+    from workload import alibi_slopes, as_element_type, document_ids, document_lengths, draw_qkv
+    Hkv = Hkv or H
+    Sq = Sq or S
+    Skv = Skv or S
+    wl = Workload(name, B=B, H=H, Hkv=Hkv, S=S, D=D, dtype=dtype, causal=causal, window=window,
+                  documents=documents, mod=mod, softcap=softcap, seed=seed, doc_seed=seed,
+                  doc_len_range=doc_range)
+    q, k, v = draw_qkv(B, H, Hkv, Sq, Skv, D, seed)
+    q, k, v = (as_element_type(t, dtype) for t in (q, k, v))
+    doc = None
+    if documents:
+        n = max(Sq, Skv)
+        doc = np.stack([document_ids(document_lengths(n, seed + b, *doc_range)) for b in range(B)])
+    slopes = alibi_slopes(H) if mod == "alibi" else None
+    return Inputs(_SqSkv(wl, Sq, Skv), q, k, v, doc, slopes)
+
+
+class _SqSkv:
+    """A Workload view with Sq != Skv."""
+
+    def __init__(self, wl: Workload, Sq: int, Skv: int):
+        self._wl, self.Sq, self.Skv = wl, Sq, Skv
+
+    def __getattr__(self, name):
+        return getattr(self._wl, name)
+
+
+__all__ = ["run_gpu", "run_oracle", "compare", "to_np", "sample_rows", "small", "make_inputs",
+           "device_variant", "oracle_kwargs"]

@@ -1,0 +1,170 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects invalid calls with the documented status codes before
+touching the GPU (validation is pure host code).
+
+These calls pass fake, never-dereferenced addresses, so every case here must
+fail validation; they are skipped where a GPU is visible, so that a mistake in
+a case can never turn into a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_tiled_attn_amd as fa
+from attention_tiled_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flexattn.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def cpu_only():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only without a GPU")
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libflexattn.so is not built (python -m attention_tiled_attn_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flexattn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_version_and_strings():
+    assert fa.flexattn_version() == 1
+    for code in range(-8, 1):
+        assert fa.flexattn_strerror(code) and fa.flexattn_strerror(code) != "unknown status"
+    assert fa.flexattn_strerror(-99) == "unknown status"
+    assert fa.flexattn_last_error() == ""
+
+
+def test_block_mask_bytes():
+    assert fa.flexattn_block_mask_bytes(2, 256, 384, 1) == 1 * 2 * (1 + 3) * 4
+    assert fa.flexattn_block_mask_bytes(2, 256, 384, 4) == 2 * 2 * (1 + 3) * 4
+    assert fa.flexattn_block_mask_bytes(1, 129, 129, 0) == 2 * 3 * 4
+    for bad in [(0, 128, 128, 0), (1, 0, 128, 0), (1, 128, -1, 0), (1, 128, 128, 8),
+                (1, 128, 128, -1)]:
+        assert fa.flexattn_block_mask_bytes(*bad) == 0
+
+
+A = 0x10000          # 16-byte aligned, never dereferenced
+GOOD = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=2, Hkv=2, Sq=128, Skv=128, D=64, scale=0.125,
+            mask_kind=0, mod_kind=0)
+
+
+def call(**over):
+    a = dict(GOOD)
+    params = over.pop("params", None)
+    bm = over.pop("block_mask", None)
+    a.update(over)
+    return fa.flexattn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Hkv"],
+                           a["Sq"], a["Skv"], a["D"], a["scale"], a["mask_kind"], a["mod_kind"],
+                           params, bm, stream=None, check=False)
+
+
+def P(**kw):
+    p = _lib.Params()
+    p.dtype = kw.get("dtype", _lib.BF16)
+    p.window = kw.get("window", 0)
+    p.softcap = kw.get("softcap", 0.0)
+    p.alibi_slopes = kw.get("alibi_slopes")
+    p.doc_ids = kw.get("doc_ids")
+    p.doc_stride = kw.get("doc_stride", 0)
+    return p
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.ERR_NULLPTR),
+    (dict(k=None), _lib.ERR_NULLPTR),
+    (dict(v=None), _lib.ERR_NULLPTR),
+    (dict(out=None), _lib.ERR_NULLPTR),
+    (dict(B=0), _lib.ERR_SHAPE),
+    (dict(H=0), _lib.ERR_SHAPE),
+    (dict(Hkv=0), _lib.ERR_SHAPE),
+    (dict(H=3, Hkv=2), _lib.ERR_SHAPE),
+    (dict(Sq=0), _lib.ERR_SHAPE),
+    (dict(Skv=-5), _lib.ERR_SHAPE),
+    (dict(D=96), _lib.ERR_UNSUPPORTED),
+    (dict(D=256), _lib.ERR_UNSUPPORTED),
+    (dict(mask_kind=8), _lib.ERR_UNSUPPORTED),
+    (dict(mask_kind=-1), _lib.ERR_UNSUPPORTED),
+    (dict(mod_kind=3), _lib.ERR_UNSUPPORTED),
+    (dict(params=P(dtype=7)), _lib.ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.ERR_ARG),
+    (dict(scale=float("inf")), _lib.ERR_ARG),
+    (dict(q=A + 8), _lib.ERR_ALIGN),
+    (dict(out=A + 2), _lib.ERR_ALIGN),
+    (dict(lse=A + 2), _lib.ERR_ALIGN),
+    (dict(mask_kind=2, params=P(window=0)), _lib.ERR_ARG),
+    (dict(mask_kind=3), _lib.ERR_ARG),                                   # window with no params
+    (dict(mask_kind=4, params=P()), _lib.ERR_NULLPTR),                   # documents, no labels
+    (dict(mask_kind=4, params=P(doc_ids=A, doc_stride=100)), _lib.ERR_ARG),  # stride < S
+    (dict(mask_kind=4, params=P(doc_ids=A + 2, doc_stride=128)), _lib.ERR_ALIGN),
+    (dict(mod_kind=1, params=P()), _lib.ERR_NULLPTR),                    # ALiBi, no slopes
+    (dict(mod_kind=1, params=P(alibi_slopes=A + 1)), _lib.ERR_ALIGN),
+    (dict(mod_kind=2, params=P(softcap=0.0)), _lib.ERR_ARG),
+    (dict(mod_kind=2, params=P(softcap=-3.0)), _lib.ERR_ARG),
+    (dict(mod_kind=2, params=P(softcap=float("inf"))), _lib.ERR_ARG),
+    (dict(Sq=2**31 - 100), _lib.ERR_OVERFLOW),
+    (dict(B=2**20, H=2**12, Hkv=1, Sq=256), _lib.ERR_OVERFLOW),
+])
+def test_fwd_validation(over, code):
+    assert call(**over) == code
+
+
+def bm_struct(**kw):
+    s = _lib.BlockMask()
+    s.tile_q = kw.get("tile_q", 128)
+    s.tile_k = kw.get("tile_k", 128)
+    s.nq = kw.get("nq", 1)
+    s.nk = kw.get("nk", 1)
+    s.num_b = kw.get("num_b", 1)
+    s.mask_kind = kw.get("mask_kind", 0)
+    s.Sq = kw.get("Sq", 128)
+    s.Skv = kw.get("Skv", 128)
+    s.kv_count = kw.get("kv_count", A)
+    s.kv_list = kw.get("kv_list", A)
+    return s
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tile_q=64), dict(tile_k=256), dict(nq=2), dict(nk=3), dict(mask_kind=1), dict(Sq=127),
+    dict(Skv=100), dict(num_b=2), dict(kv_count=None), dict(kv_list=None),
+])
+def test_fwd_rejects_mismatched_block_mask(kw):
+    assert call(block_mask=bm_struct(**kw)) == _lib.ERR_BLOCKMASK
+
+
+def test_build_block_mask_validation():
+    out = _lib.BlockMask()
+
+    def b(mk, params, B, Sq, Skv, buf, nbytes):
+        return fa.flexattn_build_block_mask(mk, params, B, Sq, Skv, buf, nbytes, out, None,
+                                            check=False)
+    need = fa.flexattn_block_mask_bytes(1, 256, 256, 1)
+    assert b(1, None, 1, 256, 256, None, need) == _lib.ERR_NULLPTR
+    assert b(1, None, 1, 256, 256, A + 2, need) == _lib.ERR_ALIGN
+    assert b(1, None, 1, 256, 256, A, need - 4) == _lib.ERR_ARG
+    assert b(9, None, 1, 256, 256, A, need) == _lib.ERR_UNSUPPORTED
+    assert b(1, None, 0, 256, 256, A, need) == _lib.ERR_SHAPE
+    assert b(2, None, 1, 256, 256, A, need) == _lib.ERR_ARG          # window needs params
+    assert b(4, P(), 1, 256, 256, A, need) == _lib.ERR_NULLPTR        # documents need labels
+    L = _lib.lib()
+    assert L.flexattn_build_block_mask(1, None, 1, 256, 256, A, need, None, None) == _lib.ERR_NULLPTR
+
+
+def test_error_raises_with_message():
+    with pytest.raises(fa.FlexAttnError, match="invalid shape"):
+        fa.flexattn_fwd(A, A, A, A, A, 0, 2, 2, 128, 128, 64, 0.1, 0, 0)

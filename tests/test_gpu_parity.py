@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small shapes are compared element by element over the whole output; the full
+workload sizes are compared on sampled query rows the oracle computes one by
+one. Tolerances: O max-abs 2e-2 and mean-abs 2e-3, LSE 1e-3; rows with no
+admitted key must be O = 0 and LSE = -inf on both sides.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_tiled_attn_amd as fa
+import oracle
+from tests._parity import (compare, device_variant, make_inputs, run_gpu, run_oracle,
+                           sample_rows, small, to_np)
+from workload import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def check_full(inp, block_mask="auto", what=""):
+    say(f"[parity] {what} B={inp.wl.B} H={inp.wl.H} Hkv={inp.wl.Hkv} Sq={inp.wl.Sq} "
+        f"Skv={inp.wl.Skv} D={inp.wl.D} {inp.wl.dtype} causal={inp.wl.causal} "
+        f"window={inp.wl.window} docs={inp.doc_ids is not None} mod={inp.wl.mod}")
+    O, L = run_gpu(inp, block_mask)
+    Oref, Lref = run_oracle(inp)
+    return compare(to_np(O), to_np(L), Oref, Lref, what)
+
+
+# ------------------------------------------------------------------ the tiny workload, whole
+def test_tiny_causal_fp32():
+    check_full(make_inputs(WORKLOADS["tiny_causal"]), what="tiny_causal")
+
+
+# ------------------------------------------------------------------ shapes x variants
+SHAPES = [
+    dict(S=1), dict(S=2), dict(S=3), dict(S=127), dict(S=129), dict(S=200), dict(S=333),
+    dict(S=256, D=128), dict(S=200, D=128), dict(S=300, H=4, Hkv=2), dict(S=260, H=4, Hkv=1, D=128),
+    dict(Sq=100, Skv=300, S=300), dict(Sq=300, Skv=100, S=300), dict(S=190, B=2, H=2),
+]
+VARIANTS = [
+    dict(), dict(causal=True), dict(causal=True, window=50), dict(window=70),
+    dict(documents=True), dict(documents=True, causal=True, window=40),
+    dict(causal=True, mod="alibi"), dict(mod="alibi"), dict(mod="softcap", softcap=5.0),
+    dict(causal=True, mod="softcap", softcap=30.0), dict(documents=True, mod="alibi", causal=True),
+]
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: ",".join(f"{k}={x}" for k, x in v.items()) or "dense")
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: ",".join(f"{k}{x}" for k, x in s.items()))
+def test_small_shapes(shape, var):
+    inp = small(**shape, **var)
+    check_full(inp, what=f"{shape} {var}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_dtypes_and_head_dims(dtype, D):
+    check_full(small(S=257, D=D, dtype=dtype, causal=True, seed=11), what=f"{dtype} D{D}")
+
+
+# ------------------------------------------------------------------ GPU-side invariants
+def test_null_block_mask_is_bitwise_equal():
+    for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict()):
+        inp = small(S=520, D=128, **var)
+        O1, L1 = run_gpu(inp, block_mask="auto")
+        O2, L2 = run_gpu(inp, block_mask=None)
+        assert torch.equal(O1, O2) and torch.equal(L1, L2), var
+
+
+def test_repeat_runs_are_bitwise_equal():
+    inp = small(S=700, D=128, causal=True, mod="alibi", H=4, Hkv=2)
+    O1, L1 = run_gpu(inp)
+    O2, L2 = run_gpu(inp)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    inp = small(S=384, D=128, H=8, Hkv=2, causal=True)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    O1, L1 = run_gpu(inp, qkv=(q, k, v))
+    rep = 4
+    k2 = k.repeat_interleave(rep, dim=1).contiguous()
+    v2 = v.repeat_interleave(rep, dim=1).contiguous()
+    var = device_variant(inp)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa.attention(q, k2, v2, var, scale=inp.wl.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, out) and torch.equal(L1, lse)
+
+
+def test_fully_masked_rows():
+    """Queries past Skv whose document has no key at all: O = 0, LSE = -inf."""
+    inp = small(Sq=400, Skv=150, S=400, documents=True, causal=True, doc_range=(40, 90))
+    O, L = run_gpu(inp)
+    Oref, Lref = run_oracle(inp)
+    assert np.isneginf(Lref).any()
+    compare(to_np(O), to_np(L), Oref, Lref, "fully masked rows")
+
+
+def test_lse_optional():
+    inp = small(S=300, causal=True)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    out, lse = fa.attention(q, k, v, fa.Variant(causal=True), scale=inp.wl.scale, with_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    Oref, _ = run_oracle(inp)
+    err = np.abs(to_np(out) - Oref)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_split_kv_merge_identity():
+    """Attention over two key halves, merged by their LSEs, equals attention
+    over all keys (the identity a sharded-over-keys run would use)."""
+    inp = small(S=512, D=128, H=2, seed=21)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    var = fa.Variant()
+    O, L = fa.attention(q, k, v, var, scale=inp.wl.scale)
+    n = 200
+    O1, L1 = fa.attention(q, k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), var, scale=inp.wl.scale)
+    O2, L2 = fa.attention(q, k[:, :, n:].contiguous(), v[:, :, n:].contiguous(), var, scale=inp.wl.scale)
+    Lm = torch.logaddexp(L1, L2)
+    Om = torch.exp(L1 - Lm)[..., None] * O1.float() + torch.exp(L2 - Lm)[..., None] * O2.float()
+    torch.cuda.synchronize()
+    assert (Lm - L).abs().max().item() < 1e-4
+    assert (Om - O.float()).abs().max().item() < 2e-2
+
+
+# ------------------------------------------------------------------ block-mask builder
+@pytest.mark.parametrize("case", [
+    dict(S=1000, causal=True), dict(S=1000, causal=True, window=300), dict(S=777, window=200),
+    dict(S=1300, documents=True), dict(S=1300, documents=True, causal=True, window=256),
+    dict(Sq=500, Skv=900, S=900, causal=True), dict(S=640),
+])
+def test_block_mask_matches_tile_classes(case):
+    inp = small(**case, doc_range=(50, 400))
+    wl = inp.wl
+    var = device_variant(inp)
+    bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv)
+    torch.cuda.synchronize()
+    counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
+    for b in range(counts.shape[0]):
+        ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
+                                  doc_row=None if inp.doc_ids is None else inp.doc_ids[b])
+        for qt in range(ref.shape[0]):
+            want = [(j << 1) | (1 if ref[qt, j] == 2 else 0) for j in range(ref.shape[1]) if ref[qt, j]]
+            got = lists[b, qt, :counts[b, qt]].tolist()
+            assert got == want, (b, qt)
+
+
+def test_block_mask_document_workload_full_size():
+    inp = make_inputs(WORKLOADS["doc_swa"])
+    wl = inp.wl
+    bm = fa.build_block_mask(device_variant(inp), wl.B, wl.Sq, wl.Skv)
+    torch.cuda.synchronize()
+    counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
+    ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=True, window=wl.window, doc_row=inp.doc_ids[0])
+    n_full = n_part = 0
+    for qt in range(ref.shape[0]):
+        want = [(j << 1) | (1 if ref[qt, j] == 2 else 0) for j in range(ref.shape[1]) if ref[qt, j]]
+        assert lists[0, qt, :counts[0, qt]].tolist() == want
+        n_full += int((ref[qt] == 2).sum())
+        n_part += int((ref[qt] == 1).sum())
+    say(f"[blockmask] doc_swa: {n_full} full + {n_part} partial tiles of {ref.size}")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+@pytest.mark.parametrize("name", ["dense", "causal_gqa", "doc_swa", "alibi_d64", "alibi_d128",
+                                  "softcap_d64", "softcap_d128"])
+def test_full_size_sampled(name):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    say(f"[parity] full-size {name}")
+    O, L = run_gpu(inp)
+    rows = sample_rows(wl, inp)
+    heads = sorted({0, wl.H // 2, wl.H - 1})
+    Oref, Lref = run_oracle(inp, rows=rows, heads=heads)
+    idx = torch.as_tensor(rows, device=O.device)
+    Og, Lg = to_np(O[:, heads][:, :, idx]), to_np(L[:, heads][:, :, idx])
+    stats = compare(Og, Lg, Oref[:, heads], Lref[:, heads], name)
+    say(f"[parity] {name}: {stats}")
+    # every element written (outputs were NaN-filled)
+    assert not torch.isnan(O).any().item() and not torch.isnan(L).any().item()

@@ -1,0 +1,52 @@
+"""Host-side logic that needs no GPU: the benchmark's FLOP accounting and the
+seeded input generators."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+from workload import (WORKLOADS, alibi_slopes, document_ids, document_lengths, draw_qkv,
+                      make_inputs)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(causal=True), dict(causal=True, window=100),
+                                dict(window=90), dict(documents=True, causal=True, window=64),
+                                dict(documents=True), dict(documents=True, window=40)])
+def test_admitted_pairs_closed_forms_match_counting(kw):
+    wl = WORKLOADS["dense"].with_(B=2, H=1, Hkv=1, S=700, D=64, doc_len_range=(30, 250), **kw)
+    inp = make_inputs(wl) if wl.documents else None
+    doc = inp.doc_ids if inp is not None else None
+    want = sum(oracle.pair_count(700, 700, causal=wl.causal, window=wl.window or None,
+                                 doc_row=None if doc is None else doc[b]) for b in range(2))
+    assert bench.admitted_pairs(wl, doc) == want
+
+
+def test_config_pair_counts():
+    c = WORKLOADS["causal_gqa"]
+    assert bench.admitted_pairs(c, None) // c.B == 33_558_528
+    assert bench.admitted_pairs(WORKLOADS["dense"], None) // 4 == 4096 * 4096
+    assert bench.admitted_pairs(WORKLOADS["alibi_d64"], None) == 536_887_296
+
+
+def test_document_lengths_cover_and_range():
+    for seed in range(5):
+        lens = document_lengths(16384, seed)
+        assert sum(lens) == 16384
+        assert all(512 <= L <= 4096 for L in lens[:-1]) and 1 <= lens[-1] <= 4096
+    ids = document_ids([3, 1, 2])
+    assert ids.tolist() == [0, 0, 0, 1, 2, 2] and ids.dtype == np.int32
+
+
+def test_alibi_slopes_geometric():
+    s = alibi_slopes(8)
+    assert s.dtype == np.float32 and np.allclose(s, 2.0 ** (-np.arange(1, 9)))
+
+
+def test_draw_order_and_determinism():
+    q, k, v = draw_qkv(1, 2, 1, 5, 6, 4, seed=3)
+    g = torch.Generator().manual_seed(3)
+    assert torch.equal(q, torch.randn((1, 2, 5, 4), generator=g))
+    assert torch.equal(k, torch.randn((1, 1, 6, 4), generator=g))
+    q2, _, _ = draw_qkv(1, 2, 1, 5, 6, 4, seed=3)
+    assert torch.equal(q, q2)

@@ -304,3 +304,31 @@ def test_mask_predicates_literal():
     assert admitted(qi, ki, causal=True).sum() == 21
     w = admitted(qi, ki, causal=True, window=2)
     assert w[3].tolist() == [False, False, True, True, False, False]   # keys 2 and 3
+
+
+# --------------------------------------------------------------- tile classification
+def test_tile_classes_causal_closed_form():
+    """Causal, S = n tiles exactly: the diagonal tiles are partial, the n(n-1)/2
+    below it full, the rest empty."""
+    from oracle import tile_classes
+    n, T = 6, 16
+    c = tile_classes(n * T, n * T, T, causal=True)
+    assert (np.diag(c) == 1).all()
+    assert (c[np.tril_indices(n, -1)] == 2).all() and (c[np.triu_indices(n, 1)] == 0).all()
+    assert (c == 2).sum() == n * (n - 1) // 2
+
+
+def test_tile_classes_tails_and_window():
+    from oracle import tile_classes
+    # ragged keys: the last key tile is never full
+    c = tile_classes(40, 40, 16)
+    assert c.shape == (3, 3) and (c[:, :2] == 2).all() and (c[:, 2] == 1).all()
+    # causal window of one tile width: two bands of partial tiles, nothing full
+    c = tile_classes(64, 64, 16, causal=True, window=16)
+    for i in range(4):
+        for j in range(4):
+            assert c[i, j] == (1 if j in (i - 1, i) else 0)
+    # documents aligned to tiles: block-diagonal full tiles
+    doc = np.repeat([0, 1], 32)
+    c = tile_classes(64, 64, 16, doc_row=doc)
+    assert (c == np.kron(np.eye(2, dtype=int), np.full((2, 2), 2))).all()
