@@ -128,7 +128,7 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   if (D != 64 && D != 128) return FLEXATTN_ERR_UNSUPPORTED;
   if (prm->dtype != FLEXATTN_BF16 && prm->dtype != FLEXATTN_FP32) return FLEXATTN_ERR_UNSUPPORTED;
   if (mod_kind < FLEXATTN_MOD_NONE || mod_kind > FLEXATTN_MOD_SOFTCAP) return FLEXATTN_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale)) return FLEXATTN_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FLEXATTN_ERR_ARG;
   if (mod_kind == FLEXATTN_MOD_ALIBI) {
     if (!prm->alibi_slopes) return FLEXATTN_ERR_NULLPTR;
     if (!aligned(prm->alibi_slopes, 4)) return FLEXATTN_ERR_ALIGN;
@@ -144,6 +144,10 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   if (static_cast<long long>(Sq) + FLEXATTN_TILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
     return FLEXATTN_ERR_OVERFLOW;
   if (static_cast<long long>(B) * H * nq + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+  // one (batch, head) slice is addressed with 32-bit byte offsets
+  const long long esz = prm->dtype == FLEXATTN_FP32 ? 4 : 2;
+  if ((static_cast<long long>(Sq > Skv ? Sq : Skv) + FLEXATTN_TILE) * D * esz > INT_MAX)
+    return FLEXATTN_ERR_OVERFLOW;
 
   if (block_mask) {
     const flexattn_block_mask* bm = block_mask;

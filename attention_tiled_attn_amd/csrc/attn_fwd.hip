@@ -21,8 +21,18 @@
 //    key order permuted to match, so each A-operand fetch is one 16-byte read.
 //  * K and V^T stages are double-buffered in LDS; the next stage's global loads
 //    are issued before the current stage's math and written to LDS after it.
-//  * Row padding plus an XOR swizzle of 16-byte blocks keep LDS reads free of
-//    bank conflicts.
+//    All global reads are buffer loads whose range is one (batch, head) slice,
+//    so rows past the end read as zero without any branch.
+//  * Conditional rescaling (Neuron FA4 explainer, "FlashAttention-4: Built for
+//    Blackwell", forward-pass fixes): the running max used as the exponent base
+//    is raised only when some row of the wave grows by more than kRescaleLog2;
+//    otherwise the stale base is kept, exponentials stay below 2^kRescaleLog2,
+//    and O and the running sum are not touched. The final O / l and
+//    LSE = base + log2(l) are the same quantities in exact arithmetic.
+//  * LDS rows are padded by 16 bytes (K rows: D+8, V^T rows: 72 bf16). With
+//    gfx950's 64 four-byte banks this makes the 16-byte fragment reads of both
+//    products conflict-free, and the V^T stores conflict-free because the 16
+//    lanes written together hold 16 different key groups of one column.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,6 +53,7 @@ constexpr int kBM = 128;        // query rows per workgroup
 constexpr int kBN = 64;         // keys per pipeline stage
 constexpr int kTile = 128;      // block-mask tile edge
 constexpr int kXcds = 8;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct Geo {
@@ -74,46 +85,58 @@ __device__ inline float sum_pair32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Load 8 consecutive elements as bf16x8 (fp32 sources are rounded to nearest even).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
+// return zero (the hardware range check). 0x00020000 in the last descriptor
+// word selects 32-bit data format, which untyped loads need on gfx9.
+__device__ inline rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 8 consecutive elements at element offset `eo`, as 4 packed bf16 pairs
+// (fp32 sources rounded to nearest even).
 template <bool F32>
-__device__ inline u32x4 load8(const void* base, size_t elem_off) {
+__device__ inline u32x4 buf_load8(rsrc_t r, unsigned eo) {
   if constexpr (!F32) {
-    return *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(base) + elem_off);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, eo * 2u, 0, 0);
   } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem_off);
-    f32x4 a = p[0], b = p[1];
-    u32x4 r;
-    r[0] = pack_bf16(a[0], a[1]);
-    r[1] = pack_bf16(a[2], a[3]);
-    r[2] = pack_bf16(b[0], b[1]);
-    r[3] = pack_bf16(b[2], b[3]);
-    return r;
+    u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, eo * 4u, 0, 0);
+    u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, eo * 4u + 16u, 0, 0);
+    u32x4 o;
+    o[0] = pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    o[1] = pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3]));
+    o[2] = pack_bf16(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    o[3] = pack_bf16(__uint_as_float(b[2]), __uint_as_float(b[3]));
+    return o;
   }
 }
 
-// Load N (2 or 4 or 8) consecutive elements as packed bf16 pairs.
+// N (4 or 8) consecutive elements as N/2 packed bf16 pairs.
 template <bool F32, int N>
-__device__ inline void loadN(const void* base, size_t elem_off, unsigned (&dst)[N / 2]) {
+__device__ inline void buf_loadN(rsrc_t r, unsigned eo, unsigned (&dst)[N / 2]) {
   if constexpr (N == 8) {
-    u32x4 r = load8<F32>(base, elem_off);
+    u32x4 v = buf_load8<F32>(r, eo);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = r[i];
-  } else if constexpr (N == 4) {
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+  } else {
+    static_assert(N == 4, "4 or 8 elements");
     if constexpr (!F32) {
-      u32x2 r = *reinterpret_cast<const u32x2*>(static_cast<const __bf16*>(base) + elem_off);
-      dst[0] = r[0];
-      dst[1] = r[1];
+      u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, eo * 2u, 0, 0);
+      dst[0] = v[0];
+      dst[1] = v[1];
     } else {
-      f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem_off);
-      dst[0] = pack_bf16(a[0], a[1]);
-      dst[1] = pack_bf16(a[2], a[3]);
+      u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, eo * 4u, 0, 0);
+      dst[0] = pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      dst[1] = pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3]));
     }
   }
 }
 
 template <int D, int MOD, bool F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_kernel(FwdLaunch p) {
+void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = Geo<D>;
   constexpr int DC = D / 16;          // 16-wide d chunks (QK^T k-steps)
   constexpr int DB = D / 32;          // 32-wide d blocks of O^T
@@ -141,23 +164,31 @@ void attn_fwd_kernel(FwdLaunch p) {
   const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
   const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
 
+  constexpr unsigned esz = F32 ? 4u : 2u;
+  const char* qbase = static_cast<const char*>(p.q) + q_head * D * esz;
+  const char* kbase = static_cast<const char*>(p.k) + kv_head * D * esz;
+  const char* vbase = static_cast<const char*>(p.v) + kv_head * D * esz;
+  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq) * D * esz);
+  const rsrc_t rk = make_rsrc(kbase, static_cast<unsigned>(p.Skv) * D * esz);
+  const rsrc_t rv = make_rsrc(vbase, static_cast<unsigned>(p.Skv) * D * esz);
+
   // ---- this wave's 32 query rows; lane owns row q_row
   const int q_row = qt * kBM + wave * 32 + l32;
   const bool q_ok = q_row < p.Sq;
 
-  // Q^T fragments (B operand): 8 consecutive d per lane half per 16-wide chunk
+  // Q^T fragments (B operand): 8 consecutive d per lane half per 16-wide chunk;
+  // rows past Sq read as zero
   bf16x8 qf[DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    u32x4 r = {0u, 0u, 0u, 0u};
-    if (q_ok) r = load8<F32>(p.q, (q_head + q_row) * D + c * 16 + g * 8);
-    qf[c] = __builtin_bit_cast(bf16x8, r);
-  }
+  for (int c = 0; c < DC; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load8<F32>(rq, static_cast<unsigned>(q_row) * D + c * 16 + g * 8));
 
   // ---- key-tile schedule
-  const int bm_b = (p.kv_count && p.bm_num_b > 1) ? b : 0;
-  const int* list = p.kv_count ? p.kv_list + (static_cast<size_t>(bm_b) * p.nq + qt) * p.nk : nullptr;
-  const int n_entries = p.kv_count ? p.kv_count[bm_b * p.nq + qt] : p.nk;
+  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
+  // (kv_count / kv_list are separate __restrict__ arguments so that these
+  // wave-uniform reads compile to scalar loads)
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qt) * p.nk : nullptr;
+  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qt] : p.nk;
   int n_stages = 2 * n_entries;
   if (n_entries > 0) {
     const int last = list ? (list[n_entries - 1] >> 1) : (p.nk - 1);
@@ -166,41 +197,36 @@ void attn_fwd_kernel(FwdLaunch p) {
 
   // ---- per-thread global->LDS mapping
   // K: kChunks 16-byte chunks, row-major; V: rows 4*vr .. 4*vr+3, columns vCols*vc ..
-  const int vc = tid & 15;
-  const int vr = tid >> 4;
+  // (consecutive lanes take consecutive key groups so the V^T stores spread
+  // over all banks)
+  const int vr = tid & 15;
+  const int vc = tid >> 4;
 
   unsigned kreg[G::kChunks][4];
   unsigned vreg[4][G::vCols / 2];
 
-  auto stage_kv0 = [&](int it, bool& full) -> int {
-    const int e = it >> 1;
-    int kt = e, f = 0;
-    if (list) {
-      const int ent = list[e];
-      kt = ent >> 1;
-      f = ent & 1;
-    }
-    full = f != 0;
-    return kt * kTile + (it & 1) * kBN;
-  };
+  // Stage it covers keys [kv0, kv0 + 64) of list entry it / 2. Entries are
+  // (key_tile << 1) | full. The entry of stage it + 2 is fetched during stage
+  // it (before that stage's K/V prefetch), so its latency is covered by a
+  // whole stage and no wait is needed when it is used.
+  auto entry_at = [list](int e) -> int { return list ? list[e] : (e << 1); };
+  auto stage_kv0 = [](int it, int ent) -> int { return (ent >> 1) * kTile + (it & 1) * kBN; };
 
+  // keys past Skv read as zero (buffer range check)
   auto load_stage = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < G::kChunks; ++i) {
       const int ci = tid + i * kThreads;
       const int row = ci / (D / 8);
       const int col = (ci % (D / 8)) * 8;
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (kv0 + row < p.Skv) r = load8<F32>(p.k, (kv_head + kv0 + row) * D + col);
+      u32x4 r = buf_load8<F32>(rk, static_cast<unsigned>(kv0 + row) * D + col);
 #pragma unroll
       for (int j = 0; j < 4; ++j) kreg[i][j] = r[j];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = kv0 + vr * 4 + i;
-#pragma unroll
-      for (int j = 0; j < G::vCols / 2; ++j) vreg[i][j] = 0u;
-      if (row < p.Skv) loadN<F32, G::vCols>(p.v, (kv_head + row) * D + vc * G::vCols, vreg[i]);
+      buf_loadN<F32, G::vCols>(rv, static_cast<unsigned>(row) * D + vc * G::vCols, vreg[i]);
     }
   };
 
@@ -221,7 +247,6 @@ void attn_fwd_kernel(FwdLaunch p) {
     const int kl = vr * 4;                 // local key (multiple of 4)
     const int a = (kl >> 2) & 3;
     const int pos = (kl & ~15) + 4 * (((a & 1) << 1) | (a >> 1));
-    const int blk = pos >> 3, off = pos & 7;
 #pragma unroll
     for (int c = 0; c < G::vCols; ++c) {
       const int d = vc * G::vCols + c;
@@ -229,8 +254,7 @@ void attn_fwd_kernel(FwdLaunch p) {
       const unsigned e0 = (vreg[0][w] >> hi) & 0xffffu, e1 = (vreg[1][w] >> hi) & 0xffffu;
       const unsigned e2 = (vreg[2][w] >> hi) & 0xffffu, e3 = (vreg[3][w] >> hi) & 0xffffu;
       u32x2 pr = {e0 | (e1 << 16), e2 | (e3 << 16)};
-      const int pblk = blk ^ ((d >> 3) & 7);
-      *reinterpret_cast<u32x2*>(vs + d * G::vStride + pblk * 8 + off) = pr;
+      *reinterpret_cast<u32x2*>(vs + d * G::vStride + pos) = pr;
     }
   };
 
@@ -246,22 +270,29 @@ void attn_fwd_kernel(FwdLaunch p) {
   const int* doc_row = (p.mask_kind & kMaskDocument) ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : nullptr;
   const int doc_q = (doc_row && q_ok) ? doc_row[q_row] : 0;
 
+  int ent_cur = 0, ent_next = 0;   // entries of stages it and it + 1
   if (n_stages > 0) {
-    bool f;
-    load_stage(stage_kv0(0, f));
+    ent_cur = entry_at(0);
+    ent_next = n_stages > 1 ? entry_at(1 >> 1) : 0;
+    load_stage(stage_kv0(0, ent_cur));
     store_stage(0);
   }
+  // Retire every outstanding load here (Q fragments included). Otherwise the
+  // wait the compiler places before the first in-loop use of the Q fragments
+  // also waits for the next stage's prefetch, which defeats the prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = 0; it < n_stages; ++it) {
     const int cur = it & 1;
-    bool full;
-    const int kv0 = stage_kv0(it, full);
+    const int ent_after = (it + 2 < n_stages) ? entry_at((it + 2) >> 1) : 0;
+    const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
+    const bool full = (ent & 1) != 0;
+    const int kv0 = stage_kv0(it, ent);
     const bool more = it + 1 < n_stages;
-    if (more) {
-      bool f2;
-      load_stage(stage_kv0(it + 1, f2));
-    }
+    if (more) load_stage(stage_kv0(it + 1, __builtin_amdgcn_readfirstlane(ent_next)));
+    ent_cur = ent_next;
+    ent_next = ent_after;
 
     const __bf16* ks = smem + cur * G::stage;
     const __bf16* vs = ks + G::kElems;
@@ -279,34 +310,44 @@ void attn_fwd_kernel(FwdLaunch p) {
       }
     }
 
-    // score_mod, mask_mod, running max
-    float mx = -INFINITY;
+    // score_mod in place, then mask_mod in place on partial tiles only
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float t = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
-        if (!full) {
-          const bool ok = kidx < p.Skv && admit(p.mask_kind, q_row, kidx, p.va.window, doc_row, doc_q);
-          t = ok ? t : -INFINITY;
-        }
-        s[kb][r] = t;
-        mx = fmaxf(mx, t);
+        s[kb][r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
       }
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = kidx < p.Skv && admit(p.mask_kind, q_row, kidx, p.va.window, doc_row, doc_q);
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = max_pair32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float base = (m_new == -INFINITY) ? 0.f : m_new;
-    if (__any(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+    if constexpr (SM::kFoldScale) mx *= p.va.c1;   // raw -> log2 units (c1 > 0)
+
+    // conditional rescale (wave-uniform decision)
+    if (__any(mx > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float base = (m_run == -INFINITY) ? 0.f : m_run;
 
-    // P = exp2(t - m), rounded to bf16 as the B operand of the second product
+    // P = exp2(t - base), rounded to bf16 as the B operand of the second product
     bf16x8 pf[4];
     float ls = 0.f;
 #pragma unroll
@@ -315,8 +356,14 @@ void attn_fwd_kernel(FwdLaunch p) {
       unsigned w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j] - base);
-        const float p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j + 1] - base);
+        float p0, p1;
+        if constexpr (SM::kFoldScale) {
+          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * j], p.va.c1, -base));
+          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * j + 1], p.va.c1, -base));
+        } else {
+          p0 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j] - base);
+          p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j + 1] - base);
+        }
         ls += p0 + p1;
         w[j] = pack_bf16(p0, p1);
       }
@@ -330,11 +377,9 @@ void attn_fwd_kernel(FwdLaunch p) {
     for (int db = 0; db < DB; ++db) {
       const int d = db * 32 + l32;
       const __bf16* vrow = vs + d * G::vStride;
-      const int sw = (d >> 3) & 7;
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {
-        const int blk = (2 * ch + g) ^ sw;
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + blk * 8);
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + (2 * ch + g) * 8);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], o[db], 0, 0, 0);
       }
     }
@@ -376,7 +421,8 @@ hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const long long total = static_cast<long long>(p.B) * p.H * nq;
   const long long per = (total + kXcds - 1) / kXcds;
   dim3 grid(static_cast<unsigned>(per * kXcds));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32>), grid, dim3(kThreads), 0, stream, p, p.kv_count,
+                     p.kv_list);
   return hipGetLastError();
 }
 

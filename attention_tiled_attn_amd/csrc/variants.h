@@ -41,19 +41,22 @@ struct VariantArgs {
 template <int MOD>
 struct ScoreMod;
 
+// With no modification the scale is folded into the exponent: scores stay raw,
+// the running max is taken on raw scores and scaled once (scale > 0), and
+// exp2 takes fma(s, c1, -m) directly.
 template <>
 struct ScoreMod<kModNone> {
+  static constexpr bool kFoldScale = true;
   struct Lane {};
   __device__ static Lane lane(const VariantArgs&, int /*h*/, int /*q*/) { return {}; }
-  __device__ static float apply(float s, const VariantArgs& a, const Lane&, int /*dk*/) {
-    return s * a.c1;
-  }
+  __device__ static float apply(float s, const VariantArgs&, const Lane&, int /*dk*/) { return s; }
 };
 
 // ALiBi: s' = scale*q.k + slope[h] * (k_idx - q_idx). The per-lane part
 // slope*log2e is prepared once; `dk` is k_idx - q_idx.
 template <>
 struct ScoreMod<kModAlibi> {
+  static constexpr bool kFoldScale = false;
   struct Lane { float sl; };
   __device__ static Lane lane(const VariantArgs& a, int h, int /*q*/) {
     return {a.slopes[h] * kLog2e};
@@ -68,6 +71,7 @@ struct ScoreMod<kModAlibi> {
 // exp2 overflow to +inf gives tanh = 1 and underflow to 0 gives -1.
 template <>
 struct ScoreMod<kModSoftcap> {
+  static constexpr bool kFoldScale = false;
   struct Lane {};
   __device__ static Lane lane(const VariantArgs&, int, int) { return {}; }
   __device__ static float apply(float s, const VariantArgs& a, const Lane&, int /*dk*/) {

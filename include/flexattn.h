@@ -54,7 +54,8 @@ enum flexattn_status {
   FLEXATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, mask or mod kind      */
   FLEXATTN_ERR_ALIGN = -4,       /* Q/K/V/O not 16-byte or LSE/params not 4-byte aligned */
   FLEXATTN_ERR_BLOCKMASK = -5,   /* block mask does not match the call                 */
-  FLEXATTN_ERR_OVERFLOW = -6,    /* sizes exceed the 32-bit index range                */
+  FLEXATTN_ERR_OVERFLOW = -6,    /* sizes exceed the 32-bit index range (also: one
+                                    (batch, head) slice must stay below 2^31 bytes)    */
   FLEXATTN_ERR_HIP = -7,         /* a HIP call failed; see flexattn_last_error()       */
   FLEXATTN_ERR_ARG = -8          /* bad scalar argument (scale, window, softcap, size)  */
 };
@@ -140,7 +141,7 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
  *   k, v  : device [B][Hkv][Skv][D] same dtype
  *   out   : device [B][H][Sq][D]    same dtype; every element is written
  *   lse   : device float32 [B][H][Sq], or NULL to skip it; every element is written
- *   D     : 64 or 128; scale: finite (1/sqrt(D) is the usual choice)
+ *   D     : 64 or 128; scale: finite and > 0 (1/sqrt(D) is the usual choice)
  *   mask_kind, mod_kind, params: the variant (see above)
  *   block_mask: from flexattn_build_block_mask for the same mask_kind, sizes
  *           and params, or NULL to visit every key tile with the per-element

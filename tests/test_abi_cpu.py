@@ -104,6 +104,9 @@ def P(**kw):
     (dict(params=P(dtype=7)), _lib.ERR_UNSUPPORTED),
     (dict(scale=float("nan")), _lib.ERR_ARG),
     (dict(scale=float("inf")), _lib.ERR_ARG),
+    (dict(scale=0.0), _lib.ERR_ARG),
+    (dict(scale=-0.5), _lib.ERR_ARG),
+    (dict(Sq=5_000_000, D=128, params=P(dtype=_lib.FP32)), _lib.ERR_OVERFLOW),
     (dict(q=A + 8), _lib.ERR_ALIGN),
     (dict(out=A + 2), _lib.ERR_ALIGN),
     (dict(lse=A + 2), _lib.ERR_ALIGN),
