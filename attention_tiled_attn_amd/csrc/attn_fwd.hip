@@ -67,10 +67,13 @@ struct Geo {
   static_assert(kChunks >= 1 && vCols >= 2 && (D / vCols) == 16, "tile geometry");
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ inline unsigned pack_bf16(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-  return static_cast<unsigned>(__builtin_bit_cast(unsigned short, x)) |
-         (static_cast<unsigned>(__builtin_bit_cast(unsigned short, y)) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
 // Exchange with lane ^ 32: the pair returned holds this lane's value and the
@@ -134,7 +137,7 @@ __device__ inline void buf_loadN(rsrc_t r, unsigned eo, unsigned (&dst)[N / 2]) 
   }
 }
 
-template <int D, int MOD, bool F32>
+template <int D, int MOD, bool F32, bool DOCS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = Geo<D>;
@@ -250,10 +253,11 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
 #pragma unroll
     for (int c = 0; c < G::vCols; ++c) {
       const int d = vc * G::vCols + c;
-      const int w = c >> 1, hi = (c & 1) * 16;
-      const unsigned e0 = (vreg[0][w] >> hi) & 0xffffu, e1 = (vreg[1][w] >> hi) & 0xffffu;
-      const unsigned e2 = (vreg[2][w] >> hi) & 0xffffu, e3 = (vreg[3][w] >> hi) & 0xffffu;
-      u32x2 pr = {e0 | (e1 << 16), e2 | (e3 << 16)};
+      // column c of rows r and r+1: low (even c) or high (odd c) halves, one v_perm each
+      const int w = c >> 1;
+      const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 pr = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel),
+                  __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel)};
       *reinterpret_cast<u32x2*>(vs + d * G::vStride + pos) = pr;
     }
   };
@@ -267,8 +271,10 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
 
   using SM = ScoreMod<MOD>;
   const typename SM::Lane sml = SM::lane(p.va, h, q_row);
-  const int* doc_row = (p.mask_kind & kMaskDocument) ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : nullptr;
-  const int doc_q = (doc_row && q_ok) ? doc_row[q_row] : 0;
+  // document labels of this batch row (document-mask kernels only)
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
 
   int ent_cur = 0, ent_next = 0;   // entries of stages it and it + 1
   if (n_stages > 0) {
@@ -310,29 +316,44 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
       }
     }
 
-    // score_mod in place, then mask_mod in place on partial tiles only
+    // Scores as 32 scalars (element 16*kb + r holds key kv0 + 32*kb +
+    // 8*(r/4) + 4*g + r%4); score_mod in place, then mask_mod in place on
+    // partial tiles only.
+    float t[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        s[kb][r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
+        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
       }
     if (!full) {
+      // Branch-free predicate. The four keys 8*i + 4*g + (0..3) of a block are
+      // consecutive, so their document labels come in one 16-byte buffer load
+      // (keys past Skv read as label 0 but are rejected by the range test).
+      const bool causal = p.mask_kind & kMaskCausal;
+      const bool window = p.mask_kind & kMaskWindow;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = kidx < p.Skv && admit(p.mask_kind, q_row, kidx, p.va.window, doc_row, doc_q);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = kv0 + kb * 32 + 8 * i + 4 * g;
+          u32x4 lab = {0u, 0u, 0u, 0u};
+          if constexpr (DOCS) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(k0) * 4u, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kidx = k0 + e;
+            bool ok = kidx < p.Skv;
+            ok &= !causal | (q_row >= kidx);
+            ok &= !window | (q_row - kidx < p.va.window);
+            if constexpr (DOCS) ok &= static_cast<int>(lab[e]) == doc_q;
+            t[kb * 16 + 4 * i + e] = ok ? t[kb * 16 + 4 * i + e] : -INFINITY;
+          }
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, t[i]);
     mx = max_pair32(mx);
     if constexpr (SM::kFoldScale) mx *= p.va.c1;   // raw -> log2 units (c1 > 0)
 
@@ -358,11 +379,11 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
       for (int j = 0; j < 4; ++j) {
         float p0, p1;
         if constexpr (SM::kFoldScale) {
-          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * j], p.va.c1, -base));
-          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * j + 1], p.va.c1, -base));
+          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j], p.va.c1, -base));
+          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j + 1], p.va.c1, -base));
         } else {
-          p0 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j] - base);
-          p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 2 * j + 1] - base);
+          p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j] - base);
+          p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1] - base);
         }
         ls += p0 + p1;
         w[j] = pack_bf16(p0, p1);
@@ -415,32 +436,39 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   }
 }
 
-template <int D, int MOD, bool F32>
+template <int D, int MOD, bool F32, bool DOCS>
 hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const int nq = (p.Sq + kBM - 1) / kBM;
   const long long total = static_cast<long long>(p.B) * p.H * nq;
   const long long per = (total + kXcds - 1) / kXcds;
   dim3 grid(static_cast<unsigned>(per * kXcds));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32>), grid, dim3(kThreads), 0, stream, p, p.kv_count,
-                     p.kv_list);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32, DOCS>), grid, dim3(kThreads), 0, stream, p,
+                     p.kv_count, p.kv_list);
   return hipGetLastError();
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool DOCS>
 hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
   switch (p.mod_kind) {
-    case kModNone: return launch_t<D, kModNone, F32>(p, stream);
-    case kModAlibi: return launch_t<D, kModAlibi, F32>(p, stream);
-    case kModSoftcap: return launch_t<D, kModSoftcap, F32>(p, stream);
+    case kModNone: return launch_t<D, kModNone, F32, DOCS>(p, stream);
+    case kModAlibi: return launch_t<D, kModAlibi, F32, DOCS>(p, stream);
+    case kModSoftcap: return launch_t<D, kModSoftcap, F32, DOCS>(p, stream);
   }
   return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_d(const FwdLaunch& p, hipStream_t stream) {
+  const bool docs = p.mask_kind & kMaskDocument;
+  if (p.is_fp32) return docs ? launch_mod<D, true, true>(p, stream) : launch_mod<D, true, false>(p, stream);
+  return docs ? launch_mod<D, false, true>(p, stream) : launch_mod<D, false, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream) {
-  if (p.D == 128) return p.is_fp32 ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
-  if (p.D == 64) return p.is_fp32 ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
+  if (p.D == 128) return launch_d<128>(p, stream);
+  if (p.D == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 
