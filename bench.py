@@ -74,22 +74,31 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, n_launch_bytes_key="per_launch_bytes"):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary (lines `kernel_sha: ...` and `hbm_bytes_per_launch: ...`), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_sha():
+        for line in f:
+            if ":" in line and not line.startswith(("#", "|", " ")):
+                k, v = line.split(":", 1)
+                fields[k.strip().strip("`-* ")] = v.strip().strip("`")
+    if fields.get("kernel_sha") != kernel_sha():
         return None
-    return rec.get(n_launch_bytes_key)
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
-    """The oracle, as it is, on whole (batch, head) slices of the same workload
-    until the budget is spent; rate in the same unit as the GPU metric."""
+def cpu_baseline(inp, budget_s: float = 15.0):
+    """The oracle, as it is, on whole query rows of the same workload, (batch,
+    head) by (batch, head), until the budget is spent; rate in the unit of the
+    GPU metric (admitted-pair FLOPs per second)."""
     import numpy as np
     import oracle
     from workload import bf16_values
@@ -99,36 +108,36 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     except Exception:
         threads = 1
     wl = inp.wl
-    q, k, v = (bf16_values(t) for t in (inp.q[:1], inp.k[:1], inp.v[:1]))
     kw = dict(causal=wl.causal, window=wl.window or None,
-              doc_ids=None if inp.doc_ids is None else inp.doc_ids[:1],
               alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
               softcap=wl.softcap if wl.mod == "softcap" else None)
-    pairs_per_head = admitted_pairs(wl.with_(B=1), None if inp.doc_ids is None else inp.doc_ids[:1])
-    # rows per chunk so that one chunk is a fraction of the budget
     t0 = time.perf_counter()
-    done_pairs = 0
-    heads_done = 0
-    rows_done = 0
+    done_pairs = rows_done = heads_done = 0
     chunk = 512
-    h = 0
-    while time.perf_counter() - t0 < budget_s and h < wl.H:
-        for r0 in range(0, wl.Sq, chunk):
-            rows = np.arange(r0, min(wl.Sq, r0 + chunk))
-            oracle.attention(q, k, v, wl.scale, rows=rows, heads=[h], **kw)
-            rows_done += rows.size
-            done_pairs += _pairs_in_rows(wl, rows, None if inp.doc_ids is None else inp.doc_ids[0])
+    for b in range(wl.B):
+        q, k, v = (bf16_values(t) for t in (inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1]))
+        doc = None if inp.doc_ids is None else inp.doc_ids[b:b + 1]
+        for h in range(wl.H):
+            whole = True
+            for r0 in range(0, wl.Sq, chunk):
+                rows = np.arange(r0, min(wl.Sq, r0 + chunk))
+                oracle.attention(q, k, v, wl.scale, rows=rows, heads=[h], doc_ids=doc, **kw)
+                rows_done += rows.size
+                done_pairs += _pairs_in_rows(wl, rows, None if doc is None else doc[0])
+                if time.perf_counter() - t0 >= budget_s:
+                    whole = r0 + chunk >= wl.Sq
+                    break
+            heads_done += int(whole)
             if time.perf_counter() - t0 >= budget_s:
                 break
-        else:
-            heads_done += 1
-        h += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
     tflops = 4.0 * wl.D * done_pairs / dt / 1e12
     return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows of batch 0 ({heads_done} whole heads of {wl.H}), "
-                      f"{done_pairs} admitted pairs, fp64 numpy, {dt:.1f} s",
-            "pairs_per_head": pairs_per_head}
+            "sample": f"{rows_done} query rows ({heads_done} whole (batch, head) slices of "
+                      f"{wl.B * wl.H}), {done_pairs} admitted pairs, fp64 numpy oracle, "
+                      f"{dt:.1f} s"}
 
 
 def _pairs_in_rows(wl, rows, doc_row) -> int:
