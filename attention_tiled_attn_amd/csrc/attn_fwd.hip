@@ -303,18 +303,30 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
     const __bf16* ks = smem + cur * G::stage;
     const __bf16* vs = ks + G::kElems;
 
-    // S^T = K Q^T : two 32-key blocks
+    // S^T = K Q^T : two 32-key blocks, the two accumulation chains
+    // interleaved. The fragment reads are kept 4 ahead of the MFMAs that use
+    // them (instruction-group order below), so LDS latency hides behind
+    // ~4 x 32 cycles of matrix work instead of stalling each MFMA.
     f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const __bf16* krow = ks + (kb * 32 + l32) * G::kStride + g * 8;
+    for (int c = 0; c < DC; ++c) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
+      for (int kb = 0; kb < 2; ++kb) {
+        const __bf16* krow = ks + (kb * 32 + l32) * G::kStride + g * 8;
         bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + c * 16);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x0020, 16, 0);   // the prefetch buffer loads
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);    // 4 fragment reads ahead
+#pragma unroll
+    for (int i = 0; i < 2 * DC - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // 1 fragment read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);    // last 4 MFMAs
 
     // Scores as 32 scalars (element 16*kb + r holds key kv0 + 32*kb +
     // 8*(r/4) + 4*g + r%4); score_mod in place, then mask_mod in place on
