@@ -15,13 +15,13 @@ import torch
 
 from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
-    MOD_SOFTCAP, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
+    MOD_SOFTCAP, QTILE, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
     flexattn_build_block_mask, flexattn_fwd, flexattn_last_error, flexattn_strerror,
     flexattn_version, lib,
 )
 
 __all__ = [
-    "flexattn_fwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
+    "QTILE", "TILE", "flexattn_fwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
     "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError",
 ]

@@ -23,6 +23,7 @@ BF16, FP32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOCUMENT = 0, 1, 2, 4
 MOD_NONE, MOD_ALIBI, MOD_SOFTCAP = 0, 1, 2
 TILE = 128
+QTILE = 256
 
 EXPORTS = ("flexattn_version", "flexattn_strerror", "flexattn_last_error",
            "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd")

@@ -67,7 +67,7 @@ const char* flexattn_last_error(void) { return g_last_error; }
 size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind) {
   if (B < 1 || Sq < 1 || Skv < 1 || mask_kind < 0 || mask_kind > 7) return 0;
   const size_t nb = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? static_cast<size_t>(B) : 1;
-  const size_t nq = static_cast<size_t>(ceil_div(Sq, FLEXATTN_TILE));
+  const size_t nq = static_cast<size_t>(ceil_div(Sq, FLEXATTN_QTILE));
   const size_t nk = static_cast<size_t>(ceil_div(Skv, FLEXATTN_TILE));
   return nb * nq * (1 + nk) * sizeof(int);
 }
@@ -82,7 +82,9 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   const size_t need = flexattn_block_mask_bytes(B, Sq, Skv, mask_kind);
   if (need == 0 || bytes < need) return FLEXATTN_ERR_ARG;
   const int nb = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? B : 1;
-  const int nq = ceil_div(Sq, FLEXATTN_TILE), nk = ceil_div(Skv, FLEXATTN_TILE);
+  if (static_cast<long long>(Sq) + FLEXATTN_QTILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
+    return FLEXATTN_ERR_OVERFLOW;
+  const int nq = ceil_div(Sq, FLEXATTN_QTILE), nk = ceil_div(Skv, FLEXATTN_TILE);
   if (static_cast<long long>(nb) * nq * (1LL + nk) > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
 
   int* counts = static_cast<int*>(buf);
@@ -103,7 +105,7 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   hipError_t e = fa::launch_block_mask(ml, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block-mask launch");
 
-  out->tile_q = FLEXATTN_TILE;
+  out->tile_q = FLEXATTN_QTILE;
   out->tile_k = FLEXATTN_TILE;
   out->nq = nq;
   out->nk = nk;
@@ -139,19 +141,20 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
 
   // 32-bit limits: in-kernel position arithmetic is int; tensor offsets are size_t.
-  const long long nq = ceil_div(Sq, FLEXATTN_TILE);
+  const long long nq = ceil_div(Sq, FLEXATTN_QTILE);
   const long long nk = ceil_div(Skv, FLEXATTN_TILE);
-  if (static_cast<long long>(Sq) + FLEXATTN_TILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
+  if (static_cast<long long>(Sq) + FLEXATTN_QTILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
     return FLEXATTN_ERR_OVERFLOW;
-  if (static_cast<long long>(B) * H * nq + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
-  // one (batch, head) slice is addressed with 32-bit byte offsets
+  if (static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_TILE) + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+  // one (batch, head) slice is addressed with 32-bit byte offsets (rows up to
+  // one query tile past the end are read, as zeros)
   const long long esz = prm->dtype == FLEXATTN_FP32 ? 4 : 2;
-  if ((static_cast<long long>(Sq > Skv ? Sq : Skv) + FLEXATTN_TILE) * D * esz > INT_MAX)
+  if ((static_cast<long long>(Sq > Skv ? Sq : Skv) + FLEXATTN_QTILE) * D * esz > INT_MAX)
     return FLEXATTN_ERR_OVERFLOW;
 
   if (block_mask) {
     const flexattn_block_mask* bm = block_mask;
-    if (bm->tile_q != FLEXATTN_TILE || bm->tile_k != FLEXATTN_TILE || bm->nq != nq || bm->nk != nk ||
+    if (bm->tile_q != FLEXATTN_QTILE || bm->tile_k != FLEXATTN_TILE || bm->nq != nq || bm->nk != nk ||
         bm->mask_kind != mask_kind || bm->Sq != Sq || bm->Skv != Skv)
       return FLEXATTN_ERR_BLOCKMASK;
     const int want_b = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? B : 1;

@@ -190,11 +190,13 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
   // (kv_count / kv_list are separate __restrict__ arguments so that these
   // wave-uniform reads compile to scalar loads)
-  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qt) * p.nk : nullptr;
-  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qt] : p.nk;
+  // the lists cover 256-row tiles; this tile is half qt % 2 of tile qt / 2
+  const int qp = qt >> 1, full_bit = 2 * (qt & 1) + 1;
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
+  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
   int n_stages = 2 * n_entries;
   if (n_entries > 0) {
-    const int last = list ? (list[n_entries - 1] >> 1) : (p.nk - 1);
+    const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
     if (last * kTile + kBN >= p.Skv) n_stages -= 1;   // last tile has a single 64-key stage
   }
 
@@ -209,11 +211,13 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   unsigned vreg[4][G::vCols / 2];
 
   // Stage it covers keys [kv0, kv0 + 64) of list entry it / 2. Entries are
-  // (key_tile << 1) | full. The entry of stage it + 2 is fetched during stage
-  // it (before that stage's K/V prefetch), so its latency is covered by a
-  // whole stage and no wait is needed when it is used.
-  auto entry_at = [list](int e) -> int { return list ? list[e] : (e << 1); };
-  auto stage_kv0 = [](int it, int ent) -> int { return (ent >> 1) * kTile + (it & 1) * kBN; };
+  // (key_tile << 4) | status bits of the two 128-row halves; a tile with no
+  // admitted pair in this half is visited as partial (every score masked, so
+  // it adds exactly nothing). The entry of stage it + 2 is fetched during
+  // stage it (before that stage's K/V prefetch), so its latency is covered by
+  // a whole stage and no wait is needed when it is used.
+  auto entry_at = [list](int e) -> int { return list ? list[e] : (e << 4); };
+  auto stage_kv0 = [](int it, int ent) -> int { return (ent >> 4) * kTile + (it & 1) * kBN; };
 
   // keys past Skv read as zero (buffer range check)
   auto load_stage = [&](int kv0) {
@@ -293,7 +297,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
     const int cur = it & 1;
     const int ent_after = (it + 2 < n_stages) ? entry_at((it + 2) >> 1) : 0;
     const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
-    const bool full = (ent & 1) != 0;
+    const bool full = ((ent >> full_bit) & 1) != 0;
     const int kv0 = stage_kv0(it, ent);
     const bool more = it + 1 < n_stages;
     if (more) load_stage(stage_kv0(it + 1, __builtin_amdgcn_readfirstlane(ent_next)));
@@ -479,6 +483,7 @@ hipError_t launch_d(const FwdLaunch& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream) {
+  if (!p.is_fp32 && p.nk <= kPairMaxKeyTiles) return launch_attn_fwd_pp(p, stream);
   if (p.D == 128) return launch_d<128>(p, stream);
   if (p.D == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;

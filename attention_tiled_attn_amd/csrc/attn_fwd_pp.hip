@@ -1,0 +1,495 @@
+// attn_fwd_pp.hip - bf16 attention forward for gfx950 (MI355X, CDNA4): 256-row
+// workgroups of two wave groups that run in ping-pong.
+//
+// What is computed is the fused, tiled forward of attn_fwd.hip (online softmax
+// over key tiles kept on chip, no approximation: Neuron FA4 explainer, "Enter
+// Tri Dao and FlashAttention"). This kernel adds the scheduling idea of the
+// FA4 forward-pass fixes (same page, "FlashAttention-4: Built for Blackwell"):
+// two independent sets of query rows alternate, so that while one set runs its
+// matrix products the other runs its exponentials.
+//
+// Mapping to CDNA4:
+//  * A workgroup of 8 waves owns 256 query rows of one (batch, head). Waves
+//    0-3 (group 0) take rows 0-127, waves 4-7 (group 1) rows 128-255; wave w
+//    and wave w + 4 share a SIMD. Each wave owns 32 rows.
+//  * Time runs in barrier-separated slots. A group alternates a matrix slot,
+//    S^T(t) = K(t) Q^T and O^T += V(t-1)^T P^T(t-1) (32 v_mfma_f32_32x32x16_bf16
+//    per wave at D = 128), with a vector slot: the online softmax of stage t.
+//    Group 1 runs one slot behind group 0, so every SIMD always has one wave
+//    multiplying and one exponentiating. Both groups run the same code; the
+//    offset is one extra barrier at the start (group 1) and at the end
+//    (group 0).
+//  * Both groups read the same K and V stage buffers, so each tile is brought
+//    on chip once per 256 query rows. Group 0 loads K, group 1 loads V, each
+//    in its vector slot and two stages ahead, as direct buffer-to-LDS copies:
+//    no registers, no VALU work, and a ring of three stage buffers.
+//  * V stays row-major in LDS. The A operand of O^T += V^T P^T (32 values of
+//    d, 8 keys per lane) comes from two ds_read_b64_tr_b16 per fragment: each
+//    16-lane group of that instruction turns a 4-key x 16-d block into one
+//    d column of 4 keys per lane.
+//  * K and V rows are unpadded; 16-byte chunks are XOR-permuted by row so that
+//    the fragment reads of both products are free of bank conflicts and every
+//    1 KB copy lands in one contiguous LDS run (lane i writes slot i).
+//  * The S^T accumulator layout gives each lane 32 scores of one query row:
+//    the row max is one permlane32 swap, the running sum stays lane-local, and
+//    the accumulators rounded to bf16 are directly the B operand P^T.
+//  * Conditional rescaling with a threshold of 2^8 (same forward-pass fixes),
+//    scale folded into exp2, XCD-aware and heavy-first tile order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "variants.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kThreads = 512;   // 8 waves: two groups of 4
+constexpr int kBM = 2 * kPairHalf;   // query rows per workgroup
+constexpr int kBN = 64;         // keys per stage
+constexpr int kTile = 128;      // key tile of the block mask
+constexpr int kRing = 3;        // stage buffers for K and for V
+constexpr int kXcds = 8;
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D>
+struct PGeo {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBufBytes = kBN * D * 2;        // one K or V stage
+  static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
+  static constexpr int kDma = kBufBytes / 1024 / 4;    // 1 KB copies per wave of a group
+  static_assert(kDma >= 1 && kBufBytes % 4096 == 0, "stage geometry");
+};
+
+// Chunk permutations (chunk c of row r sits at position c ^ swz(r)). K: the
+// 16 rows read together by one quarter-wave of a b128 fragment read hit 16
+// different chunk positions. V: the 4 rows read together by one half-wave of
+// a transposing b64 read hit disjoint groups of 4 chunks.
+template <int D>
+__device__ inline int kswz(int r) { return (r / (128 / D)) % (D / 8); }
+template <int D>
+__device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+__device__ inline unsigned pack_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ inline float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// The same descriptor as four scalar words, for the copy below: base, stride 0,
+// `bytes` records (offsets at or past it read as zero), 32-bit data format.
+__device__ inline u32x4 make_desc(const void* base, unsigned bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  d[1] = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// 16 bytes per lane from global offset `voff` straight into LDS at
+// lds_base + 16 * lane. Written as one asm block so that the compiler neither
+// moves it nor adds waits for it: completion is tracked by the vmcnt waits in
+// the kernel, before the barrier that publishes the data.
+// M0 is named as clobbered although the compiler reserves it: these kernels
+// contain no other instruction that reads M0, so nothing is lost.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void copy_to_lds(u32x4 desc, unsigned voff, unsigned lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(desc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// x = ok ? x : -inf, in x's own register. A plain select would let the
+// masked scores of partial tiles live in other registers than the unmasked
+// scores of full tiles, and the compiler then copies all 32 scores on every
+// stage to merge the two paths.
+__device__ inline void mask_in_place(float& x, bool ok, float ninf) {
+  asm("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(__builtin_amdgcn_ballot_w64(ok)));
+}
+
+__device__ inline unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// vmcnt(n) with the other counters left free (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int D, int MOD, bool DOCS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
+  using G = PGeo<D>;
+  constexpr int DC = D / 16;   // 16-wide d chunks (k-steps of S^T)
+  constexpr int DB = D / 32;   // 32-row d blocks of O^T
+  constexpr int RB = G::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
+  __shared__ int ents[kPairMaxKeyTiles];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int wq = wave & 3;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  // ---- workgroup -> (b, h, 256-row tile): XCD-contiguous, heavy tiles first
+  const int np = (p.Sq + kBM - 1) / kBM;
+  const int total = p.B * p.H * np;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int wg = blockIdx.x;
+  const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
+  if (lin >= total) return;
+  const int qp = np - 1 - (lin % np);
+  const int bh = lin / np;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int kvh = h / (p.H / p.Hkv);
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
+  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + q_head * D;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + kv_head * D;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + kv_head * D;
+  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq) * RB);
+  const unsigned kv_bytes = static_cast<unsigned>(p.Skv) * RB;
+  const u32x4 desc = grp ? make_desc(vbase, kv_bytes) : make_desc(kbase, kv_bytes);
+
+  const int q_row = qp * kBM + grp * kPairHalf + wq * 32 + l32;
+  const bool q_ok = q_row < p.Sq;
+
+  // Q^T fragments (B operand of S^T): rows past Sq read as zero
+  bf16x8 qf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+        rq, static_cast<unsigned>(q_row) * RB + (c * 16 + g * 8) * 2, 0, 0));
+
+  // ---- key-tile list of this 256-row tile, into LDS. Entry:
+  // (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0 (half 0 = rows
+  // 0-127 of the tile, half 1 = rows 128-255). No block mask: every tile,
+  // both halves partial.
+  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
+  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
+  for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : ((i << 4) | 0x5);
+  int n_stages = 2 * n_entries;
+  if (n_entries > 0) {
+    const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
+    if (last * kTile + kBN >= p.Skv) n_stages -= 1;   // last tile has a single 64-key stage
+  }
+  __syncthreads();
+  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) >> 1]; };
+  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t & 1) * kBN; };
+
+  // ---- per-lane LDS offsets
+  // K fragment (S^T A operand): row l32 (+32 kb), chunk 2c + g
+  unsigned koff[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) koff[c] = l32 * RB + (((2 * c + g) ^ kswz<D>(l32)) * 16);
+  // V^T fragment via transposing reads: 16-lane group G, lane sl reads 4 d
+  // values of key row 16 ch + 8 j + 4 (G / 2) + sl / 4 starting at
+  // d = 32 db + 16 (G % 2) + 4 (sl % 4)
+  unsigned voff[DB];
+  {
+    const int G16 = lane >> 4, sl = lane & 15;
+    const int row0 = 4 * (G16 >> 1) + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * (G16 & 1) + ((sl & 3) >> 1);
+      voff[db] = row0 * RB + ((chunk ^ vswz<D>(row0)) * 16) + (sl & 1) * 8;
+    }
+  }
+  // copies: this wave fills 1 KB runs wq * kDma + j of a stage buffer; lane i
+  // writes slot i of the run, i.e. chunk position s % kCpr of row s / kCpr
+  unsigned goff[G::kDma];
+#pragma unroll
+  for (int j = 0; j < G::kDma; ++j) {
+    const int s = (wq * G::kDma + j) * 64 + lane;
+    const int r = s / G::kCpr, pos = s % G::kCpr;
+    const int c = pos ^ (grp ? vswz<D>(r) : kswz<D>(r));
+    goff[j] = r * RB + c * 16;
+  }
+  const unsigned my_lds =
+      __builtin_amdgcn_readfirstlane(lds_addr(grp ? vbuf : kbuf) + wq * G::kDma * 1024);
+  // group 0 copies K(t), group 1 V(t), into ring slot `ring`
+  auto issue_copy = [&](int t, int e, int ring) {
+    const unsigned gbase = static_cast<unsigned>(stage_kv0(t, e)) * RB;
+    const unsigned lbase = my_lds + ring * G::kBufBytes;
+#pragma unroll
+    for (int j = 0; j < G::kDma; ++j)
+      copy_to_lds(desc, gbase + goff[j], __builtin_amdgcn_readfirstlane(lbase + j * 1024));
+  };
+
+  // ---- running state
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  using SM = ScoreMod<MOD>;
+  const typename SM::Lane sml = SM::lane(p.va, h, q_row);
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
+
+  bf16x8 pf[4];
+
+  // S^T(t) = K(t) Q^T: two 32-key blocks, fragment reads 4 ahead of the MFMAs
+  auto qk = [&](int ring, f32x16 (&s)[2]) {
+    const unsigned char* kb_ = kbuf + ring * G::kBufBytes;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff[c] + kb * 32 * RB);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DC - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+  };
+
+  // O^T += V(t)^T P^T(t): the A fragment of (db, ch) is two transposing reads
+  // (keys 16 ch + 4 g + 0..3 and 16 ch + 8 + 4 g + 0..3, matching the key order
+  // of the P^T operand built from the S^T accumulators)
+  auto pv = [&](int ring) {
+    const unsigned char* vb = vbuf + ring * G::kBufBytes;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const unsigned char* a0 = vb + voff[db] + (16 * ch) * RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * RB));
+        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ch], o[db],
+                                                        0, 0, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x0100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+  };
+
+  // online softmax of one stage: scores -> P^T (bf16) in pf, running max/sum
+  auto softmax = [&](const f32x16 (&s)[2], int kv0, bool full) {
+    float t[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
+      }
+    const float ninf = -INFINITY;
+    if (!full) {
+      const bool causal = p.mask_kind & kMaskCausal;
+      const bool window = p.mask_kind & kMaskWindow;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = kv0 + kb * 32 + 8 * i + 4 * g;
+          u32x4 lab = {0u, 0u, 0u, 0u};
+          if constexpr (DOCS) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(k0) * 4u, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kidx = k0 + e;
+            bool ok = kidx < p.Skv;
+            ok &= !causal | (q_row >= kidx);
+            ok &= !window | (q_row - kidx < p.va.window);
+            if constexpr (DOCS) ok &= static_cast<int>(lab[e]) == doc_q;
+            mask_in_place(t[kb * 16 + 4 * i + e], ok, ninf);
+          }
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, t[i]);
+    mx = max_pair32(mx);
+    if constexpr (SM::kFoldScale) mx *= p.va.c1;
+    if (__any(mx > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float base = (m_run == -INFINITY) ? 0.f : m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int kb = ch >> 1, r0 = (ch & 1) * 8;
+      unsigned w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p0, p1;
+        if constexpr (SM::kFoldScale) {
+          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j], p.va.c1, -base));
+          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j + 1], p.va.c1, -base));
+        } else {
+          p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j] - base);
+          p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1] - base);
+        }
+        ls += p0 + p1;
+        w[j] = pack_bf16(p0, p1);
+      }
+      const u32x4 wv = {w[0], w[1], w[2], w[3]};
+      pf[ch] = __builtin_bit_cast(bf16x8, wv);
+    }
+    l_run += ls;
+  };
+
+  // ---- prologue: stages 0 and 1 (group 0 copies K, group 1 copies V)
+  const int T = n_stages;
+  if (T > 0) issue_copy(0, ent(0), 0);
+  if (T > 1) issue_copy(1, ent(1), 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (grp == 1) __syncthreads();   // group 1 runs one slot behind
+
+  int e_prev = 0, e_cur = ent(0), e_next = ent(1);
+  int ring = 0;   // ring slot of stage u (u % 3); stage u - 1 and u + 2 share slot (u + 2) % 3
+  const int sh = 2 * grp;
+  for (int u = 0; u < T; ++u) {
+    const int ring_old = ring == 0 ? kRing - 1 : ring - 1;
+    const int ec = __builtin_amdgcn_readfirstlane(e_cur) >> sh;
+    const int ep = __builtin_amdgcn_readfirstlane(e_prev) >> sh;
+    const bool do_s = ec & 1;              // this half has admitted pairs in stage u
+    const bool do_pv = u >= 1 && (ep & 1);
+
+    // matrix slot. S^T is computed even for a stage this half skips (a
+    // conditional product would make the scores a loop phi, which the compiler
+    // resolves by copying all 32 of them every stage).
+    f32x16 s[2];
+    qk(ring, s);
+    if (do_pv) pv(ring_old);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // vector slot
+    const int e_n2 = ent(u + 2);
+    if (do_s) softmax(s, stage_kv0(u, __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0);
+    if (u + 2 < T) {
+      issue_copy(u + 2, __builtin_amdgcn_readfirstlane(e_n2), ring_old);
+      wait_vm<G::kDma>();   // this group's copies of stage u + 1 are complete
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    e_prev = e_cur;
+    e_cur = e_next;
+    e_next = e_n2;
+    ring = ring == kRing - 1 ? 0 : ring + 1;
+  }
+  // last matrix slot: O^T += V^T P^T of the last stage; its vector slot is empty
+  {
+    const int ep = __builtin_amdgcn_readfirstlane(e_prev) >> sh;
+    if (T >= 1 && (ep & 1)) pv(ring == 0 ? kRing - 1 : ring - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();   // matches group 1's extra barrier
+
+  // ---- epilogue: normalise, LSE, store
+  const float l_tot = sum_pair32(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (q_ok) {
+    const size_t orow = (q_head + q_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const u32x2 vv = {pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
+                          pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.out) + orow + d0) = vv;
+      }
+    if (p.lse && g == 0)
+      p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int MOD, bool DOCS>
+hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
+  const int np = (p.Sq + kBM - 1) / kBM;
+  const long long total = static_cast<long long>(p.B) * p.H * np;
+  const long long per = (total + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+                     dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
+  return hipGetLastError();
+}
+
+template <int D, bool DOCS>
+hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
+  switch (p.mod_kind) {
+    case kModNone: return launch_t<D, kModNone, DOCS>(p, stream);
+    case kModAlibi: return launch_t<D, kModAlibi, DOCS>(p, stream);
+    case kModSoftcap: return launch_t<D, kModSoftcap, DOCS>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) {
+  const bool docs = p.mask_kind & kMaskDocument;
+  if (p.D == 128) return docs ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
+  if (p.D == 64) return docs ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -9,6 +9,12 @@
 
 namespace fa {
 
+// Block-mask lists are kept per 256-row query tile, made of two 128-row
+// halves; entries are (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0.
+constexpr int kPairHalf = 128;
+// Largest key-tile count whose list the bf16 kernel caches in LDS.
+constexpr int kPairMaxKeyTiles = 2048;
+
 struct FwdLaunch {
   const void* q;
   const void* k;
@@ -20,13 +26,16 @@ struct FwdLaunch {
   int mask_kind;
   int mod_kind;
   VariantArgs va;
-  // block mask (kv_count == nullptr: visit every key tile as partial)
+  // block mask (kv_count == nullptr: visit every key tile as partial);
+  // nq counts 256-row query tiles
   const int* kv_count;
   const int* kv_list;
   int nq, nk, bm_num_b;
 };
 
 hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream);
+// bf16 inputs with nk <= kPairMaxKeyTiles (256-row ping-pong kernel)
+hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream);
 
 struct MaskLaunch {
   int mask_kind;

@@ -224,11 +224,17 @@ def main(argv=None):
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kern_avg_ms * 1e-3) / 1e12
 
-    # tile FLOPs: every computed 128x128 tile counts in full
+    # tile FLOPs: every computed (128-row half, 128-key) tile counts in full
     bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv, dev)
     torch.cuda.synchronize()
-    counts = bm.counts().sum().item() * (wl.B if bm.struct.num_b == 1 else 1)
-    tile_flop = 4.0 * wl.D * 128 * 128 * counts * wl.H
+    cnt, lst = bm.counts().cpu(), bm.lists().cpu()
+    halves = 0
+    for bb in range(cnt.shape[0]):
+        for qp in range(cnt.shape[1]):
+            e = lst[bb, qp, :int(cnt[bb, qp])]
+            halves += int(((e & 1) + ((e >> 2) & 1)).sum())
+    halves *= wl.B if bm.struct.num_b == 1 else 1
+    tile_flop = 4.0 * wl.D * 128 * 128 * halves * wl.H
 
     bytes_alg = (q.numel() + k.numel() + v.numel() + out.numel()) * q.element_size() + lse.numel() * 4
     traffic = traffic_from_profile(wl.name)

@@ -43,8 +43,10 @@ extern "C" {
 
 #define FLEXATTN_VERSION 1
 
-/* Tile edge of the block mask, in query rows and in keys. */
+/* Block-mask tiles: FLEXATTN_QTILE query rows (two halves of FLEXATTN_TILE
+ * rows) by FLEXATTN_TILE keys. */
 #define FLEXATTN_TILE 128
+#define FLEXATTN_QTILE 256
 
 /* Status codes: 0 on success, negative on failure. */
 enum flexattn_status {
@@ -94,22 +96,27 @@ typedef struct flexattn_params {
   int doc_stride;            /* elements per batch row of doc_ids, >= max(Sq, Skv)    */
 } flexattn_params;
 
-/* Block mask: for every query tile of FLEXATTN_TILE rows, the ascending list of
- * key tiles of FLEXATTN_TILE keys that hold at least one admitted pair, each
- * flagged full (every pair in range and admitted, so the kernel skips the
- * per-element mask) or partial. Empty tiles are absent and never computed.
+/* Block mask: for every query tile of FLEXATTN_QTILE rows, the ascending list
+ * of key tiles of FLEXATTN_TILE keys that hold at least one admitted pair for
+ * either half of the query tile (rows 0-127 = half 0, rows 128-255 = half 1).
+ * Each entry is
+ *     (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0
+ * where any_h says the half has an admitted pair in the tile and full_h that
+ * every pair of the half is in range and admitted (the kernel then skips the
+ * per-element mask). Tiles empty for both halves are absent and never
+ * computed; a half that is empty in a listed tile skips it.
  * The lists depend on the batch only through DOCUMENT masks (num_b = B then,
  * else num_b = 1 and row 0 serves every batch); no mask depends on the head.
  * Filled in by flexattn_build_block_mask; the arrays live in the caller's
  * buffer. */
 typedef struct flexattn_block_mask {
-  int tile_q, tile_k;   /* both FLEXATTN_TILE                                    */
+  int tile_q, tile_k;   /* FLEXATTN_QTILE, FLEXATTN_TILE                         */
   int nq, nk;           /* ceil(Sq / tile_q), ceil(Skv / tile_k)                  */
   int num_b;            /* 1 or B                                                */
   int mask_kind;        /* the mask_kind it was built for                        */
   int Sq, Skv;          /* the sizes it was built for                            */
   const int* kv_count;  /* device int32 [num_b][nq]: entries in each list        */
-  const int* kv_list;   /* device int32 [num_b][nq][nk]: (kv_tile << 1) | is_full,
+  const int* kv_list;   /* device int32 [num_b][nq][nk]: entries as above,
                            ascending; entries past kv_count are unspecified      */
 } flexattn_block_mask;
 
@@ -126,8 +133,8 @@ const char* flexattn_last_error(void);
  * (int32 counts and lists). Returns 0 for invalid sizes or mask kinds. */
 size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind);
 
-/* Classify every (query tile, key tile) pair of the mask as full, partial or
- * empty and write the per-query-tile key-tile lists into `buf` (device memory
+/* Classify every (query half-tile, key tile) pair of the mask as full,
+ * partial or empty and write the per-query-tile key-tile lists into `buf` (device memory
  * of at least flexattn_block_mask_bytes(B, Sq, Skv, mask_kind) bytes, 4-byte
  * aligned). `params` supplies window and doc_ids as for flexattn_fwd (may be
  * NULL when the mask needs neither). On success fills *out, whose pointers

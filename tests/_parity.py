@@ -16,6 +16,25 @@ O_MEAN_ABS = 2e-3
 LSE_ABS = 1e-3
 
 
+def pair_lists(ref: np.ndarray) -> list[list[int]]:
+    """Expected block-mask lists from per-(128-row tile, 128-key tile) classes
+    (0 empty, 1 partial, 2 full): one list per 256-row query tile, entry
+    (kv_tile << 4) | class bits of half 1 << 2 | class bits of half 0, where a
+    class is coded 0 (empty), 1 (partial) or 3 (full)."""
+    code = {0: 0, 1: 1, 2: 3}
+    out = []
+    for qp in range((ref.shape[0] + 1) // 2):
+        lst = []
+        for j in range(ref.shape[1]):
+            bits = code[int(ref[2 * qp, j])]
+            if 2 * qp + 1 < ref.shape[0]:
+                bits |= code[int(ref[2 * qp + 1, j])] << 2
+            if bits:
+                lst.append((j << 4) | bits)
+        out.append(lst)
+    return out
+
+
 def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
     wl = inp.wl
     return fa.Variant(

@@ -51,9 +51,10 @@ def test_version_and_strings():
 
 
 def test_block_mask_bytes():
-    assert fa.flexattn_block_mask_bytes(2, 256, 384, 1) == 1 * 2 * (1 + 3) * 4
-    assert fa.flexattn_block_mask_bytes(2, 256, 384, 4) == 2 * 2 * (1 + 3) * 4
-    assert fa.flexattn_block_mask_bytes(1, 129, 129, 0) == 2 * 3 * 4
+    # [num_b][nq] counts + [num_b][nq][nk] lists, nq = ceil(Sq / 256), nk = ceil(Skv / 128)
+    assert fa.flexattn_block_mask_bytes(2, 256, 384, 1) == 1 * 1 * (1 + 3) * 4
+    assert fa.flexattn_block_mask_bytes(2, 257, 384, 4) == 2 * 2 * (1 + 3) * 4
+    assert fa.flexattn_block_mask_bytes(1, 129, 129, 0) == 1 * 3 * 4
     for bad in [(0, 128, 128, 0), (1, 0, 128, 0), (1, 128, -1, 0), (1, 128, 128, 8),
                 (1, 128, 128, -1)]:
         assert fa.flexattn_block_mask_bytes(*bad) == 0
@@ -129,7 +130,7 @@ def test_fwd_validation(over, code):
 
 def bm_struct(**kw):
     s = _lib.BlockMask()
-    s.tile_q = kw.get("tile_q", 128)
+    s.tile_q = kw.get("tile_q", 256)
     s.tile_k = kw.get("tile_k", 128)
     s.nq = kw.get("nq", 1)
     s.nk = kw.get("nk", 1)
@@ -143,7 +144,7 @@ def bm_struct(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(tile_q=64), dict(tile_k=256), dict(nq=2), dict(nk=3), dict(mask_kind=1), dict(Sq=127),
+    dict(tile_q=128), dict(tile_k=256), dict(nq=2), dict(nk=3), dict(mask_kind=1), dict(Sq=127),
     dict(Skv=100), dict(num_b=2), dict(kv_count=None), dict(kv_list=None),
 ])
 def test_fwd_rejects_mismatched_block_mask(kw):

@@ -13,7 +13,7 @@ import torch
 
 import attention_tiled_attn_amd as fa
 import oracle
-from tests._parity import (compare, device_variant, make_inputs, run_gpu, run_oracle,
+from tests._parity import (compare, device_variant, make_inputs, pair_lists, run_gpu, run_oracle,
                            sample_rows, small, to_np)
 from workload import WORKLOADS
 
@@ -149,10 +149,9 @@ def test_block_mask_matches_tile_classes(case):
     for b in range(counts.shape[0]):
         ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
                                   doc_row=None if inp.doc_ids is None else inp.doc_ids[b])
-        for qt in range(ref.shape[0]):
-            want = [(j << 1) | (1 if ref[qt, j] == 2 else 0) for j in range(ref.shape[1]) if ref[qt, j]]
-            got = lists[b, qt, :counts[b, qt]].tolist()
-            assert got == want, (b, qt)
+        for qp, want in enumerate(pair_lists(ref)):
+            got = lists[b, qp, :counts[b, qp]].tolist()
+            assert got == want, (b, qp)
 
 
 def test_block_mask_document_workload_full_size():
@@ -163,11 +162,10 @@ def test_block_mask_document_workload_full_size():
     counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
     ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=True, window=wl.window, doc_row=inp.doc_ids[0])
     n_full = n_part = 0
-    for qt in range(ref.shape[0]):
-        want = [(j << 1) | (1 if ref[qt, j] == 2 else 0) for j in range(ref.shape[1]) if ref[qt, j]]
-        assert lists[0, qt, :counts[0, qt]].tolist() == want
-        n_full += int((ref[qt] == 2).sum())
-        n_part += int((ref[qt] == 1).sum())
+    for qp, want in enumerate(pair_lists(ref)):
+        assert lists[0, qp, :counts[0, qp]].tolist() == want
+    n_full = int((ref == 2).sum())
+    n_part = int((ref == 1).sum())
     say(f"[blockmask] doc_swa: {n_full} full + {n_part} partial tiles of {ref.size}")
 
 

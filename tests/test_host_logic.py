@@ -50,3 +50,21 @@ def test_draw_order_and_determinism():
     assert torch.equal(k, torch.randn((1, 1, 6, 4), generator=g))
     q2, _, _ = draw_qkv(1, 2, 1, 5, 6, 4, seed=3)
     assert torch.equal(q, q2)
+
+
+def test_pair_lists_from_tile_classes():
+    """The expected-list helper of the GPU block-mask tests, checked on causal
+    classes: 256-row tile p holds key tiles 0..2p+1; tile 2p is partial for
+    half 0 and full for half 1, tile 2p+1 is empty for half 0 and partial for
+    half 1; all earlier tiles are full for both halves."""
+    from oracle import tile_classes
+    from tests._parity import pair_lists
+    n = 6
+    lists = pair_lists(tile_classes(n * 128, n * 128, 128, causal=True))
+    assert len(lists) == n // 2
+    for p, lst in enumerate(lists):
+        want = [(j << 4) | 0xF for j in range(2 * p)] + [((2 * p) << 4) | 0xD, ((2 * p + 1) << 4) | 0x4]
+        assert lst == want, p
+    # an odd number of 128-row tiles: the last 256-row tile has no second half
+    lists = pair_lists(tile_classes(3 * 128, 3 * 128, 128))
+    assert lists[1] == [(j << 4) | 0x3 for j in range(3)]
