@@ -61,6 +61,7 @@ constexpr int kTile = 128;      // key tile of the block mask
 constexpr int kRing = 3;        // stage buffers for K and for V
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kSumLimit = 256.0f;   // 2^kRescaleLog2
 
 template <int D>
 struct PGeo {
@@ -350,40 +351,72 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
           }
         }
     }
-    float mx = -INFINITY;
+    // P = exp2(t - base) rounded to bf16 into pf; returns this lane's fp32 sum
+    // of the unrounded values
+    auto exps = [&](float base) -> float {
+      float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, t[i]);
-    mx = max_pair32(mx);
-    if constexpr (SM::kFoldScale) mx *= p.va.c1;
-    if (__any(mx > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int ch = 0; ch < 4; ++ch) {
+        const int kb = ch >> 1, r0 = (ch & 1) * 8;
+        unsigned w[4];
 #pragma unroll
-      for (int i = 0; i < DB; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    const float base = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int kb = ch >> 1, r0 = (ch & 1) * 8;
-      unsigned w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p0, p1;
-        if constexpr (SM::kFoldScale) {
-          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j], p.va.c1, -base));
-          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j + 1], p.va.c1, -base));
-        } else {
-          p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j] - base);
-          p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1] - base);
+        for (int j = 0; j < 4; ++j) {
+          float p0, p1;
+          if constexpr (SM::kFoldScale) {
+            p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j], p.va.c1, -base));
+            p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j + 1], p.va.c1, -base));
+          } else {
+            p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j] - base);
+            p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1] - base);
+          }
+          w[j] = pack_bf16(p0, p1);
+          acc += p0 + p1;
         }
-        ls += p0 + p1;
-        w[j] = pack_bf16(p0, p1);
+        const u32x4 wv = {w[0], w[1], w[2], w[3]};
+        pf[ch] = __builtin_bit_cast(bf16x8, wv);
       }
-      const u32x4 wv = {w[0], w[1], w[2], w[3]};
-      pf[ch] = __builtin_bit_cast(bf16x8, wv);
+      return acc;
+    };
+    float ls = 0.f;
+    // Exponent base. Any base gives the same O / l and base + log2 l in exact
+    // arithmetic; the base is raised to the row max only when some score of
+    // the stage exceeds it by more than 2^kRescaleLog2 (the conditional
+    // rescaling of the FA4 forward-pass fixes). Without ALiBi the stage is
+    // first computed against the current base and checked afterwards: every
+    // weight is at most the lane's row sum, so a sum <= 2^kRescaleLog2 (which
+    // also rules out inf) proves no weight overflowed the bound, and the max
+    // is computed only when the check fails or no base exists yet. This pays
+    // off with soft-capping, whose tanh already keeps the vector ALU busy;
+    // without a score mod the denser exponential stream slows the other
+    // wave's matrix products more than the skipped max saves, and with ALiBi
+    // the bias grows with the key position so the max rises nearly every
+    // stage. Those take the max first.
+    // After a failed check the base moves to the row max whenever it grew at
+    // all, so that the following stages pass the check again.
+    bool need_max = true;
+    float grow = kRescaleLog2;
+    if constexpr (MOD == kModSoftcap) {
+      if (!__any(m_run == -INFINITY)) {
+        ls = exps(m_run);
+        need_max = __any(!(ls <= kSumLimit));
+        grow = 0.f;
+      }
+    }
+    if (need_max) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, t[i]);
+      mx = max_pair32(mx);
+      if constexpr (SM::kFoldScale) mx *= p.va.c1;
+      if (__any(mx > m_run + grow)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        m_run = m_new;
+      }
+      ls = exps((m_run == -INFINITY) ? 0.f : m_run);
     }
     l_run += ls;
   };
@@ -410,8 +443,10 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // conditional product would make the scores a loop phi, which the compiler
     // resolves by copying all 32 of them every stage).
     f32x16 s[2];
+    __builtin_amdgcn_s_setprio(1);   // the multiplying wave goes first on its SIMD
     qk(ring, s);
     if (do_pv) pv(ring_old);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -437,7 +472,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // last matrix slot: O^T += V^T P^T of the last stage; its vector slot is empty
   {
     const int ep = __builtin_amdgcn_readfirstlane(e_prev) >> sh;
+    __builtin_amdgcn_s_setprio(1);
     if (T >= 1 && (ep & 1)) pv(ring == 0 ? kRing - 1 : ring - 1);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __syncthreads();
