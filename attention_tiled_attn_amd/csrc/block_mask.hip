@@ -9,13 +9,13 @@
 // full ones is how a sparse variant (sliding window, document packing) runs at
 // dense-tile speed on the tiles it does compute.
 //
-// One wave per (batch row, 256-row query tile). The causal and window parts act on the
-// difference d = q - k, and over a rectangle of positions d takes every integer
-// between its extremes, so those two parts are classified exactly from the
-// rectangle's corners. The document part is classified from the label range of
-// the query rows and of the keys; when that is inconclusive the wave tests every
-// pair of the tile. Keys at or past Skv never count as admitted, so a tile that
-// reaches past Skv is at most partial.
+// The causal and window parts act on the difference d = q - k, and over a
+// rectangle of positions d takes every integer between its extremes, so those
+// two parts are classified exactly from the rectangle's corners. The document
+// part is classified from the label ranges of the query rows and of the keys;
+// where they cannot tell "empty" from "partial" the tile is kept as partial.
+// Keys at or past Skv never count as admitted, so a tile that reaches past Skv
+// is at most partial.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -51,40 +51,16 @@ __device__ inline void label_range(const int* doc, int lo, int hi, int lane, int
   mx = wave_max(b);
 }
 
-// Class of the rectangle (query rows [q_lo, q_hi]) x (keys [k_lo, k_hi]),
-// both non-empty. cls_d is the class under causal/window alone; dq_* and
-// dk_* are the label ranges of the rows and of the keys (documents only).
-__device__ inline int classify(const MaskLaunch& p, const int* doc, int lane, int q_lo, int q_hi,
-                               int k_lo, int k_hi, int cls_d, int dq_min, int dq_max, int dk_min,
-                               int dk_max) {
-  int cls = cls_d;
-  if (cls != kEmpty && doc) {
-    if (dq_max < dk_min || dk_max < dq_min) cls = kEmpty;
-    else if (dq_min == dq_max && dk_min == dk_max && dq_min == dk_min) cls = cls_d;  // one shared document
-    else cls = kUnknown;
-  }
-  if (cls == kUnknown) {
-    // test every in-range pair: lane takes query rows q_lo+lane and q_lo+64+lane
-    bool any = false, all = true;
-    for (int r = 0; r < 2; ++r) {
-      const int q = q_lo + r * 64 + lane;
-      if (q > q_hi) continue;
-      const int dq = doc[q];
-      for (int k = k_lo; k <= k_hi; ++k) {
-        const bool ok = admit(p.mask_kind, q, k, p.window, doc, dq);
-        any = any || ok;
-        all = all && ok;
-      }
-    }
-    const bool w_any = __any(any);
-    const bool w_all = __all(all);
-    cls = !w_any ? kEmpty : (w_all ? kFull : kPartial);
-  }
-  return cls;
-}
-
-// One wave per (batch row, 256-row query tile); the two 128-row halves are
-// classified separately and share one list.
+// One wave per (batch row, 256-row query tile); each lane classifies one key
+// tile (64 per pass) for both 128-row halves, and the non-empty tiles are
+// compacted in order with a ballot.
+//
+// Per half, causal and window give the class cls_d exactly from the corners.
+// Documents: with the label ranges of the half's rows [dq_min, dq_max] and of
+// the tile's keys [dk_min, dk_max], disjoint ranges mean empty and one shared
+// label means cls_d. A full tile needs every pair to share its label, which
+// the ranges decide exactly, so "full" is never given wrongly; the one
+// question they leave open is "empty or partial", answered "partial".
 __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
   const int qp = blockIdx.x;
   const int bb = blockIdx.y;
@@ -110,38 +86,71 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
 
   int* out = p.kv_list + (static_cast<size_t>(bb) * p.nq + qp) * p.nk;
   int n = 0;
-  for (int kt = 0; kt < p.nk; ++kt) {
-    const int k_lo = kt * kTile;
-    const int k_hi = min(p.Skv, k_lo + kTile) - 1;
+  for (int kt0 = 0; kt0 < p.nk; kt0 += 64) {
+    const int kt = kt0 + lane;
+    const bool valid = kt < p.nk;
+    const int k_lo = valid ? kt * kTile : 0;
+    const int k_hi = valid ? min(p.Skv, k_lo + kTile) - 1 : 0;
     const bool in_range = k_lo + kTile <= p.Skv;
 
-    // causal and window: over a half, d ranges over [q_lo - k_hi, q_hi - k_lo]
-    int cls_d[2];
+    int cls[2];
     bool need_labels = false;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const long long dmin = static_cast<long long>(q_lo[hf]) - k_hi;
       const long long dmax = static_cast<long long>(q_hi[hf]) - k_lo;
-      if (!live[hf] || dmax < lo_d || dmin > hi_d) cls_d[hf] = kEmpty;
-      else if (dmin >= lo_d && dmax <= hi_d) cls_d[hf] = kFull;
-      else cls_d[hf] = kPartial;
-      need_labels = need_labels || cls_d[hf] != kEmpty;
+      if (!valid || !live[hf] || dmax < lo_d || dmin > hi_d) cls[hf] = kEmpty;
+      else if (dmin >= lo_d && dmax <= hi_d) cls[hf] = kFull;
+      else cls[hf] = kPartial;
+      need_labels = need_labels || cls[hf] != kEmpty;
     }
-    int dk_min = 0, dk_max = 0;
-    if (docs && need_labels) label_range(doc, k_lo, k_hi, lane, dk_min, dk_max);
+    if (docs && need_labels) {
+      int dk_min = 0x7fffffff, dk_max = -0x7fffffff - 1;
+      int k = k_lo;
+      if (in_range && (reinterpret_cast<uintptr_t>(doc + k_lo) & 15) == 0) {
+        // a whole tile: 32 aligned 16-byte loads, several in flight
+        const int4* v4 = reinterpret_cast<const int4*>(doc + k_lo);
+#pragma unroll 8
+        for (int i = 0; i < kTile / 4; ++i) {
+          const int4 v = v4[i];
+          dk_min = min(dk_min, min(min(v.x, v.y), min(v.z, v.w)));
+          dk_max = max(dk_max, max(max(v.x, v.y), max(v.z, v.w)));
+        }
+        k = k_hi + 1;
+      }
+      for (; k <= k_hi; ++k) {
+        const int v = doc[k];
+        dk_min = min(dk_min, v);
+        dk_max = max(dk_max, v);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if (cls[hf] == kEmpty) continue;
+        if (dq_max[hf] < dk_min || dk_max < dq_min[hf]) cls[hf] = kEmpty;
+        else if (!(dq_min[hf] == dq_max[hf] && dk_min == dk_max && dq_min[hf] == dk_min)) cls[hf] = kUnknown;
+      }
+    }
+
+    // Ranges that overlap without one shared label leave "empty or partial"
+    // open; such a tile is kept as partial. The per-element mask then decides
+    // every pair of it, so results are unchanged (a visited tile with no
+    // admitted pair adds exactly nothing); only its compute may be spent
+    // in vain. Testing its pairs here cost more than computing it.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      if (cls[hf] == kUnknown) cls[hf] = kPartial;
 
     int bits = 0;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      int cls = classify(p, doc, lane, q_lo[hf], q_hi[hf], k_lo, k_hi, cls_d[hf], dq_min[hf],
-                         dq_max[hf], dk_min, dk_max);
-      if (cls == kFull && !in_range) cls = kPartial;
-      if (cls != kEmpty) bits |= (cls == kFull ? 3 : 1) << (2 * hf);
+      int c = cls[hf];
+      if (c == kFull && !in_range) c = kPartial;
+      if (c != kEmpty) bits |= (c == kFull ? 3 : 1) << (2 * hf);
     }
-    if (bits) {
-      if (lane == 0) out[n] = (kt << 4) | bits;
-      ++n;
-    }
+    const uint64_t have = __ballot(bits != 0);
+    const int before = __builtin_popcountll(have & ((1ull << lane) - 1ull));
+    if (bits) out[n + before] = (kt << 4) | bits;
+    n += __builtin_popcountll(have);
   }
   if (lane == 0) p.kv_count[bb * p.nq + qp] = n;
 }

@@ -268,7 +268,7 @@ def main(argv=None):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": bytes_alg,
-            "kernel": "attn_fwd_kernel",
+            "kernel": "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel",
         },
         "kernel_sha": kernel_sha(),
         "gpu": torch.cuda.get_device_name(dev),

@@ -138,8 +138,13 @@ size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind);
  * of at least flexattn_block_mask_bytes(B, Sq, Skv, mask_kind) bytes, 4-byte
  * aligned). `params` supplies window and doc_ids as for flexattn_fwd (may be
  * NULL when the mask needs neither). On success fills *out, whose pointers
- * point into buf, and enqueues the build on `stream`. The classification is
- * exact: it agrees with the per-element mask on every in-range pair. */
+ * point into buf, and enqueues the build on `stream`. A half is marked full
+ * exactly when every pair in it is in range and admitted, and absent only when
+ * no pair in it is admitted. Without DOCUMENT masks the classes are exact;
+ * with them, a half whose document labels overlap those of the key tile
+ * without all being one label may be listed as partial although no pair in
+ * it is admitted (the forward kernel's per-element mask then admits nothing
+ * there, so results do not change). */
 int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
                               void* buf, size_t bytes, flexattn_block_mask* out, void* stream);
 

@@ -35,6 +35,50 @@ def pair_lists(ref: np.ndarray) -> list[list[int]]:
     return out
 
 
+def check_pair_lists(counts: np.ndarray, lists: np.ndarray, ref: np.ndarray, Sq: int, Skv: int,
+                     doc_row: np.ndarray | None = None) -> int:
+    """Check the block-mask lists of one batch row against per-(128-row tile,
+    128-key tile) classes `ref` (0 empty, 1 partial, 2 full). Without documents
+    the lists must equal pair_lists(ref). With documents, full and partial
+    halves must match exactly, and a half the oracle finds empty may be listed
+    as partial only when the label range of its rows overlaps that of the
+    tile's keys without both being one single label. Returns the number of
+    such extra partial halves."""
+    if doc_row is None:
+        for qp, want in enumerate(pair_lists(ref)):
+            assert lists[qp, :counts[qp]].tolist() == want, qp
+        return 0
+    extra = 0
+    nq128, nk = ref.shape
+    for qp in range((nq128 + 1) // 2):
+        got = {}
+        entries = lists[qp, :counts[qp]].tolist()
+        assert entries == sorted(entries), qp
+        for e in entries:
+            got[e >> 4] = e & 0xF
+        for j in range(nk):
+            bits = got.get(j, 0)
+            for hf in range(2):
+                qt = 2 * qp + hf
+                g = (bits >> (2 * hf)) & 3          # 0 empty, 1 partial, 3 full
+                o = int(ref[qt, j]) if qt < nq128 else 0
+                if o == 2:
+                    assert g == 3, (qp, j, hf)
+                elif o == 1:
+                    assert g == 1, (qp, j, hf)
+                else:
+                    assert g in (0, 1), (qp, j, hf)
+                    if g == 1:
+                        ql = doc_row[qt * 128:min(Sq, qt * 128 + 128)]
+                        kl = doc_row[j * 128:min(Skv, j * 128 + 128)]
+                        overlap = ql.min() <= kl.max() and kl.min() <= ql.max()
+                        single = ql.min() == ql.max() == kl.min() == kl.max()
+                        assert overlap and not single, (qp, j, hf)
+                        extra += 1
+            assert (bits != 0) == (j in got), (qp, j)
+    return extra
+
+
 def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
     wl = inp.wl
     return fa.Variant(

@@ -68,3 +68,30 @@ def test_pair_lists_from_tile_classes():
     # an odd number of 128-row tiles: the last 256-row tile has no second half
     lists = pair_lists(tile_classes(3 * 128, 3 * 128, 128))
     assert lists[1] == [(j << 4) | 0x3 for j in range(3)]
+
+
+def test_check_pair_lists_contract():
+    """The document-mask checker accepts a listed-but-empty half only where the
+    label ranges are inconclusive, and rejects a wrong full/partial class."""
+    import numpy as np
+    import pytest
+    from oracle import tile_classes
+    from tests._parity import check_pair_lists, pair_lists
+    S = 512
+    doc = np.repeat(np.arange(4), 128).astype(np.int32)          # one document per 128 positions
+    doc[100:140] = 7                                              # a short document across a tile edge
+    ref = tile_classes(S, S, 128, causal=True, doc_row=doc)
+    lists = pair_lists(ref)
+    nk = ref.shape[1]
+    counts = np.array([len(x) for x in lists])
+    arr = np.zeros((len(lists), nk), dtype=np.int64)
+    for i, x in enumerate(lists):
+        arr[i, :len(x)] = x
+    assert check_pair_lists(counts, arr, ref, S, S, doc) == 0
+    # half 1 of query tile 0 (rows 128-255) against key tile 0 (labels 0 and 7):
+    # row labels {1, 7} overlap {0, 7}, so a partial in place of the oracle's class is allowed
+    # only if the oracle says empty; a corrupted full flag is always rejected
+    bad = arr.copy()
+    bad[0, 0] |= 0x3 << 2
+    with pytest.raises(AssertionError):
+        check_pair_lists(counts, bad, ref, S, S, doc)
