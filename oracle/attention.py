@@ -45,7 +45,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["kv_head_of", "admitted", "modified_scores", "attention", "pair_count", "tile_classes"]
+__all__ = ["kv_head_of", "admitted", "modified_scores", "attention", "attention_backward",
+           "pair_count", "tile_classes"]
 
 
 def kv_head_of(h: int, H: int, Hkv: int) -> int:
@@ -137,6 +138,63 @@ def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None
             O[b, h] = np.where(any_kept[:, None], o, 0.0)
             LSE[b, h] = np.where(any_kept, lse, -np.inf)
     return O, LSE
+
+
+def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
+                       window: int | None = None, doc_ids=None, alibi_slopes=None,
+                       softcap: float | None = None):
+    """fp64 gradients of the attention forward: for the loss L = sum(O * dout),
+    returns (dQ, dK, dV) with the shapes of q, k and v.
+
+    The pages name a backward pass (used in training, reproducible in FA4's
+    deterministic mode: Neuron FA4 explainer, "FlashAttention-4: Built for
+    Blackwell", backward-pass fixes) but give no formulas; this is the exact
+    derivative of the definition in `attention`, written out row by row:
+
+        P      = softmax of the admitted modified scores (0 where masked,
+                 and a row with no admitted key has P = 0 and O = 0)
+        dV    += P^T dout                      (summed over the query heads of a group)
+        dP     = dout V^T
+        dS'    = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied to dP)
+        dS     = dS' * d s' / d s              (1 for no mod and ALiBi; 1 - tanh^2(s / c) for soft-capping)
+        dQ     = scale * dS K,   dK += scale * dS^T Q
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    if dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    rows, keys = np.arange(Sq), np.arange(Skv)
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        doc_row = None if doc_ids is None else np.asarray(doc_ids)[b]
+        keep = admitted(rows[:, None], keys[None, :], causal=causal, window=window, doc_row=doc_row)
+        any_kept = keep.any(axis=1)
+        for h in range(H):
+            kh = kv_head_of(h, H, Hkv)
+            s = (q[b, h] @ k[b, kh].T) * scale
+            sm = modified_scores(s, h, rows[:, None], keys[None, :], alibi_slopes=alibi_slopes,
+                                 softcap=softcap)
+            sm = np.where(keep, sm, -np.inf)
+            m = np.where(any_kept, sm.max(axis=1, initial=-np.inf), 0.0)
+            w = np.exp(sm - m[:, None])
+            l = w.sum(axis=1)
+            P = np.where(any_kept[:, None], w / np.where(l > 0, l, 1.0)[:, None], 0.0)
+            dV[b, kh] += P.T @ dout[b, h]
+            dP = dout[b, h] @ v[b, kh].T
+            dSm = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            if softcap is not None:
+                dS = dSm * (1.0 - np.tanh(s / float(softcap)) ** 2)
+            else:
+                dS = dSm
+            dQ[b, h] = scale * (dS @ k[b, kh])
+            dK[b, kh] += scale * (dS.T @ q[b, h])
+    return dQ, dK, dV
 
 
 def pair_count(Sq: int, Skv: int, *, causal: bool = False, window: int | None = None,
