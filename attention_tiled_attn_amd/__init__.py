@@ -16,14 +16,14 @@ import torch
 from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
     MOD_SOFTCAP, QTILE, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
-    flexattn_build_block_mask, flexattn_fwd, flexattn_last_error, flexattn_strerror,
+    flexattn_build_block_mask, flexattn_bwd, flexattn_fwd, flexattn_last_error, flexattn_strerror,
     flexattn_version, lib,
 )
 
 __all__ = [
-    "QTILE", "TILE", "flexattn_fwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
+    "QTILE", "TILE", "flexattn_fwd", "flexattn_bwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
-    "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError",
+    "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError", "attention_backward",
 ]
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
@@ -134,3 +134,35 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
                  make_params(var, q.dtype), block_mask.struct if block_mask is not None else None,
                  stream)
     return out, lse
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, dout: torch.Tensor, var: Variant | None = None, *,
+                       scale: float | None = None,
+                       block_mask: BuiltBlockMask | None | str = "auto",
+                       dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                       dv: torch.Tensor | None = None, delta: torch.Tensor | None = None,
+                       stream=None):
+    """(dQ, dK, dV) for the loss sum(out * dout), with out and lse from
+    attention() on the same inputs and variant (bf16 tensors). `delta` is the
+    [B, H, Sq] float32 scratch the call needs (allocated here if not given)."""
+    var = var or Variant()
+    B, H, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    for t in (q, k, v, out, dout):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise TypeError("q, k, v, out, dout must be contiguous bf16 device tensors")
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if isinstance(block_mask, str):
+        block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
+    flexattn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, B, H, Hkv, Sq, Skv, D, scale,
+                 var.mask_kind, var.mod_kind, make_params(var, q.dtype),
+                 block_mask.struct if block_mask is not None else None, stream)
+    return dq, dk, dv

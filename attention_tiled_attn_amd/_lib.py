@@ -26,7 +26,7 @@ TILE = 128
 QTILE = 256
 
 EXPORTS = ("flexattn_version", "flexattn_strerror", "flexattn_last_error",
-           "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd")
+           "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd", "flexattn_bwd")
 
 
 class FlexAttnError(RuntimeError):
@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.flexattn_fwd.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_float, c_int, c_int, ctypes.POINTER(Params),
                                    ctypes.POINTER(BlockMask), vp]
+        L.flexattn_bwd.restype = c_int
+        L.flexattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int,
+                                   c_int, c_int, c_int, c_float, c_int, c_int,
+                                   ctypes.POINTER(Params), ctypes.POINTER(BlockMask), vp]
         _lib = L
     return _lib
 
@@ -147,4 +151,17 @@ def flexattn_fwd(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: int,
                             _stream(stream, q))
     if check:
         _check(st, "flexattn_fwd")
+    return st
+
+
+def flexattn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, B: int, H: int, Hkv: int, Sq: int,
+                 Skv: int, D: int, scale: float, mask_kind: int, mod_kind: int,
+                 params: Params | None = None, block_mask: BlockMask | None = None, stream=None, *,
+                 check: bool = True) -> int:
+    st = lib().flexattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _ptr(delta), B, H, Hkv, Sq, Skv, D, scale,
+                            mask_kind, mod_kind, ctypes.byref(params) if params else None,
+                            ctypes.byref(block_mask) if block_mask else None, _stream(stream, q))
+    if check:
+        _check(st, "flexattn_bwd")
     return st

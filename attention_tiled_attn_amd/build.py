@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libflexattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "block_mask.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_bwd.hip", "block_mask.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

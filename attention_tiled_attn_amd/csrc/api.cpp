@@ -118,12 +118,14 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   return FLEXATTN_OK;
 }
 
-int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
-                 const flexattn_params* params, const flexattn_block_mask* block_mask,
-                 void* stream) {
-  const flexattn_params* prm = params ? params : &kDefaultParams;
-  if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the forward and backward calls (everything but the
+// pointers specific to each).
+int check_attn_args(const flexattn_params* prm, int B, int H, int Hkv, int Sq, int Skv, int D,
+                    float scale, int mask_kind, int mod_kind, const flexattn_block_mask* block_mask) {
   if (H < 1 || Hkv < 1 || H % Hkv != 0) return FLEXATTN_ERR_SHAPE;
   int st = check_mask_args(mask_kind, prm, B, Sq, Skv);
   if (st) return st;
@@ -137,21 +139,18 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   }
   if (mod_kind == FLEXATTN_MOD_SOFTCAP && !(prm->softcap > 0.f && std::isfinite(prm->softcap)))
     return FLEXATTN_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
-  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
-
   // 32-bit limits: in-kernel position arithmetic is int; tensor offsets are size_t.
   const long long nq = ceil_div(Sq, FLEXATTN_QTILE);
   const long long nk = ceil_div(Skv, FLEXATTN_TILE);
   if (static_cast<long long>(Sq) + FLEXATTN_QTILE > INT_MAX || static_cast<long long>(Skv) + FLEXATTN_TILE > INT_MAX)
     return FLEXATTN_ERR_OVERFLOW;
   if (static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_TILE) + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+  if (static_cast<long long>(B) * Hkv * nk + 8 > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
   // one (batch, head) slice is addressed with 32-bit byte offsets (rows up to
   // one query tile past the end are read, as zeros)
   const long long esz = prm->dtype == FLEXATTN_FP32 ? 4 : 2;
   if ((static_cast<long long>(Sq > Skv ? Sq : Skv) + FLEXATTN_QTILE) * D * esz > INT_MAX)
     return FLEXATTN_ERR_OVERFLOW;
-
   if (block_mask) {
     const flexattn_block_mask* bm = block_mask;
     if (bm->tile_q != FLEXATTN_QTILE || bm->tile_k != FLEXATTN_TILE || bm->nq != nq || bm->nk != nk ||
@@ -161,6 +160,34 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
     if (bm->num_b != want_b) return FLEXATTN_ERR_BLOCKMASK;
     if (!bm->kv_count || !bm->kv_list) return FLEXATTN_ERR_BLOCKMASK;
   }
+  return FLEXATTN_OK;
+}
+
+void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, int mod_kind) {
+  va.c1 = scale * fa::kLog2e;
+  const float cap = mod_kind == FLEXATTN_MOD_SOFTCAP ? prm->softcap : 1.f;
+  va.sc_in = 2.f * fa::kLog2e * scale / cap;
+  va.sc_out = cap * fa::kLog2e;
+  va.window = prm->window;
+  va.slopes = prm->alibi_slopes;
+  va.doc = prm->doc_ids;
+  va.doc_stride = prm->doc_stride;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream) {
+  const flexattn_params* prm = params ? params : &kDefaultParams;
+  if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
+  int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
 
   fa::FwdLaunch p{};
   p.q = q;
@@ -177,21 +204,62 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.is_fp32 = prm->dtype == FLEXATTN_FP32;
   p.mask_kind = mask_kind;
   p.mod_kind = mod_kind;
-  p.va.c1 = scale * fa::kLog2e;
-  const float cap = mod_kind == FLEXATTN_MOD_SOFTCAP ? prm->softcap : 1.f;
-  p.va.sc_in = 2.f * fa::kLog2e * scale / cap;
-  p.va.sc_out = cap * fa::kLog2e;
-  p.va.window = prm->window;
-  p.va.slopes = prm->alibi_slopes;
-  p.va.doc = prm->doc_ids;
-  p.va.doc_stride = prm->doc_stride;
+  fill_variant(p.va, prm, scale, mod_kind);
   p.kv_count = block_mask ? block_mask->kv_count : nullptr;
   p.kv_list = block_mask ? block_mask->kv_list : nullptr;
-  p.nq = static_cast<int>(nq);
-  p.nk = static_cast<int>(nk);
+  p.nq = ceil_div(Sq, FLEXATTN_QTILE);
+  p.nk = ceil_div(Skv, FLEXATTN_TILE);
   p.bm_num_b = block_mask ? block_mask->num_b : 1;
   hipError_t e = fa::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return FLEXATTN_OK;
+}
+
+int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream) {
+  const flexattn_params* prm = params ? params : &kDefaultParams;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
+    return FLEXATTN_ERR_NULLPTR;
+  int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
+  if (st) return st;
+  if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
+  if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FLEXATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return FLEXATTN_ERR_ALIGN;
+
+  fa::BwdLaunch p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = D;
+  p.mask_kind = mask_kind;
+  p.mod_kind = mod_kind;
+  p.scale = scale;
+  fill_variant(p.va, prm, scale, mod_kind);
+  p.kv_count = block_mask ? block_mask->kv_count : nullptr;
+  p.kv_list = block_mask ? block_mask->kv_list : nullptr;
+  p.nq = ceil_div(Sq, FLEXATTN_QTILE);
+  p.nk = ceil_div(Skv, FLEXATTN_TILE);
+  p.bm_num_b = block_mask ? block_mask->num_b : 1;
+  hipError_t e = fa::launch_attn_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return FLEXATTN_OK;
 }
 

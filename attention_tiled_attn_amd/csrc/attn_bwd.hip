@@ -1,0 +1,579 @@
+// attn_bwd.hip - attention backward for gfx950 (MI355X, CDNA4), bf16.
+//
+// Gradients of L = sum(O * dO) for the forward of attn_fwd_pp.hip. The pages
+// name the backward pass and a deterministic mode for it without formulas
+// (Neuron FA4 explainer, "FlashAttention-4: Built for Blackwell", backward-pass
+// fixes); differentiating the definition gives, per query row q, with
+// P = exp(s' - LSE) recomputed from the forward's LSE:
+//
+//     dV += P^T dO,  dP = dO V^T,  dS' = P * (dP - delta),  delta = rowsum(dO * O)
+//     dS  = dS' * ds'/ds  (1, or 1 - tanh^2 for soft-capping)
+//     dQ  = scale * dS K,  dK += scale * dS^T Q
+//
+// Two kernels, no atomics (every gradient element is summed by one lane in a
+// fixed order, so results are reproducible bit for bit):
+//  * attn_bwd_dq_kernel: one workgroup (4 waves x 32 rows) per 128 query rows
+//    of one (batch, head); it first forms delta for its rows (written to the
+//    caller's scratch for the second kernel), then walks the key tiles of the
+//    block mask: S^T = K Q^T and dP^T = V dO^T (A operands K and V rows), then
+//    dQ^T += K^T dS^T (A operand K^T through transposing LDS reads).
+//  * attn_bwd_dkdv_kernel: one workgroup (4 waves x 32 keys) per 128 keys of
+//    one (batch, key/value head); it walks the query heads of the group and
+//    the 64-row query stages that can see its keys: S = Q K^T and dP = dO V^T
+//    (B operands K^T and V^T kept in registers), then dV^T += dO^T P and
+//    dK^T += Q^T dS (A operands through transposing LDS reads of dO and Q).
+// Tiles go from HBM/L2 straight into LDS (buffer-to-LDS copies, a ring of
+// three 64-row stages), rows unpadded with 16-byte chunks permuted so that
+// both the b128 row reads and the transposing reads are free of bank
+// conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_util.h"
+#include "launch.h"
+#include "variants.h"
+
+namespace fa {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kRows = 128;      // query rows (dq) or keys (dkdv) per workgroup
+constexpr int kStage = 64;      // keys (dq) or query rows (dkdv) per stage
+constexpr int kTile = 128;      // key tile of the block mask
+constexpr int kRing = 3;
+constexpr int kXcds = 8;
+
+template <int D>
+struct BGeo {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBufBytes = kStage * D * 2;     // one 64-row tile
+  static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
+  static constexpr int kDma = kBufBytes / 1024 / 4;    // 1 KB copies per wave and tile
+  static_assert(kDma >= 1 && kBufBytes % 4096 == 0, "stage geometry");
+};
+
+// Chunk permutation of a row-major tile read both ways: the 16 rows a
+// quarter-wave reads in one b128 row-fragment read hit 16 different chunk
+// positions, and the 4 consecutive rows a half-wave reads in one transposing
+// read hit 4 different aligned groups of 4 chunks.
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  const int pr = r >> 1;
+  return 4 * (pr & 1) + ((pr >> 1) & 3);
+}
+
+template <int D>
+__device__ inline unsigned row_off(int r, int chunk) {
+  return static_cast<unsigned>(r * BGeo<D>::kRowBytes + ((chunk ^ swz<D>(r)) * 16));
+}
+
+// Copy 64 rows of D bf16 starting at byte `gbase` of the slice behind `desc`
+// into a stage buffer: this wave fills 1 KB runs wq * kDma + j; lane i writes
+// slot i, i.e. row s / kCpr at chunk position s % kCpr.
+template <int D>
+__device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned lds_base, int wq, int lane) {
+  using G = BGeo<D>;
+#pragma unroll
+  for (int j = 0; j < G::kDma; ++j) {
+    const int s = (wq * G::kDma + j) * 64 + lane;
+    const int r = s / G::kCpr, pos = s % G::kCpr;
+    const unsigned goff = static_cast<unsigned>(r * G::kRowBytes + ((pos ^ swz<D>(r)) * 16));
+    copy_to_lds(desc, gbase + goff,
+                __builtin_amdgcn_readfirstlane(lds_base + (wq * G::kDma + j) * 1024));
+  }
+}
+
+// A fragment of X^T for a 32x32x16 MFMA, from a row-major stage tile X (rows =
+// the reduction index): lane (d = 32 db + l32, half g) gets rows
+// 16 ch + 8 j + 4 g + 0..3 for j = 0, 1 at column d, through two transposing
+// reads. toff[db][j] is this lane's offset for ch = 0.
+template <int D>
+__device__ inline bf16x8 trans_frag(const unsigned char* buf, unsigned toff0, unsigned toff1, int ch) {
+  const unsigned char* a0 = buf + toff0 + 16 * ch * BGeo<D>::kRowBytes;
+  const unsigned char* a1 = buf + toff1 + 16 * ch * BGeo<D>::kRowBytes;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+  const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Per-lane offsets of trans_frag for ch = 0: 16-lane group G16, lane sl reads
+// 4 columns of row 8 j + 4 (G16 / 2) + sl / 4 starting at
+// d = 32 db + 16 (G16 % 2) + 4 (sl % 4).
+template <int D>
+__device__ inline unsigned trans_off(int lane, int db, int j) {
+  const int G16 = lane >> 4, sl = lane & 15;
+  const int r = 8 * j + 4 * (G16 >> 1) + (sl >> 2);
+  const int d0 = 32 * db + 16 * (G16 & 1) + 4 * (sl & 3);
+  return row_off<D>(r, d0 >> 3) + (d0 & 7) * 2;
+}
+
+// Modified score in log2 units, and d s'/d s for the chain rule.
+template <int MOD>
+__device__ inline float mod_score(float s, const VariantArgs& va, float slope2, int dk, float& dmod) {
+  if constexpr (MOD == kModAlibi) {
+    dmod = 1.f;
+    return __builtin_fmaf(s, va.c1, slope2 * static_cast<float>(dk));
+  } else if constexpr (MOD == kModSoftcap) {
+    const float e = __builtin_amdgcn_exp2f(s * va.sc_in);
+    const float th = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+    dmod = __builtin_fmaf(-th, th, 1.0f);
+    return th * va.sc_out;
+  } else {
+    dmod = 1.f;
+    return s * va.c1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and delta)
+template <int D, int MOD, bool DOCS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
+  using G = BGeo<D>;
+  constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
+  __shared__ int ents[kPairMaxKeyTiles];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int nq = (p.Sq + kRows - 1) / kRows;
+  const int total = p.B * p.H * nq;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int lin = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (lin >= total) return;
+  const int qt = nq - 1 - (lin % nq);
+  const int bh = lin / nq;
+  const int h = bh % p.H, b = bh / p.H;
+  const int kvh = h / (p.H / p.Hkv);
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
+  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
+  const unsigned qbytes = static_cast<unsigned>(p.Sq) * RB;
+  const rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + q_head * D, qbytes);
+  const rsrc_t ro = make_rsrc(static_cast<const __bf16*>(p.out) + q_head * D, qbytes);
+  const rsrc_t rdo = make_rsrc(static_cast<const __bf16*>(p.dout) + q_head * D, qbytes);
+  const unsigned kvbytes = static_cast<unsigned>(p.Skv) * RB;
+  const u32x4 kdesc = make_desc(static_cast<const __bf16*>(p.k) + kv_head * D, kvbytes);
+  const u32x4 vdesc = make_desc(static_cast<const __bf16*>(p.v) + kv_head * D, kvbytes);
+
+  const int q_row = qt * kRows + wave * 32 + l32;
+  const bool q_ok = q_row < p.Sq;
+
+  // B operands (Q^T, dO^T) and this row's delta = dO . O
+  bf16x8 qf[DC], dof[DC];
+  float delta = 0.f;
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    const unsigned off = static_cast<unsigned>(q_row) * RB + (c * 16 + g * 8) * 2;
+    qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    dof[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
+    const bf16x8 of = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) delta = __builtin_fmaf(static_cast<float>(dof[c][e]), static_cast<float>(of[e]), delta);
+  }
+  delta = sum_pair32(delta);
+  if (q_ok && g == 0) p.delta[q_head + q_row] = delta;
+  const float lse_raw = q_ok ? p.lse[q_head + q_row] : -INFINITY;
+  // exponent base in log2 units; a row that admitted nothing has P = 0
+  const float lse2 = (lse_raw == -INFINITY) ? INFINITY : lse_raw * kLog2e;
+  float slope2 = 0.f;
+  if constexpr (MOD == kModAlibi) slope2 = p.va.slopes[h] * kLog2e;
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
+
+  // key-tile list: half qt % 2 of 256-row tile qt / 2; a tile empty for this
+  // half is visited as partial (its masked scores give P = 0, adding nothing)
+  const int qp = qt >> 1, full_bit = 2 * (qt & 1) + 1;
+  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
+  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
+  for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : (i << 4);
+  int T = 2 * n_entries;
+  if (n_entries > 0) {
+    const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
+    if (last * kTile + kStage >= p.Skv) T -= 1;
+  }
+  __syncthreads();
+  auto ent = [&](int t) -> int { return ents[min(t, max(T - 1, 0)) >> 1]; };
+  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t & 1) * kStage; };
+
+  unsigned koff[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) koff[c] = row_off<D>(l32, 2 * c + g);
+  unsigned toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) toff[db][j] = trans_off<D>(lane, db, j);
+
+  const unsigned kl = lds_addr(kbuf), vl = lds_addr(vbuf);
+  auto copy_stage = [&](int t, int ring) {
+    const unsigned gb = static_cast<unsigned>(stage_kv0(t, __builtin_amdgcn_readfirstlane(ent(t)))) * RB;
+    copy_tile<D>(kdesc, gb, kl + ring * G::kBufBytes, wave, lane);
+    copy_tile<D>(vdesc, gb, vl + ring * G::kBufBytes, wave, lane);
+  };
+
+  if (T > 0) copy_stage(0, 0);
+  if (T > 1) copy_stage(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  int ring = 0;
+  for (int t = 0; t < T; ++t) {
+    const int e = __builtin_amdgcn_readfirstlane(ent(t));
+    const bool full = ((e >> full_bit) & 1) != 0;
+    const int kv0 = stage_kv0(t, e);
+    const unsigned char* kb_ = kbuf + ring * G::kBufBytes;
+    const unsigned char* vb_ = vbuf + ring * G::kBufBytes;
+
+    // S^T = K Q^T and dP^T = V dO^T
+    f32x16 s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff[c] + kb * 32 * RB);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vb_ + koff[c] + kb * 32 * RB);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[c], dp[kb], 0, 0, 0);
+      }
+
+    // dS^T = P^T (dP^T - delta) ds'/ds, packed to bf16 in the key order of
+    // the B operand (element 16 kb + r is key kv0 + 32 kb + 8 (r / 4) + 4 g + r % 4)
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int kb = ch >> 1, r0 = (ch & 1) * 8;
+      unsigned w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v2[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int r = r0 + 2 * jj + x;
+          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          float dmod;
+          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, kidx - q_row, dmod);
+          if (!full) {
+            bool ok = kidx < p.Skv;
+            ok &= !(p.mask_kind & kMaskCausal) | (q_row >= kidx);
+            ok &= !(p.mask_kind & kMaskWindow) | (q_row - kidx < p.va.window);
+            if constexpr (DOCS) {
+              const int lab = __builtin_amdgcn_raw_buffer_load_b32(rdoc, static_cast<unsigned>(kidx) * 4u, 0, 0);
+              ok &= lab == doc_q;
+            }
+            tt = ok ? tt : -INFINITY;
+          }
+          const float pr = __builtin_amdgcn_exp2f(tt - lse2);
+          v2[x] = pr * (dp[kb][r] - delta) * dmod;
+        }
+        w[jj] = pack_bf16(v2[0], v2[1]);
+      }
+      const u32x4 wv = {w[0], w[1], w[2], w[3]};
+      dsf[ch] = __builtin_bit_cast(bf16x8, wv);
+    }
+
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(kb_, toff[db][0], toff[db][1], ch),
+                                                         dsf[ch], dq[db], 0, 0, 0);
+
+    // stage t + 2 into the slot stage t - 1 used; retire stage t + 1
+    const int ring2 = ring == 0 ? kRing - 1 : ring - 1;
+    if (t + 2 < T) {
+      copy_stage(t + 2, ring2);
+      wait_vm<2 * G::kDma>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();
+    ring = ring == kRing - 1 ? 0 : ring + 1;
+  }
+
+  if (q_ok) {
+    const size_t orow = (q_head + q_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const u32x2 vv = {pack_bf16(dq[db][4 * i] * p.scale, dq[db][4 * i + 1] * p.scale),
+                          pack_bf16(dq[db][4 * i + 2] * p.scale, dq[db][4 * i + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dq) + orow + d0) = vv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+template <int D, int MOD, bool DOCS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdLaunch p) {
+  using G = BGeo<D>;
+  constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kRing * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing * G::kBufBytes];
+  __shared__ __attribute__((aligned(16))) float lbuf[kRing * kStage];
+  __shared__ __attribute__((aligned(16))) float dbuf[kRing * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int nk = (p.Skv + kRows - 1) / kRows;
+  const int total = p.B * p.Hkv * nk;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int lin = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (lin >= total) return;
+  const int kt = lin % nk;                  // ascending: under a causal mask the low tiles see the most rows
+  const int bkh = lin / nk;
+  const int kvh = bkh % p.Hkv, b = bkh / p.Hkv;
+  const int rep = p.H / p.Hkv;
+  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
+  const unsigned kvbytes = static_cast<unsigned>(p.Skv) * RB;
+  const rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + kv_head * D, kvbytes);
+  const rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + kv_head * D, kvbytes);
+
+  const int k_row = kt * kRows + wave * 32 + l32;
+  const bool k_ok = k_row < p.Skv;
+
+  // B operands K^T and V^T: lane (key l32, half g) holds 8 consecutive d
+  bf16x8 kf[DC], vf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    const unsigned off = static_cast<unsigned>(k_row) * RB + (c * 16 + g * 8) * 2;
+    kf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    vf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+  }
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
+  const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
+
+  // the 64-row query stages that can see keys [k_lo, k_hi] of this tile
+  const bool causal = p.mask_kind & kMaskCausal;
+  const bool window = p.mask_kind & kMaskWindow;
+  const int k_lo = kt * kRows;
+  const int k_hi = min(p.Skv, k_lo + kRows) - 1;
+  const int q_first = causal ? min(k_lo, p.Sq) : 0;
+  const int q_end = window ? static_cast<int>(min(static_cast<long long>(p.Sq),
+                                                  static_cast<long long>(k_hi) + p.va.window))
+                           : p.Sq;
+  const int s0 = q_first / kStage;
+  const int ns = q_end > q_first ? (q_end + kStage - 1) / kStage - s0 : 0;
+  const int T = rep * ns;
+
+  unsigned qoff[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) qoff[c] = row_off<D>(l32, 2 * c + g);
+  unsigned toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) toff[db][j] = trans_off<D>(lane, db, j);
+
+  const unsigned ql = lds_addr(qbuf), ol = lds_addr(obuf);
+  const unsigned ll = lds_addr(lbuf), dl = lds_addr(dbuf);
+  // stage u: query head rep kvh + u / ns, rows 64 (s0 + u % ns) ..
+  auto copy_stage = [&](int u, int ring) {
+    const int hh = kvh * rep + u / ns;
+    const int r0 = (s0 + u % ns) * kStage;
+    const size_t q_head = (static_cast<size_t>(b) * p.H + hh) * p.Sq;
+    const unsigned qbytes = static_cast<unsigned>(p.Sq) * RB;
+    const u32x4 qd = make_desc(static_cast<const __bf16*>(p.q) + q_head * D, qbytes);
+    const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + q_head * D, qbytes);
+    copy_tile<D>(qd, static_cast<unsigned>(r0) * RB, ql + ring * G::kBufBytes, wave, lane);
+    copy_tile<D>(od, static_cast<unsigned>(r0) * RB, ol + ring * G::kBufBytes, wave, lane);
+    if (wave == 0 && lane < 16) {
+      // 64 floats of LSE and of delta: 16 lanes x 16 bytes each
+      const u32x4 lsd = make_desc(p.lse + q_head, static_cast<unsigned>(p.Sq) * 4u);
+      const u32x4 dld = make_desc(p.delta + q_head, static_cast<unsigned>(p.Sq) * 4u);
+      copy_to_lds(lsd, static_cast<unsigned>(r0) * 4u + lane * 16u,
+                  __builtin_amdgcn_readfirstlane(ll + ring * kStage * 4));
+      copy_to_lds(dld, static_cast<unsigned>(r0) * 4u + lane * 16u,
+                  __builtin_amdgcn_readfirstlane(dl + ring * kStage * 4));
+    }
+  };
+  auto retire = [&](bool issued) {
+    // copies of the previous stage complete (wave 0 also copied LSE and delta)
+    if (issued) {
+      if (wave == 0) wait_vm<2 * G::kDma + 2>();
+      else wait_vm<2 * G::kDma>();
+    } else {
+      wait_vm<0>();
+    }
+  };
+
+  if (T > 0) copy_stage(0, 0);
+  if (T > 1) copy_stage(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dkt[i] = dvt[i] = f32x16{};
+
+  int ring = 0;
+  for (int u = 0; u < T; ++u) {
+    const int hh = kvh * rep + u / ns;
+    const int r0 = (s0 + u % ns) * kStage;
+    const unsigned char* qb_ = qbuf + ring * G::kBufBytes;
+    const unsigned char* ob_ = obuf + ring * G::kBufBytes;
+    const float* lb = lbuf + ring * kStage;
+    const float* dlb = dbuf + ring * kStage;
+    // every pair of the stage in range and admitted?
+    const int q_last = r0 + kStage - 1;
+    bool full = !DOCS && q_last < p.Sq && k_hi == k_lo + kRows - 1;
+    if (causal) full = full && r0 >= k_hi;
+    if (window) full = full && (q_last - k_lo < p.va.window);
+    float slope2 = 0.f;
+    if constexpr (MOD == kModAlibi) slope2 = p.va.slopes[hh] * kLog2e;
+
+    // S = Q K^T and dP = dO V^T: two 32-row query blocks
+    f32x16 s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qb_ + qoff[c] + qb * 32 * RB);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[c], s[qb], 0, 0, 0);
+        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ob_ + qoff[c] + qb * 32 * RB);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[c], dp[qb], 0, 0, 0);
+      }
+
+    // P and dS in the query order of the B operand (element 16 qb + i is row
+    // r0 + 32 qb + 8 (i / 4) + 4 g + i % 4)
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int qb = ch >> 1, i0 = (ch & 1) * 8;
+      unsigned wp[4], wd[4];
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        // rows r0 + 32 qb + 8 (i / 4) + 4 g + 0..3 for i = i0 + 4 hv ..
+        const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + ql0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + ql0);
+        u32x4 lab = {0u, 0u, 0u, 0u};
+        if constexpr (DOCS) {
+          if (!full) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0) * 4u, 0, 0);
+        }
+        float pv[4], dv4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = i0 + 4 * hv + x;
+          const int qrow = r0 + ql0 + x;
+          float dmod;
+          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, k_row - qrow, dmod);
+          if (!full) {
+            bool ok = k_ok && qrow < p.Sq;
+            ok &= !causal | (qrow >= k_row);
+            ok &= !window | (qrow - k_row < p.va.window);
+            if constexpr (DOCS) ok &= static_cast<int>(lab[x]) == doc_k;
+            tt = ok ? tt : -INFINITY;
+          }
+          const float lse2 = (l4[x] == -INFINITY) ? INFINITY : l4[x] * kLog2e;
+          const float pr = __builtin_amdgcn_exp2f(tt - lse2);
+          pv[x] = pr;
+          dv4[x] = pr * (dp[qb][i] - d4[x]) * dmod;
+        }
+        wp[2 * hv] = pack_bf16(pv[0], pv[1]);
+        wp[2 * hv + 1] = pack_bf16(pv[2], pv[3]);
+        wd[2 * hv] = pack_bf16(dv4[0], dv4[1]);
+        wd[2 * hv + 1] = pack_bf16(dv4[2], dv4[3]);
+      }
+      const u32x4 wpv = {wp[0], wp[1], wp[2], wp[3]};
+      const u32x4 wdv = {wd[0], wd[1], wd[2], wd[3]};
+      pf[ch] = __builtin_bit_cast(bf16x8, wpv);
+      dsf[ch] = __builtin_bit_cast(bf16x8, wdv);
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(ob_, toff[db][0], toff[db][1], ch),
+                                                          pf[ch], dvt[db], 0, 0, 0);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qb_, toff[db][0], toff[db][1], ch),
+                                                          dsf[ch], dkt[db], 0, 0, 0);
+      }
+
+    const int ring2 = ring == 0 ? kRing - 1 : ring - 1;
+    const bool more = u + 2 < T;
+    if (more) copy_stage(u + 2, ring2);
+    retire(more);
+    __syncthreads();
+    ring = ring == kRing - 1 ? 0 : ring + 1;
+  }
+
+  if (k_ok) {
+    const size_t orow = (kv_head + k_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const u32x2 kk = {pack_bf16(dkt[db][4 * i] * p.scale, dkt[db][4 * i + 1] * p.scale),
+                          pack_bf16(dkt[db][4 * i + 2] * p.scale, dkt[db][4 * i + 3] * p.scale)};
+        const u32x2 vv = {pack_bf16(dvt[db][4 * i], dvt[db][4 * i + 1]),
+                          pack_bf16(dvt[db][4 * i + 2], dvt[db][4 * i + 3])};
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dk) + orow + d0) = kk;
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dv) + orow + d0) = vv;
+      }
+  }
+}
+
+template <int D, int MOD, bool DOCS>
+hipError_t launch_t(const BwdLaunch& p, hipStream_t stream) {
+  {
+    const long long total = static_cast<long long>(p.B) * p.H * ((p.Sq + kRows - 1) / kRows);
+    const long long per = (total + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+                       dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long total = static_cast<long long>(p.B) * p.Hkv * ((p.Skv + kRows - 1) / kRows);
+  const long long per = (total + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool DOCS>
+hipError_t launch_mod(const BwdLaunch& p, hipStream_t stream) {
+  switch (p.mod_kind) {
+    case kModNone: return launch_t<D, kModNone, DOCS>(p, stream);
+    case kModAlibi: return launch_t<D, kModAlibi, DOCS>(p, stream);
+    case kModSoftcap: return launch_t<D, kModSoftcap, DOCS>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdLaunch& p, hipStream_t stream) {
+  if (p.nk > kPairMaxKeyTiles) return hipErrorInvalidValue;
+  const bool docs = p.mask_kind & kMaskDocument;
+  if (p.D == 128) return docs ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
+  if (p.D == 64) return docs ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -37,6 +37,30 @@ hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream);
 // bf16 inputs with nk <= kPairMaxKeyTiles (256-row ping-pong kernel)
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream);
 
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  int B, H, Hkv, Sq, Skv, D;
+  int mask_kind;
+  int mod_kind;
+  float scale;
+  VariantArgs va;
+  const int* kv_count;   // block mask (256-row query tiles), or nullptr
+  const int* kv_list;
+  int nq, nk, bm_num_b;
+};
+
+// dQ (and delta) first, then dK/dV, both on `stream`
+hipError_t launch_attn_bwd(const BwdLaunch& p, hipStream_t stream);
+
 struct MaskLaunch {
   int mask_kind;
   int window;

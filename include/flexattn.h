@@ -165,6 +165,31 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const flexattn_params* params, const flexattn_block_mask* block_mask,
                  void* stream);
 
+/* Attention backward: the gradients of L = sum(O * dout) with respect to q, k
+ * and v, for O = flexattn_fwd(q, k, v, ...) with the same variant. The pages
+ * name a backward pass used in training and a deterministic mode for it
+ * (Neuron FA4 explainer, "FlashAttention-4: Built for Blackwell", backward-pass
+ * fixes); the gradients follow from the definition above by differentiation.
+ *   q, k, v    : as for flexattn_fwd; bf16 only (params->dtype = FLEXATTN_BF16),
+ *                Skv <= 2048 * FLEXATTN_TILE (else FLEXATTN_ERR_UNSUPPORTED)
+ *   out, lse   : the forward's O [B][H][Sq][D] bf16 and LSE [B][H][Sq] float32
+ *   dout       : device [B][H][Sq][D] bf16, the gradient arriving at O
+ *   dq         : device [B][H][Sq][D] bf16; every element is written
+ *   dk, dv     : device [B][Hkv][Skv][D] bf16; every element is written (with
+ *                grouped heads, the sum over the query heads of the group)
+ *   delta      : device float32 [B][H][Sq], caller-owned scratch that the call
+ *                overwrites with rowsum(dout * out); its contents afterwards
+ *                are unspecified
+ *   block_mask : as for flexattn_fwd (used for dq; dk/dv classify their own
+ *                tiles), or NULL
+ * Each gradient element is accumulated in a fixed order by one thread (no
+ * atomics), so results are bitwise reproducible run to run. */
+int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

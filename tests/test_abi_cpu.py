@@ -172,3 +172,41 @@ def test_build_block_mask_validation():
 def test_error_raises_with_message():
     with pytest.raises(fa.FlexAttnError, match="invalid shape"):
         fa.flexattn_fwd(A, A, A, A, A, 0, 2, 2, 128, 128, 64, 0.1, 0, 0)
+
+
+# ------------------------------------------------------------------ backward validation
+BGOOD = dict(q=A, k=A, v=A, out=A, lse=A, dout=A, dq=A, dk=A, dv=A, delta=A, B=1, H=2, Hkv=2,
+             Sq=128, Skv=128, D=64, scale=0.125, mask_kind=0, mod_kind=0)
+
+
+def bcall(**over):
+    a = dict(BGOOD)
+    params = over.pop("params", None)
+    bm = over.pop("block_mask", None)
+    a.update(over)
+    return fa.flexattn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"],
+                           a["dv"], a["delta"], a["B"], a["H"], a["Hkv"], a["Sq"], a["Skv"], a["D"],
+                           a["scale"], a["mask_kind"], a["mod_kind"], params, bm, stream=None,
+                           check=False)
+
+
+@pytest.mark.parametrize("over,code", [
+    *[(dict(**{name: None}), _lib.ERR_NULLPTR)
+      for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "delta")],
+    (dict(H=3, Hkv=2), _lib.ERR_SHAPE),
+    (dict(D=96), _lib.ERR_UNSUPPORTED),
+    (dict(params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),     # bf16 only
+    (dict(Skv=2048 * 128 + 1), _lib.ERR_UNSUPPORTED),           # key-tile list limit
+    (dict(scale=0.0), _lib.ERR_ARG),
+    (dict(dout=A + 8), _lib.ERR_ALIGN),
+    (dict(dq=A + 4), _lib.ERR_ALIGN),
+    (dict(dk=A + 2), _lib.ERR_ALIGN),
+    (dict(dv=A + 8), _lib.ERR_ALIGN),
+    (dict(delta=A + 2), _lib.ERR_ALIGN),
+    (dict(lse=A + 1), _lib.ERR_ALIGN),
+    (dict(mask_kind=4, params=P()), _lib.ERR_NULLPTR),
+    (dict(mod_kind=1, params=P()), _lib.ERR_NULLPTR),
+    (dict(block_mask=bm_struct(tile_q=128)), _lib.ERR_BLOCKMASK),
+])
+def test_bwd_validation(over, code):
+    assert bcall(**over) == code

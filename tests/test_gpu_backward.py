@@ -1,0 +1,104 @@
+"""GPU parity of the attention backward (flexattn_bwd) against the fp64
+oracle's gradients, on the same bf16 inputs and output gradient."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_tiled_attn_amd as fa
+import oracle
+from tests._parity import device_variant, oracle_kwargs, small, to_np
+from workload import bf16_values, draw_dout
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances, per tensor, relative to the reference's own size: the output is
+# rounded to bf16 (at most 2^-8 relative), and P and dS enter the matrix
+# products rounded to bf16 (at most 2^-8 relative each), so the largest error
+# stays below about 3 * 2^-8 = 1.2e-2 of max|ref| and the mean error near
+# 2^-8 of mean|ref|. Measured: at most 5.6e-3 and 2.5e-3.
+REL_MAX = 1.5e-2
+REL_MEAN = 5.0e-3
+
+
+def say(msg):
+    import sys
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_bwd(inp, block_mask="auto", seed=11):
+    wl = inp.wl
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    dout = draw_dout(wl.B, wl.H, wl.Sq, wl.D, seed).to(torch.bfloat16).cuda()
+    var = device_variant(inp)
+    out, lse = fa.attention(q, k, v, var, scale=wl.scale)
+    grads = fa.attention_backward(q, k, v, out, lse, dout, var, scale=wl.scale, block_mask=block_mask)
+    torch.cuda.synchronize()
+    return grads, dout
+
+
+def ref_bwd(inp, dout):
+    q, k, v = (bf16_values(t) for t in (inp.q, inp.k, inp.v))
+    return oracle.attention_backward(q, k, v, bf16_values(dout.cpu()), inp.wl.scale,
+                                     **oracle_kwargs(inp))
+
+
+def check(inp, what, block_mask="auto"):
+    say(f"[bwd] {what}")
+    (dq, dk, dv), dout = run_bwd(inp, block_mask)
+    ref = ref_bwd(inp, dout)
+    stats = {}
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        g = to_np(got)
+        assert not np.isnan(g).any(), f"{what}: NaN in {name}"
+        err = np.abs(g - want)
+        scale_max = max(np.abs(want).max(initial=0.0), 1e-6)
+        scale_mean = max(np.abs(want).mean() if want.size else 0.0, 1e-6)
+        stats[name] = (err.max(initial=0.0) / scale_max, err.mean() / scale_mean)
+        assert stats[name][0] <= REL_MAX and stats[name][1] <= REL_MEAN, f"{what}: {name} {stats}"
+    say(f"[bwd]   " + " ".join(f"{n}: max {a:.2e} mean {b:.2e}" for n, (a, b) in stats.items()))
+    return stats
+
+
+VARIANTS = [
+    dict(), dict(causal=True), dict(causal=True, window=48), dict(window=40),
+    dict(documents=True), dict(documents=True, causal=True, window=64),
+    dict(mod="alibi", causal=True), dict(mod="softcap", softcap=5.0),
+    dict(mod="softcap", softcap=5.0, causal=True),
+]
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: ",".join(f"{a}={b}" for a, b in v.items()) or "dense")
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_variants(var, D):
+    check(small(S=200, D=D, **var), f"S=200 D={D} {var}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(S=1), dict(S=63), dict(S=64), dict(S=129), dict(S=333),
+    dict(Sq=100, Skv=300), dict(Sq=300, Skv=100), dict(B=2, H=4, Hkv=2, S=260),
+    dict(B=1, H=8, Hkv=1, S=150, causal=True),
+], ids=lambda s: ",".join(f"{a}{b}" for a, b in s.items()))
+def test_backward_shapes(shape):
+    check(small(D=64, **shape), f"{shape}")
+
+
+def test_backward_longer_causal_gqa():
+    check(small(B=1, H=4, Hkv=2, S=1100, D=128, causal=True), "S=1100 causal GQA D=128")
+
+
+def test_backward_is_reproducible():
+    """No atomics: two runs give identical bits."""
+    inp = small(B=2, H=4, Hkv=2, S=300, D=128, causal=True)
+    (a, _), (b, _) = run_bwd(inp), run_bwd(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_null_block_mask_is_bitwise_equal():
+    for var in (dict(causal=True, window=70), dict(documents=True, causal=True)):
+        inp = small(S=300, D=64, **var)
+        (a, _), (b, _) = run_bwd(inp, "auto"), run_bwd(inp, None)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), var

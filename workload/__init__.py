@@ -89,6 +89,14 @@ def draw_qkv(B: int, H: int, Hkv: int, Sq: int, Skv: int, D: int, seed: int):
     return q, k, v
 
 
+def draw_dout(B: int, H: int, Sq: int, D: int, seed: int) -> torch.Tensor:
+    """The output gradient dO for backward tests and benches: float32 N(0, 1)
+    on the CPU from a torch CPU generator seeded with `seed` + 1000."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 1000)
+    return torch.randn((B, H, Sq, D), generator=g, dtype=torch.float32)
+
+
 def as_element_type(x: torch.Tensor, dtype: str) -> torch.Tensor:
     """Cast a float32 CPU tensor to the workload's element type (bf16 uses
     round-to-nearest-even, which is what torch's cast does)."""
