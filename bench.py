@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dense] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload dense] [--no-cpu-baseline] [--pass bwd]
 
 One step is the whole hot path on one batch: build the block mask for the
 workload's mask, then run the attention forward (both kernels, enqueued on
@@ -9,6 +9,10 @@ torch's current stream). Inputs are seeded synthetic tensors resident in HBM
 before timing starts. The metric is effective TFLOPS counting only admitted
 (unmasked) pairs: 4 * D * pairs * B * H per forward (two products, 2 FLOP per
 multiply-add). Prints one JSON line.
+
+With --pass bwd the step is the block-mask build plus the backward call
+(flexattn_bwd: dQ, then dK/dV) on the forward's O and LSE, counted by the usual
+convention as 2.5 times the forward's FLOPs (five products per tile).
 """
 from __future__ import annotations
 
@@ -140,6 +144,47 @@ def cpu_baseline(inp, budget_s: float = 15.0):
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_bwd(inp, dout, budget_s: float = 15.0):
+    """The oracle's gradients, as they are, on whole (batch, query head)
+    slices of the same workload until the budget is spent; rate in the unit of
+    the GPU metric (2.5 x the forward FLOPs of the admitted pairs done)."""
+    import numpy as np
+    import oracle
+    from workload import bf16_values
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wl = inp.wl
+    rep = wl.H // wl.Hkv
+    t0 = time.perf_counter()
+    done_pairs = slices = 0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            kh = h // rep
+            q = bf16_values(inp.q[b:b + 1, h:h + 1])
+            k = bf16_values(inp.k[b:b + 1, kh:kh + 1])
+            v = bf16_values(inp.v[b:b + 1, kh:kh + 1])
+            g = bf16_values(dout[b:b + 1, h:h + 1])
+            doc = None if inp.doc_ids is None else inp.doc_ids[b:b + 1]
+            kw = dict(causal=wl.causal, window=wl.window or None, doc_ids=doc,
+                      alibi_slopes=None if inp.slopes is None else inp.slopes[h:h + 1].astype(np.float64),
+                      softcap=wl.softcap if wl.mod == "softcap" else None)
+            oracle.attention_backward(q, k, v, g, wl.scale, **kw)
+            slices += 1
+            done_pairs += _pairs_in_rows(wl, np.arange(wl.Sq), None if doc is None else doc[0])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": 2.5 * 4.0 * wl.D * done_pairs / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{slices} whole (batch, head) slices of {wl.B * wl.H}, {done_pairs} admitted "
+                      f"pairs, fp64 numpy oracle gradients, {dt:.1f} s"}
+
+
 def _pairs_in_rows(wl, rows, doc_row) -> int:
     import numpy as np
     import oracle
@@ -159,6 +204,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for counter scaling)")
     args = ap.parse_args(argv)
@@ -193,12 +240,28 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": n * 4}), file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    bwd = args.which == "bwd"
+    if bwd:
+        from workload import draw_dout
+        if wl.dtype != "bf16":
+            print(json.dumps({"error": "the backward takes bf16 inputs"}))
+            sys.exit(2)
+        dout_cpu = draw_dout(wl.B, wl.H, wl.Sq, wl.D, wl.seed).to(torch.bfloat16)
+        dout = dout_cpu.to(dev)
+        fa.attention(q, k, v, var, scale=wl.scale, out=out, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
 
     def step(ev=None):
         bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv, dev)
         if ev is not None:
             ev[0].record(stream)
-        fa.attention(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse)
+        if bwd:
+            fa.attention_backward(q, k, v, out, lse, dout, var, scale=wl.scale, block_mask=bm,
+                                  dq=dq, dk=dk, dv=dv, delta=delta)
+        else:
+            fa.attention(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse)
         if ev is not None:
             ev[1].record(stream)
         return bm
@@ -221,6 +284,8 @@ def main(argv=None):
 
     pairs = admitted_pairs(wl, inp.doc_ids)            # summed over batch rows
     flop = 4.0 * wl.D * pairs * wl.H                   # per forward
+    if bwd:
+        flop *= 2.5                                    # per backward, by convention
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kern_avg_ms * 1e-3) / 1e12
 
@@ -234,13 +299,16 @@ def main(argv=None):
             e = lst[bb, qp, :int(cnt[bb, qp])]
             halves += int(((e & 1) + ((e >> 2) & 1)).sum())
     halves *= wl.B if bm.struct.num_b == 1 else 1
-    tile_flop = 4.0 * wl.D * 128 * 128 * halves * wl.H
+    tile_flop = 4.0 * wl.D * 128 * 128 * halves * wl.H * (2.5 if bwd else 1.0)
 
     bytes_alg = (q.numel() + k.numel() + v.numel() + out.numel()) * q.element_size() + lse.numel() * 4
-    traffic = traffic_from_profile(wl.name)
+    if bwd:   # also reads dO and O, writes dQ, dK, dV and delta
+        bytes_alg += (2 * q.numel() + q.numel() + k.numel() + v.numel()) * q.element_size() + lse.numel() * 4
+    traffic = None if bwd else traffic_from_profile(wl.name)
 
     rec = {
-        "metric": "attention fwd effective TFLOPS (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",
+        "metric": ("attention bwd effective TFLOPS (2.5x forward unmasked FLOPs), 1 GPU" if bwd else
+                   "attention fwd effective TFLOPS (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU"),
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -268,13 +336,14 @@ def main(argv=None):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": bytes_alg,
-            "kernel": "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel",
+            "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkdv_kernel" if bwd else
+                       "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel"),
         },
         "kernel_sha": kernel_sha(),
         "gpu": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp)
+        rec["cpu_baseline"] = cpu_baseline_bwd(inp, dout_cpu) if bwd else cpu_baseline(inp)
     print(json.dumps(rec), flush=True)
 
 
