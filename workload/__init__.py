@@ -65,6 +65,10 @@ WORKLOADS = {
     "dense": Workload("dense", B=4, H=16, Hkv=16, S=4096, D=128, dtype="bf16", seed=1),
     "causal_gqa": Workload("causal_gqa", B=2, H=32, Hkv=8, S=8192, D=128, dtype="bf16",
                            causal=True, seed=2),
+    # one GPU's share of causal_gqa when the heads are split over 8 GPUs
+    # (whole GQA groups: 1 key/value head and its 4 query heads per GPU)
+    "causal_gqa_shard8": Workload("causal_gqa_shard8", B=2, H=4, Hkv=1, S=8192, D=128,
+                                  dtype="bf16", causal=True, seed=2),
     "doc_swa": Workload("doc_swa", B=1, H=16, Hkv=16, S=16384, D=128, dtype="bf16",
                         causal=True, window=1024, documents=True, seed=3, doc_seed=3),
     "alibi_d64": Workload("alibi_d64", B=1, H=32, Hkv=32, S=32768, D=64, dtype="bf16",
