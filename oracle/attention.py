@@ -37,6 +37,14 @@ Readings where the pages are silent (each also listed in the design notes):
   * ALiBi adds slope[h] * (k_idx - q_idx) to the scaled score; soft-capping
     replaces it by c * tanh(s / c);
   * grouped heads: query head h reads key/value head h // (H // Hkv).
+  * query row i stands at key position i + q_offset (0 by default, so rows and
+    keys start together); masks, ALiBi distances and document labels see that
+    position. Decoding and chunked prefill after Skv - Sq cached keys take
+    q_offset = Skv - Sq (the pages name Sq != Skv work only as a direction);
+  * prefix masking (named, not defined, in the PyTorch 2.5 / FlexAttention
+    article's overview and "What Happened?"): with causal, the keys before
+    `prefix` are visible to every query, the causal rule holds for the rest,
+    and the other masks still compose by AND.
 
 Every function here is pinned by tests that do not reuse it (closed forms,
 invariants, a scalar brute force and a library routine).
@@ -57,18 +65,23 @@ def kv_head_of(h: int, H: int, Hkv: int) -> int:
 
 
 def admitted(q_idx, k_idx, *, causal: bool = False, window: int | None = None,
-             doc_row=None) -> np.ndarray:
-    """The mask: True where query q_idx may attend to key k_idx.
+             doc_row=None, prefix: int | None = None) -> np.ndarray:
+    """The mask: True where the query at position q_idx may attend to the key
+    at position k_idx.
 
     `q_idx`, `k_idx` broadcast against each other (e.g. a column and a row of
-    indices); `doc_row` is the document label of every position of one batch
-    row (or None).
+    positions); `doc_row` is the document label of every position of one
+    batch row (or None). `prefix` (prefix-LM, with causal): keys before it
+    are visible to every query, the causal rule applies from it on.
     """
     q_idx = np.asarray(q_idx, dtype=np.int64)
     k_idx = np.asarray(k_idx, dtype=np.int64)
     keep = np.ones(np.broadcast_shapes(q_idx.shape, k_idx.shape), dtype=bool)
     if causal:
-        keep &= q_idx >= k_idx
+        c = q_idx >= k_idx
+        if prefix is not None and prefix > 0:
+            c = c | (k_idx < prefix)
+        keep &= c
     if window is not None and window > 0:
         keep &= (q_idx - k_idx) < window
     if doc_row is not None:
@@ -94,13 +107,16 @@ def modified_scores(s: np.ndarray, h: int, q_idx, k_idx, *, alibi_slopes=None,
 
 def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None = None,
               doc_ids=None, alibi_slopes=None, softcap: float | None = None, rows=None,
-              heads=None):
+              heads=None, q_offset: int = 0, prefix: int | None = None):
     """fp64 attention forward, the definition written out.
 
     q: [B, H, Sq, D], k and v: [B, Hkv, Skv, D] (any real dtype; computed in
-    float64). doc_ids: [B, >= max(Sq, Skv)] document label per position, or
-    None. rows: optional 1-D array of query indices to evaluate (for sampled
-    checks at full size); heads: optional list of query heads to evaluate.
+    float64). Query row i sits at position i + q_offset of the key sequence
+    (masks, score mods and document labels see positions). doc_ids:
+    [B, >= max(Sq + q_offset, Skv)] document label per position, or None.
+    prefix: prefix-LM boundary (see `admitted`). rows: optional 1-D array of
+    query indices to evaluate (for sampled checks at full size); heads:
+    optional list of query heads to evaluate.
 
     Returns (O, LSE): O [B, H, len(rows), D] float64 and LSE [B, H, len(rows)]
     float64 (natural log). Heads not in `heads` are left as NaN.
@@ -120,13 +136,14 @@ def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None
     LSE = np.full((B, H, rows.size), np.nan)
     for b in range(B):
         doc_row = None if doc_ids is None else np.asarray(doc_ids)[b]
-        keep = admitted(rows[:, None], keys[None, :], causal=causal, window=window,
-                        doc_row=doc_row)
+        pos = rows + q_offset
+        keep = admitted(pos[:, None], keys[None, :], causal=causal, window=window,
+                        doc_row=doc_row, prefix=prefix)
         any_kept = keep.any(axis=1)
         for h in heads:
             kh = kv_head_of(h, H, Hkv)
             s = (q[b, h, rows, :] @ k[b, kh].T) * scale
-            s = modified_scores(s, h, rows[:, None], keys[None, :],
+            s = modified_scores(s, h, pos[:, None], keys[None, :],
                                 alibi_slopes=alibi_slopes, softcap=softcap)
             s = np.where(keep, s, -np.inf)
             m = np.where(any_kept, s.max(axis=1, initial=-np.inf), 0.0)
@@ -142,7 +159,8 @@ def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None
 
 def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
                        window: int | None = None, doc_ids=None, alibi_slopes=None,
-                       softcap: float | None = None):
+                       softcap: float | None = None, q_offset: int = 0,
+                       prefix: int | None = None):
     """fp64 gradients of the attention forward: for the loss L = sum(O * dout),
     returns (dQ, dK, dV) with the shapes of q, k and v.
 
@@ -173,12 +191,14 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
     dV = np.zeros_like(v)
     for b in range(B):
         doc_row = None if doc_ids is None else np.asarray(doc_ids)[b]
-        keep = admitted(rows[:, None], keys[None, :], causal=causal, window=window, doc_row=doc_row)
+        pos = rows + q_offset
+        keep = admitted(pos[:, None], keys[None, :], causal=causal, window=window, doc_row=doc_row,
+                        prefix=prefix)
         any_kept = keep.any(axis=1)
         for h in range(H):
             kh = kv_head_of(h, H, Hkv)
             s = (q[b, h] @ k[b, kh].T) * scale
-            sm = modified_scores(s, h, rows[:, None], keys[None, :], alibi_slopes=alibi_slopes,
+            sm = modified_scores(s, h, pos[:, None], keys[None, :], alibi_slopes=alibi_slopes,
                                  softcap=softcap)
             sm = np.where(keep, sm, -np.inf)
             m = np.where(any_kept, sm.max(axis=1, initial=-np.inf), 0.0)
@@ -198,19 +218,20 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
 
 
 def pair_count(Sq: int, Skv: int, *, causal: bool = False, window: int | None = None,
-               doc_row=None) -> int:
+               doc_row=None, q_offset: int = 0, prefix: int | None = None) -> int:
     """Number of admitted (query, key) pairs, counted element by element."""
     total = 0
     keys = np.arange(Skv)
     for lo in range(0, Sq, 1024):
-        r = np.arange(lo, min(Sq, lo + 1024))
+        r = np.arange(lo, min(Sq, lo + 1024)) + q_offset
         total += int(admitted(r[:, None], keys[None, :], causal=causal,
-                              window=window, doc_row=doc_row).sum())
+                              window=window, doc_row=doc_row, prefix=prefix).sum())
     return total
 
 
 def tile_classes(Sq: int, Skv: int, tile: int, *, causal: bool = False,
-                 window: int | None = None, doc_row=None) -> np.ndarray:
+                 window: int | None = None, doc_row=None, q_offset: int = 0,
+                 prefix: int | None = None) -> np.ndarray:
     """Classify every (query tile, key tile) pair by testing every pair of
     positions: 0 = empty (no admitted pair), 2 = full (every query row in
     range admits every key of the tile, and the tile lies inside [0, Skv)),
@@ -223,8 +244,8 @@ def tile_classes(Sq: int, Skv: int, tile: int, *, causal: bool = False,
     out = np.zeros((nq, nk), dtype=np.int64)
     for i in range(nq):
         rows = np.arange(i * tile, min(Sq, (i + 1) * tile))
-        keep = admitted(rows[:, None], np.arange(Skv)[None, :], causal=causal, window=window,
-                        doc_row=doc_row)
+        keep = admitted(rows[:, None] + q_offset, np.arange(Skv)[None, :], causal=causal,
+                        window=window, doc_row=doc_row, prefix=prefix)
         for j in range(nk):
             blk = keep[:, j * tile:(j + 1) * tile]
             if not blk.any():

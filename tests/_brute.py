@@ -8,9 +8,10 @@ import math
 
 
 def brute_attention(q, k, v, scale, *, causal=False, window=None, doc_ids=None,
-                    alibi_slopes=None, softcap=None):
+                    alibi_slopes=None, softcap=None, q_offset=0, prefix=None):
     """q: nested lists [B][H][Sq][D]; k, v: [B][Hkv][Skv][D]. Returns nested
-    lists O [B][H][Sq][D] and LSE [B][H][Sq]."""
+    lists O [B][H][Sq][D] and LSE [B][H][Sq]. Query i stands at key position
+    i + q_offset; with `prefix` the keys before it are exempt from causality."""
     B, H, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv, Skv = len(k[0]), len(k[0][0])
     O = [[[[0.0] * D for _ in range(Sq)] for _ in range(H)] for _ in range(B)]
@@ -19,20 +20,22 @@ def brute_attention(q, k, v, scale, *, causal=False, window=None, doc_ids=None,
         for h in range(H):
             g = h * Hkv // H          # query heads split into Hkv equal consecutive groups
             for i in range(Sq):
+                p = i + q_offset
                 kept = []
                 for j in range(Skv):
-                    if causal and j > i:
+                    in_prefix = prefix is not None and j < prefix
+                    if causal and j > p and not in_prefix:
                         continue
-                    if window and i - j >= window:
+                    if window and p - j >= window:
                         continue
-                    if doc_ids is not None and doc_ids[b][i] != doc_ids[b][j]:
+                    if doc_ids is not None and doc_ids[b][p] != doc_ids[b][j]:
                         continue
                     dot = 0.0
                     for d in range(D):
                         dot += q[b][h][i][d] * k[b][g][j][d]
                     s = dot * scale
                     if alibi_slopes is not None:
-                        s = s + alibi_slopes[h] * (j - i)
+                        s = s + alibi_slopes[h] * (j - p)
                     if softcap is not None:
                         s = softcap * math.tanh(s / softcap)
                     kept.append((j, s))

@@ -19,6 +19,9 @@ VARIANTS = [
     dict(alibi=True, causal=True),
     dict(softcap=2.0),
     dict(softcap=2.0, causal=True, window=4),
+    dict(causal=True, prefix=3),
+    dict(causal=True, q_offset=-2, alibi=True),
+    dict(causal=True, doc=True, q_offset=2, window=5),
 ]
 
 
@@ -32,9 +35,10 @@ def _inputs(seed, B=1, H=2, Hkv=1, S=6, D=3):
 
 
 def _kw(var, S, H):
-    kw = dict(causal=var.get("causal", False), window=var.get("window"))
+    kw = dict(causal=var.get("causal", False), window=var.get("window"),
+              q_offset=var.get("q_offset", 0), prefix=var.get("prefix"))
     if var.get("doc"):
-        kw["doc_ids"] = np.array([[0, 0, 0, 1, 1, 2, 2, 2][:S]])
+        kw["doc_ids"] = np.array([[0, 0, 0, 1, 1, 2, 2, 2][:S + max(0, kw["q_offset"])]])
     if var.get("alibi"):
         kw["alibi_slopes"] = np.array([0.5, 0.25][:H])
     if "softcap" in var:

@@ -239,6 +239,11 @@ BRUTE = [
     dict(alibi=True),
     dict(softcap=1.5),
     dict(causal=True, softcap=4.0, docs=True),
+    dict(causal=True, q_offset=3),
+    dict(causal=True, window=4, alibi=True, q_offset=2),
+    dict(docs=True, causal=True, q_offset=1, softcap=2.0),
+    dict(causal=True, prefix=4),
+    dict(causal=True, prefix=3, window=5, q_offset=2),
 ]
 
 
@@ -249,12 +254,14 @@ def test_matches_scalar_brute_force(kw, shape):
     B, H, Hkv, Sq, Skv, D = shape
     q, k, v = rnd((B, H, Sq, D), 35), rnd((B, Hkv, Skv, D), 36), rnd((B, Hkv, Skv, D), 37)
     doc = None
+    off = kw.get("q_offset", 0)
     if kw.get("docs"):
-        n = max(Sq, Skv)
+        n = max(Sq + off, Skv)
         doc = np.stack([document_ids(document_lengths(n, 40 + b, 2, 5)) for b in range(B)])
     slopes = alibi_slopes(H).astype(np.float64) if kw.get("alibi") else None
     args = dict(causal=kw.get("causal", False), window=kw.get("window"), doc_ids=doc,
-                alibi_slopes=slopes, softcap=kw.get("softcap"))
+                alibi_slopes=slopes, softcap=kw.get("softcap"), q_offset=off,
+                prefix=kw.get("prefix"))
     O, L = attention(q, k, v, 0.6, **args)
     Ob, Lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), 0.6,
                              **{a: (b.tolist() if isinstance(b, np.ndarray) else b)
@@ -275,6 +282,75 @@ def test_matches_torch_sdpa_float64(causal):
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.2)
     assert np.abs(O - ref.numpy()).max() < 1e-12
+
+
+# --------------------------------------------------------------- query offset and prefix-LM
+def sdpa_masked(q, k, v, scale, mask):
+    """torch's float64 attention with an explicit boolean mask [Sq, Skv]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask), scale=scale).numpy()
+
+
+def test_decode_step_sees_every_key():
+    """One query at the last position of a causal sequence attends to all keys:
+    plain (maskless) attention of that query."""
+    B, H, Skv, D = 2, 3, 37, 8
+    q, k, v = rnd((B, H, 1, D), 60), rnd((B, H, Skv, D), 61), rnd((B, H, Skv, D), 62)
+    O, L = attention(q, k, v, 0.3, causal=True, q_offset=Skv - 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.3).numpy()
+    assert np.abs(O - ref).max() < 1e-12
+    s = np.einsum("bhd,bhjd->bhj", q[:, :, 0], k) * 0.3
+    assert np.abs(L[:, :, 0] - np.log(np.exp(s).sum(-1))).max() < 1e-12
+
+
+def test_chunked_prefill_is_bottom_right_causal():
+    """Sq new queries after Skv - Sq cached keys: the causal mask is the lower
+    triangle shifted right by Skv - Sq (torch.tril with that diagonal)."""
+    Sq, Skv, D = 9, 23, 6
+    q, k, v = rnd((1, 2, Sq, D), 63), rnd((1, 2, Skv, D), 64), rnd((1, 2, Skv, D), 65)
+    O, _ = attention(q, k, v, 0.5, causal=True, q_offset=Skv - Sq)
+    mask = torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq).numpy()
+    assert np.abs(O - sdpa_masked(q, k, v, 0.5, mask)).max() < 1e-12
+
+
+def test_offset_rows_equal_rows_of_the_full_problem():
+    """Queries Skv-Sq..Skv-1 of a square problem, given as a chunk with their
+    offset, get the same rows (all variants that read positions)."""
+    Skv, Sq, D, H = 20, 7, 4, 4
+    q, k, v = rnd((1, H, Skv, D), 66), rnd((1, 2, Skv, D), 67), rnd((1, 2, Skv, D), 68)
+    doc = document_ids(document_lengths(Skv, 9, 3, 8))[None]
+    kw = dict(causal=True, window=6, doc_ids=doc, alibi_slopes=alibi_slopes(H).astype(np.float64))
+    Of, Lf = attention(q, k, v, 0.4, **kw)
+    Oc, Lc = attention(q[:, :, Skv - Sq:], k, v, 0.4, q_offset=Skv - Sq, **kw)
+    assert np.abs(Oc - Of[:, :, Skv - Sq:]).max() < 1e-12
+    assert np.abs(Lc - Lf[:, :, Skv - Sq:]).max() < 1e-12
+
+
+def test_prefix_lm_closed_forms():
+    S, D = 18, 5
+    q, k, v = rnd((1, 2, S, D), 69), rnd((1, 2, S, D), 70), rnd((1, 2, S, D), 71)
+    # a prefix covering every key is no mask at all; a prefix of 0 is causal
+    Od, _ = attention(q, k, v, 0.7)
+    assert np.abs(attention(q, k, v, 0.7, causal=True, prefix=S)[0] - Od).max() < 1e-12
+    Oc, _ = attention(q, k, v, 0.7, causal=True)
+    assert np.abs(attention(q, k, v, 0.7, causal=True, prefix=0)[0] - Oc).max() < 1e-12
+    # a prefix P: full block on the first P keys, causal after (explicit mask)
+    P = 7
+    mask = torch.ones(S, S, dtype=torch.bool).tril().numpy()
+    mask[:, :P] = True
+    assert np.abs(attention(q, k, v, 0.7, causal=True, prefix=P)[0]
+                  - sdpa_masked(q, k, v, 0.7, mask)).max() < 1e-12
+
+
+def test_offset_and_prefix_pair_counts():
+    # Sq queries after `off` cached keys, causal: query i sees off + i + 1 keys
+    Sq, off = 300, 500
+    assert pair_count(Sq, Sq + off, causal=True, q_offset=off) == Sq * off + Sq * (Sq + 1) // 2
+    # prefix P adds P(P - 1) / 2 pairs to causal (query q < P gains P - 1 - q keys)
+    S, P = 400, 130
+    assert pair_count(S, S, causal=True, prefix=P) == S * (S + 1) // 2 + P * (P - 1) // 2
 
 
 # --------------------------------------------------------------- mask and pair-count closed forms
