@@ -14,7 +14,7 @@ from dataclasses import dataclass
 import torch
 
 from ._lib import (  # noqa: F401
-    BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
+    BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_PREFIX, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
     MOD_SOFTCAP, QTILE, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
     flexattn_build_block_mask, flexattn_bwd, flexattn_fwd, flexattn_last_error, flexattn_strerror,
     flexattn_version, lib,
@@ -35,13 +35,16 @@ class Variant:
 
     causal: bool = False
     window: int = 0                       # > 0: keep keys with q - k < window
-    doc_ids: torch.Tensor | None = None   # int32 [B, >= max(Sq, Skv)] on the device
+    doc_ids: torch.Tensor | None = None   # int32 [B, >= max(Sq + q_offset, Skv)] on the device
     alibi_slopes: torch.Tensor | None = None  # float32 [H] on the device
     softcap: float | None = None
+    q_offset: int = 0                     # query row i sits at key position i + q_offset
+    prefix: int | None = None             # with causal: keys below it are seen by every query
 
     @property
     def mask_kind(self) -> int:
-        return mask_kind_of(self.causal, self.window, self.doc_ids is not None)
+        return mask_kind_of(self.causal, self.window, self.doc_ids is not None,
+                            self.prefix is not None)
 
     @property
     def mod_kind(self) -> int:
@@ -54,9 +57,9 @@ class Variant:
         return MOD_NONE
 
 
-def mask_kind_of(causal: bool, window: int, documents: bool) -> int:
+def mask_kind_of(causal: bool, window: int, documents: bool, prefix: bool = False) -> int:
     return ((MASK_CAUSAL if causal else 0) | (MASK_WINDOW if window and window > 0 else 0)
-            | (MASK_DOCUMENT if documents else 0))
+            | (MASK_DOCUMENT if documents else 0) | (MASK_PREFIX if prefix else 0))
 
 
 def make_params(var: Variant, dtype: torch.dtype) -> Params:
@@ -67,6 +70,8 @@ def make_params(var: Variant, dtype: torch.dtype) -> Params:
     p.window = int(var.window or 0)
     p.softcap = float(var.softcap) if var.softcap is not None else 0.0
     p.alibi_slopes = var.alibi_slopes.data_ptr() if var.alibi_slopes is not None else None
+    p.q_offset = int(var.q_offset)
+    p.prefix = int(var.prefix) if var.prefix is not None else 0
     if var.doc_ids is not None:
         if var.doc_ids.dtype != torch.int32 or not var.doc_ids.is_contiguous():
             raise TypeError("doc_ids must be a contiguous int32 tensor")

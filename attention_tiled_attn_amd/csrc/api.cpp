@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "../../include/flexattn.h"
 #include "launch.h"
@@ -25,17 +26,41 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0};
+const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0, 0, 0};
+
+constexpr int kMaskBits = FLEXATTN_MASK_CAUSAL | FLEXATTN_MASK_WINDOW | FLEXATTN_MASK_DOCUMENT |
+                          FLEXATTN_MASK_PREFIX;
+
+// The mask parameters a block mask depends on: 0 where the kind does not use
+// them (q_offset is used by every positional mask).
+struct MaskKey {
+  int window, q_offset, prefix;
+};
+MaskKey mask_key(int mask_kind, const flexattn_params* prm) {
+  MaskKey m{0, 0, 0};
+  if (mask_kind & FLEXATTN_MASK_WINDOW) m.window = prm->window;
+  if (mask_kind & FLEXATTN_MASK_PREFIX) m.prefix = prm->prefix;
+  if (mask_kind != FLEXATTN_MASK_NONE) m.q_offset = prm->q_offset;
+  return m;
+}
 
 // Checks shared by the forward pass and the block-mask builder.
 int check_mask_args(int mask_kind, const flexattn_params* prm, int B, int Sq, int Skv) {
   if (B < 1 || Sq < 1 || Skv < 1) return FLEXATTN_ERR_SHAPE;
-  if (mask_kind < 0 || mask_kind > 7) return FLEXATTN_ERR_UNSUPPORTED;
+  if (mask_kind < 0 || (mask_kind & ~kMaskBits)) return FLEXATTN_ERR_UNSUPPORTED;
   if ((mask_kind & FLEXATTN_MASK_WINDOW) && prm->window < 1) return FLEXATTN_ERR_ARG;
+  if (mask_kind & FLEXATTN_MASK_PREFIX) {
+    if (!(mask_kind & FLEXATTN_MASK_CAUSAL) || prm->prefix < 0) return FLEXATTN_ERR_ARG;
+  }
+  if (prm->q_offset < 0) return FLEXATTN_ERR_ARG;
+  // query positions i + q_offset (plus one query tile of rows past the end)
+  // stay in int range
+  if (static_cast<long long>(Sq) + prm->q_offset + FLEXATTN_QTILE > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
   if (mask_kind & FLEXATTN_MASK_DOCUMENT) {
     if (!prm->doc_ids) return FLEXATTN_ERR_NULLPTR;
     if (!aligned(prm->doc_ids, 4)) return FLEXATTN_ERR_ALIGN;
-    if (prm->doc_stride < (Sq > Skv ? Sq : Skv)) return FLEXATTN_ERR_ARG;
+    const long long need = std::max(static_cast<long long>(Sq) + prm->q_offset, static_cast<long long>(Skv));
+    if (prm->doc_stride < need) return FLEXATTN_ERR_ARG;
     if (static_cast<long long>(B) * prm->doc_stride > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
   }
   return FLEXATTN_OK;
@@ -65,7 +90,7 @@ const char* flexattn_strerror(int status) {
 const char* flexattn_last_error(void) { return g_last_error; }
 
 size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind) {
-  if (B < 1 || Sq < 1 || Skv < 1 || mask_kind < 0 || mask_kind > 7) return 0;
+  if (B < 1 || Sq < 1 || Skv < 1 || mask_kind < 0 || (mask_kind & ~kMaskBits)) return 0;
   const size_t nb = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? static_cast<size_t>(B) : 1;
   const size_t nq = static_cast<size_t>(ceil_div(Sq, FLEXATTN_QTILE));
   const size_t nk = static_cast<size_t>(ceil_div(Skv, FLEXATTN_TILE));
@@ -94,6 +119,9 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   ml.window = prm->window;
   ml.doc = prm->doc_ids;
   ml.doc_stride = prm->doc_stride;
+  const MaskKey key = mask_key(mask_kind, prm);
+  ml.q_offset = key.q_offset;
+  ml.prefix = key.prefix;
   ml.B = B;
   ml.Sq = Sq;
   ml.Skv = Skv;
@@ -115,6 +143,9 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   out->Skv = Skv;
   out->kv_count = counts;
   out->kv_list = lists;
+  out->window = key.window;
+  out->q_offset = key.q_offset;
+  out->prefix = key.prefix;
   return FLEXATTN_OK;
 }
 
@@ -158,12 +189,16 @@ int check_attn_args(const flexattn_params* prm, int B, int H, int Hkv, int Sq, i
       return FLEXATTN_ERR_BLOCKMASK;
     const int want_b = (mask_kind & FLEXATTN_MASK_DOCUMENT) ? B : 1;
     if (bm->num_b != want_b) return FLEXATTN_ERR_BLOCKMASK;
+    const MaskKey key = mask_key(mask_kind, prm);
+    if (bm->window != key.window || bm->q_offset != key.q_offset || bm->prefix != key.prefix)
+      return FLEXATTN_ERR_BLOCKMASK;
     if (!bm->kv_count || !bm->kv_list) return FLEXATTN_ERR_BLOCKMASK;
   }
   return FLEXATTN_OK;
 }
 
-void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, int mod_kind) {
+void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, int mask_kind,
+                  int mod_kind) {
   va.c1 = scale * fa::kLog2e;
   const float cap = mod_kind == FLEXATTN_MOD_SOFTCAP ? prm->softcap : 1.f;
   va.sc_in = 2.f * fa::kLog2e * scale / cap;
@@ -172,6 +207,8 @@ void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, 
   va.slopes = prm->alibi_slopes;
   va.doc = prm->doc_ids;
   va.doc_stride = prm->doc_stride;
+  va.q_offset = prm->q_offset;
+  va.prefix = (mask_kind & FLEXATTN_MASK_PREFIX) ? prm->prefix : 0;
 }
 
 }  // namespace
@@ -204,7 +241,7 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.is_fp32 = prm->dtype == FLEXATTN_FP32;
   p.mask_kind = mask_kind;
   p.mod_kind = mod_kind;
-  fill_variant(p.va, prm, scale, mod_kind);
+  fill_variant(p.va, prm, scale, mask_kind, mod_kind);
   p.kv_count = block_mask ? block_mask->kv_count : nullptr;
   p.kv_list = block_mask ? block_mask->kv_list : nullptr;
   p.nq = ceil_div(Sq, FLEXATTN_QTILE);
@@ -252,7 +289,7 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   p.mask_kind = mask_kind;
   p.mod_kind = mod_kind;
   p.scale = scale;
-  fill_variant(p.va, prm, scale, mod_kind);
+  fill_variant(p.va, prm, scale, mask_kind, mod_kind);
   p.kv_count = block_mask ? block_mask->kv_count : nullptr;
   p.kv_list = block_mask ? block_mask->kv_list : nullptr;
   p.nq = ceil_div(Sq, FLEXATTN_QTILE);

@@ -186,7 +186,8 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   if constexpr (MOD == kModAlibi) slope2 = p.va.slopes[h] * kLog2e;
   const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
-  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
+  const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
   // key-tile list: half qt % 2 of 256-row tile qt / 2; a tile empty for this
   // half is visited as partial (its masked scores give P = 0, adding nothing)
@@ -265,11 +266,11 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
           const int r = r0 + 2 * jj + x;
           const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           float dmod;
-          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, kidx - q_row, dmod);
+          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, kidx - q_pos, dmod);
           if (!full) {
             bool ok = kidx < p.Skv;
-            ok &= !(p.mask_kind & kMaskCausal) | (q_row >= kidx);
-            ok &= !(p.mask_kind & kMaskWindow) | (q_row - kidx < p.va.window);
+            ok &= !(p.mask_kind & kMaskCausal) | (q_pos >= kidx) | (kidx < p.va.prefix);
+            ok &= !(p.mask_kind & kMaskWindow) | (q_pos - kidx < p.va.window);
             if constexpr (DOCS) {
               const int lab = __builtin_amdgcn_raw_buffer_load_b32(rdoc, static_cast<unsigned>(kidx) * 4u, 0, 0);
               ok &= lab == doc_q;
@@ -365,13 +366,16 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
 
   // the 64-row query stages that can see keys [k_lo, k_hi] of this tile
+  // (query row r sits at position r + q_offset; keys below the prefix are
+  // exempt from the causal part)
   const bool causal = p.mask_kind & kMaskCausal;
   const bool window = p.mask_kind & kMaskWindow;
+  const int off = p.va.q_offset;
   const int k_lo = kt * kRows;
   const int k_hi = min(p.Skv, k_lo + kRows) - 1;
-  const int q_first = causal ? min(k_lo, p.Sq) : 0;
+  const int q_first = (causal && k_lo >= p.va.prefix) ? min(max(k_lo - off, 0), p.Sq) : 0;
   const int q_end = window ? static_cast<int>(min(static_cast<long long>(p.Sq),
-                                                  static_cast<long long>(k_hi) + p.va.window))
+                                                  static_cast<long long>(k_hi) + p.va.window - off))
                            : p.Sq;
   const int s0 = q_first / kStage;
   const int ns = q_end > q_first ? (q_end + kStage - 1) / kStage - s0 : 0;
@@ -438,8 +442,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
     // every pair of the stage in range and admitted?
     const int q_last = r0 + kStage - 1;
     bool full = !DOCS && q_last < p.Sq && k_hi == k_lo + kRows - 1;
-    if (causal) full = full && r0 >= k_hi;
-    if (window) full = full && (q_last - k_lo < p.va.window);
+    if (causal) full = full && (r0 + off >= k_hi || k_hi < p.va.prefix);
+    if (window) full = full && (q_last + off - k_lo < p.va.window);
     float slope2 = 0.f;
     if constexpr (MOD == kModAlibi) slope2 = p.va.slopes[hh] * kLog2e;
 
@@ -471,7 +475,7 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + ql0);
         u32x4 lab = {0u, 0u, 0u, 0u};
         if constexpr (DOCS) {
-          if (!full) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0) * 4u, 0, 0);
+          if (!full) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0 + off) * 4u, 0, 0);
         }
         float pv[4], dv4[4];
 #pragma unroll
@@ -479,11 +483,12 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
           const int i = i0 + 4 * hv + x;
           const int qrow = r0 + ql0 + x;
           float dmod;
-          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, k_row - qrow, dmod);
+          const int qpos = qrow + off;
+          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, k_row - qpos, dmod);
           if (!full) {
             bool ok = k_ok && qrow < p.Sq;
-            ok &= !causal | (qrow >= k_row);
-            ok &= !window | (qrow - k_row < p.va.window);
+            ok &= !causal | (qpos >= k_row) | (k_row < p.va.prefix);
+            ok &= !window | (qpos - k_row < p.va.window);
             if constexpr (DOCS) ok &= static_cast<int>(lab[x]) == doc_k;
             tt = ok ? tt : -INFINITY;
           }

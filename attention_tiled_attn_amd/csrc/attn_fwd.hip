@@ -274,11 +274,12 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   float l_run = 0.f;
 
   using SM = ScoreMod<MOD>;
-  const typename SM::Lane sml = SM::lane(p.va, h, q_row);
+  const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
+  const typename SM::Lane sml = SM::lane(p.va, h, q_pos);
   // document labels of this batch row (document-mask kernels only)
   const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
-  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
   int ent_cur = 0, ent_next = 0;   // entries of stages it and it + 1
   if (n_stages > 0) {
@@ -341,7 +342,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
+        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_pos);
       }
     if (!full) {
       // Branch-free predicate. The four keys 8*i + 4*g + (0..3) of a block are
@@ -360,8 +361,8 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
           for (int e = 0; e < 4; ++e) {
             const int kidx = k0 + e;
             bool ok = kidx < p.Skv;
-            ok &= !causal | (q_row >= kidx);
-            ok &= !window | (q_row - kidx < p.va.window);
+            ok &= !causal | (q_pos >= kidx) | (kidx < p.va.prefix);
+            ok &= !window | (q_pos - kidx < p.va.window);
             if constexpr (DOCS) ok &= static_cast<int>(lab[e]) == doc_q;
             t[kb * 16 + 4 * i + e] = ok ? t[kb * 16 + 4 * i + e] : -INFINITY;
           }

@@ -187,10 +187,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   float m_run = -INFINITY;
   float l_run = 0.f;
   using SM = ScoreMod<MOD>;
-  const typename SM::Lane sml = SM::lane(p.va, h, q_row);
+  const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
+  const typename SM::Lane sml = SM::lane(p.va, h, q_pos);
   const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
-  const int doc_q = (DOCS && q_ok) ? doc_row[q_row] : 0;
+  const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
   bf16x8 pf[4];
 
@@ -248,7 +249,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_row);
+        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_pos);
       }
     const float ninf = -INFINITY;
     if (!full) {
@@ -265,8 +266,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
           for (int e = 0; e < 4; ++e) {
             const int kidx = k0 + e;
             bool ok = kidx < p.Skv;
-            ok &= !causal | (q_row >= kidx);
-            ok &= !window | (q_row - kidx < p.va.window);
+            ok &= !causal | (q_pos >= kidx) | (kidx < p.va.prefix);
+            ok &= !window | (q_pos - kidx < p.va.window);
             if constexpr (DOCS) ok &= static_cast<int>(lab[e]) == doc_q;
             mask_in_place(t[kb * 16 + 4 * i + e], ok, ninf);
           }

@@ -9,9 +9,13 @@
 // full ones is how a sparse variant (sliding window, document packing) runs at
 // dense-tile speed on the tiles it does compute.
 //
-// The causal and window parts act on the difference d = q - k, and over a
-// rectangle of positions d takes every integer between its extremes, so those
-// two parts are classified exactly from the rectangle's corners. The document
+// Query rows stand at positions row + q_offset. The causal and window parts
+// act on the difference d = q - k of positions, and over a rectangle of
+// positions d takes every integer between its extremes, so those two parts are
+// classified exactly from the rectangle's corners. Under a prefix-LM mask the
+// keys below the prefix drop the causal part: a tile is split at the prefix
+// and each side classified exactly, the tile being full when both sides are
+// and empty when both are. The document
 // part is classified from the label ranges of the query rows and of the keys;
 // where they cannot tell "empty" from "partial" the tile is kept as partial.
 // Keys at or past Skv never count as admitted, so a tile that reaches past Skv
@@ -70,19 +74,32 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
   const bool docs = p.mask_kind & kMaskDocument;
   const int* doc = docs ? p.doc + static_cast<size_t>(bb) * p.doc_stride : nullptr;
 
+  // positions of each half's rows
   int q_lo[2], q_hi[2], dq_min[2] = {0, 0}, dq_max[2] = {0, 0};
   bool live[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    q_lo[hf] = qp * 2 * kTile + hf * kTile;
-    q_hi[hf] = min(p.Sq, q_lo[hf] + kTile) - 1;
-    live[hf] = q_lo[hf] < p.Sq;
+    const int r_lo = qp * 2 * kTile + hf * kTile;
+    live[hf] = r_lo < p.Sq;
+    q_lo[hf] = r_lo + p.q_offset;
+    q_hi[hf] = min(p.Sq, r_lo + kTile) - 1 + p.q_offset;
     if (docs && live[hf]) label_range(doc, q_lo[hf], q_hi[hf], lane, dq_min[hf], dq_max[hf]);
   }
 
-  // admitted differences d = q - k form the interval [lo_d, hi_d]
+  // admitted differences d = q - k form the interval [lo_d, hi_d]; keys
+  // below the prefix take [lo_p, hi_d] (no causal bound)
   const long long lo_d = causal ? 0 : -(1LL << 40);
+  const long long lo_p = -(1LL << 40);
   const long long hi_d = window ? static_cast<long long>(p.window) - 1 : (1LL << 40);
+  const int prefix = causal ? p.prefix : 0;
+  // class of rows [qa, qb] x keys [ka, kb] under d in [lo, hi]
+  auto rect = [&](int qa, int qb, int ka, int kb, long long lo) -> int {
+    const long long dmin = static_cast<long long>(qa) - kb;
+    const long long dmax = static_cast<long long>(qb) - ka;
+    if (dmax < lo || dmin > hi_d) return kEmpty;
+    if (dmin >= lo && dmax <= hi_d) return kFull;
+    return kPartial;
+  };
 
   int* out = p.kv_list + (static_cast<size_t>(bb) * p.nq + qp) * p.nk;
   int n = 0;
@@ -97,11 +114,18 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
     bool need_labels = false;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const long long dmin = static_cast<long long>(q_lo[hf]) - k_hi;
-      const long long dmax = static_cast<long long>(q_hi[hf]) - k_lo;
-      if (!valid || !live[hf] || dmax < lo_d || dmin > hi_d) cls[hf] = kEmpty;
-      else if (dmin >= lo_d && dmax <= hi_d) cls[hf] = kFull;
-      else cls[hf] = kPartial;
+      if (!valid || !live[hf]) {
+        cls[hf] = kEmpty;
+      } else if (k_lo >= prefix) {
+        cls[hf] = rect(q_lo[hf], q_hi[hf], k_lo, k_hi, lo_d);
+      } else if (k_hi < prefix) {
+        cls[hf] = rect(q_lo[hf], q_hi[hf], k_lo, k_hi, lo_p);
+      } else {
+        const int a = rect(q_lo[hf], q_hi[hf], k_lo, prefix - 1, lo_p);
+        const int c = rect(q_lo[hf], q_hi[hf], prefix, k_hi, lo_d);
+        cls[hf] = (a == kEmpty && c == kEmpty) ? kEmpty
+                  : (a == kFull && c == kFull) ? kFull : kPartial;
+      }
       need_labels = need_labels || cls[hf] != kEmpty;
     }
     if (docs && need_labels) {

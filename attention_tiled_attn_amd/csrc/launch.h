@@ -66,6 +66,8 @@ struct MaskLaunch {
   int window;
   const int* doc;
   int doc_stride;
+  int q_offset;   // position of query row 0
+  int prefix;     // prefix-LM boundary (0 = none)
   int B, Sq, Skv;
   int nq, nk, num_b;
   int* kv_count;

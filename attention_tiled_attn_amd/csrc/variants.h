@@ -22,7 +22,7 @@ namespace fa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-enum : int { kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 4 };
+enum : int { kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 4, kMaskPrefix = 8 };
 enum : int { kModNone = 0, kModAlibi = 1, kModSoftcap = 2 };
 
 // Per-call constants the functors read. Filled on the host.
@@ -34,6 +34,8 @@ struct VariantArgs {
   const float* slopes;  // ALiBi slopes [H]
   const int* doc;       // document labels [B][doc_stride]
   int doc_stride;
+  int q_offset;      // position of query row 0 in the key sequence
+  int prefix;        // causal part admits keys below it too (0 = plain causal)
 };
 
 // ---------------------------------------------------------------- score_mod
@@ -82,15 +84,9 @@ struct ScoreMod<kModSoftcap> {
 };
 
 // ---------------------------------------------------------------- mask_mod
-// Per-element predicate for partial tiles: causal q >= k, window q - k < W,
-// document doc[q] == doc[k]; AND-composed by the flag word `kind`.
-// `doc_row` points at this batch row's labels; `doc_q` is doc_row[q].
-__device__ inline bool admit(int kind, int q, int k, int window, const int* doc_row, int doc_q) {
-  bool ok = true;
-  if (kind & kMaskCausal) ok = ok && (q >= k);
-  if (kind & kMaskWindow) ok = ok && (q - k < window);
-  if (kind & kMaskDocument) ok = ok && (doc_row[k] == doc_q);
-  return ok;
-}
+// The kernels evaluate the per-element predicate inline on partial tiles, on
+// positions (query row + q_offset, key index): causal q >= k, relaxed to
+// q >= k || k < prefix for prefix-LM; window q - k < W; document
+// doc[q] == doc[k]; AND-composed by the flag word of the mask kind.
 
 }  // namespace fa

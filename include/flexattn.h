@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_VERSION 1
+#define FLEXATTN_VERSION 2
 
 /* Block-mask tiles: FLEXATTN_QTILE query rows (two halves of FLEXATTN_TILE
  * rows) by FLEXATTN_TILE keys. */
@@ -67,25 +67,38 @@ enum flexattn_status {
  * run on bf16 matrix cores with float32 accumulation; O is stored as float32. */
 enum flexattn_dtype { FLEXATTN_BF16 = 0, FLEXATTN_FP32 = 1 };
 
-/* mask_mod kinds: bit flags, AND-composed; 0 = every key admitted.
+/* Positions. Key j sits at position k_idx = j; query row i sits at position
+ * q_idx = i + params->q_offset (0 by default: rows and keys start together).
+ * Masks, score mods and document labels see positions, so decoding or a
+ * prefill chunk that follows Skv - Sq cached keys passes q_offset = Skv - Sq.
+ *
+ * mask_mod kinds: bit flags, AND-composed; 0 = every key admitted.
  *   CAUSAL   : q_idx >= k_idx
  *   WINDOW   : q_idx - k_idx < params->window       (combine with CAUSAL for a
  *                                                      causal sliding window)
- *   DOCUMENT : doc[b][q_idx] == doc[b][k_idx]        (document packing)        */
+ *   DOCUMENT : doc[b][q_idx] == doc[b][k_idx]        (document packing)
+ *   PREFIX   : with CAUSAL only: the causal part becomes
+ *              q_idx >= k_idx || k_idx < params->prefix (prefix-LM: the prefix
+ *              is seen by every query; WINDOW and DOCUMENT still apply)
+ * The pages name prefix masking among FlexAttention's variants without
+ * defining it (PyTorch 2.5 / FlexAttention article, overview and "What
+ * Happened?"); the prefix-LM reading above is this library's.              */
 enum flexattn_mask_kind {
   FLEXATTN_MASK_NONE = 0,
   FLEXATTN_MASK_CAUSAL = 1,
   FLEXATTN_MASK_WINDOW = 2,
-  FLEXATTN_MASK_DOCUMENT = 4
+  FLEXATTN_MASK_DOCUMENT = 4,
+  FLEXATTN_MASK_PREFIX = 8
 };
 
 /* score_mod kinds, applied to the scaled score s = scale * q.k:
- *   ALIBI   : s + alibi_slopes[h] * (k_idx - q_idx)
+ *   ALIBI   : s + alibi_slopes[h] * (k_idx - q_idx)      (positions, as above)
  *   SOFTCAP : softcap * tanh(s / softcap)                                       */
 enum flexattn_mod_kind { FLEXATTN_MOD_NONE = 0, FLEXATTN_MOD_ALIBI = 1, FLEXATTN_MOD_SOFTCAP = 2 };
 
 /* Parameters of the variants. Host struct, read during the call only.
- * A NULL params pointer means: dtype BF16, no window, no documents, no mods. */
+ * A NULL params pointer means: dtype BF16, no window, no documents, no mods,
+ * q_offset 0. */
 typedef struct flexattn_params {
   int dtype;                 /* enum flexattn_dtype                                   */
   int window;                /* > 0 when the mask has FLEXATTN_MASK_WINDOW            */
@@ -93,7 +106,10 @@ typedef struct flexattn_params {
   const float* alibi_slopes; /* device float32 [H] when mod_kind is FLEXATTN_MOD_ALIBI */
   const int* doc_ids;        /* device int32 [B][doc_stride] document label per position,
                                 when the mask has FLEXATTN_MASK_DOCUMENT               */
-  int doc_stride;            /* elements per batch row of doc_ids, >= max(Sq, Skv)    */
+  int doc_stride;            /* elements per batch row of doc_ids,
+                                >= max(Sq + q_offset, Skv)                            */
+  int q_offset;              /* >= 0: position of query row 0 (see "Positions")       */
+  int prefix;                /* >= 0 when the mask has FLEXATTN_MASK_PREFIX           */
 } flexattn_params;
 
 /* Block mask: for every query tile of FLEXATTN_QTILE rows, the ascending list
@@ -118,6 +134,8 @@ typedef struct flexattn_block_mask {
   const int* kv_count;  /* device int32 [num_b][nq]: entries in each list        */
   const int* kv_list;   /* device int32 [num_b][nq][nk]: entries as above,
                            ascending; entries past kv_count are unspecified      */
+  int window, q_offset, prefix;  /* the params it was built for (0 where the mask
+                                    kind does not use them)                      */
 } flexattn_block_mask;
 
 /* Library version (FLEXATTN_VERSION of the build). */
@@ -136,8 +154,10 @@ size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind);
 /* Classify every (query half-tile, key tile) pair of the mask as full,
  * partial or empty and write the per-query-tile key-tile lists into `buf` (device memory
  * of at least flexattn_block_mask_bytes(B, Sq, Skv, mask_kind) bytes, 4-byte
- * aligned). `params` supplies window and doc_ids as for flexattn_fwd (may be
- * NULL when the mask needs neither). On success fills *out, whose pointers
+ * aligned). `params` supplies window, doc_ids, q_offset and prefix as for
+ * flexattn_fwd (may be NULL when the mask needs none of them). On success
+ * fills *out (which records those parameters: a call whose params differ
+ * where the mask uses them gets FLEXATTN_ERR_BLOCKMASK), whose pointers
  * point into buf, and enqueues the build on `stream`. A half is marked full
  * exactly when every pair in it is in range and admitted, and absent only when
  * no pair in it is admitted. Without DOCUMENT masks the classes are exact;

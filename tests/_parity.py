@@ -36,7 +36,7 @@ def pair_lists(ref: np.ndarray) -> list[list[int]]:
 
 
 def check_pair_lists(counts: np.ndarray, lists: np.ndarray, ref: np.ndarray, Sq: int, Skv: int,
-                     doc_row: np.ndarray | None = None) -> int:
+                     doc_row: np.ndarray | None = None, q_offset: int = 0) -> int:
     """Check the block-mask lists of one batch row against per-(128-row tile,
     128-key tile) classes `ref` (0 empty, 1 partial, 2 full). Without documents
     the lists must equal pair_lists(ref). With documents, full and partial
@@ -69,7 +69,7 @@ def check_pair_lists(counts: np.ndarray, lists: np.ndarray, ref: np.ndarray, Sq:
                 else:
                     assert g in (0, 1), (qp, j, hf)
                     if g == 1:
-                        ql = doc_row[qt * 128:min(Sq, qt * 128 + 128)]
+                        ql = doc_row[qt * 128 + q_offset:min(Sq, qt * 128 + 128) + q_offset]
                         kl = doc_row[j * 128:min(Skv, j * 128 + 128)]
                         overlap = ql.min() <= kl.max() and kl.min() <= ql.max()
                         single = ql.min() == ql.max() == kl.min() == kl.max()
@@ -87,6 +87,8 @@ def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
         doc_ids=torch.from_numpy(inp.doc_ids).to(device) if inp.doc_ids is not None else None,
         alibi_slopes=torch.from_numpy(inp.slopes).to(device) if inp.slopes is not None else None,
         softcap=wl.softcap if wl.mod == "softcap" else None,
+        q_offset=wl.q_offset,
+        prefix=wl.prefix,
     )
 
 
@@ -105,7 +107,8 @@ def oracle_kwargs(inp: Inputs) -> dict:
     wl = inp.wl
     return dict(causal=wl.causal, window=wl.window or None, doc_ids=inp.doc_ids,
                 alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
-                softcap=wl.softcap if wl.mod == "softcap" else None)
+                softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
+                prefix=wl.prefix)
 
 
 def run_oracle(inp: Inputs, rows=None, heads=None):
@@ -152,20 +155,21 @@ def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0) ->
 
 def small(name="t", *, B=1, H=2, Hkv=None, S=200, Sq=None, Skv=None, D=64, dtype="bf16",
           causal=False, window=0, documents=False, mod="none", softcap=30.0, seed=7,
-          doc_range=(16, 96)) -> Inputs:
-    """Small seeded inputs (Sq and Skv may differ)."""
+          doc_range=(16, 96), q_offset=0, prefix=None) -> Inputs:
+    """Small seeded inputs (Sq and Skv may differ; query row i at key
+    position i + q_offset)."""
     from workload import alibi_slopes, as_element_type, document_ids, document_lengths, draw_qkv
     Hkv = Hkv or H
     Sq = Sq or S
     Skv = Skv or S
     wl = Workload(name, B=B, H=H, Hkv=Hkv, S=S, D=D, dtype=dtype, causal=causal, window=window,
                   documents=documents, mod=mod, softcap=softcap, seed=seed, doc_seed=seed,
-                  doc_len_range=doc_range)
+                  doc_len_range=doc_range, q_offset=q_offset, prefix=prefix)
     q, k, v = draw_qkv(B, H, Hkv, Sq, Skv, D, seed)
     q, k, v = (as_element_type(t, dtype) for t in (q, k, v))
     doc = None
     if documents:
-        n = max(Sq, Skv)
+        n = max(Sq + q_offset, Skv)
         doc = np.stack([document_ids(document_lengths(n, seed + b, *doc_range)) for b in range(B)])
     slopes = alibi_slopes(H) if mod == "alibi" else None
     return Inputs(_SqSkv(wl, Sq, Skv), q, k, v, doc, slopes)

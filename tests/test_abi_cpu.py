@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.flexattn_version() == 1
+    assert fa.flexattn_version() == 2
     for code in range(-8, 1):
         assert fa.flexattn_strerror(code) and fa.flexattn_strerror(code) != "unknown status"
     assert fa.flexattn_strerror(-99) == "unknown status"
@@ -55,7 +55,7 @@ def test_block_mask_bytes():
     assert fa.flexattn_block_mask_bytes(2, 256, 384, 1) == 1 * 1 * (1 + 3) * 4
     assert fa.flexattn_block_mask_bytes(2, 257, 384, 4) == 2 * 2 * (1 + 3) * 4
     assert fa.flexattn_block_mask_bytes(1, 129, 129, 0) == 1 * 3 * 4
-    for bad in [(0, 128, 128, 0), (1, 0, 128, 0), (1, 128, -1, 0), (1, 128, 128, 8),
+    for bad in [(0, 128, 128, 0), (1, 0, 128, 0), (1, 128, -1, 0), (1, 128, 128, 16),
                 (1, 128, 128, -1)]:
         assert fa.flexattn_block_mask_bytes(*bad) == 0
 
@@ -83,6 +83,8 @@ def P(**kw):
     p.alibi_slopes = kw.get("alibi_slopes")
     p.doc_ids = kw.get("doc_ids")
     p.doc_stride = kw.get("doc_stride", 0)
+    p.q_offset = kw.get("q_offset", 0)
+    p.prefix = kw.get("prefix", 0)
     return p
 
 
@@ -99,7 +101,13 @@ def P(**kw):
     (dict(Skv=-5), _lib.ERR_SHAPE),
     (dict(D=96), _lib.ERR_UNSUPPORTED),
     (dict(D=256), _lib.ERR_UNSUPPORTED),
-    (dict(mask_kind=8), _lib.ERR_UNSUPPORTED),
+    (dict(mask_kind=16), _lib.ERR_UNSUPPORTED),
+    (dict(mask_kind=8), _lib.ERR_ARG),                                   # prefix without causal
+    (dict(mask_kind=10, params=P(window=4)), _lib.ERR_ARG),
+    (dict(mask_kind=9, params=P(prefix=-1)), _lib.ERR_ARG),
+    (dict(params=P(q_offset=-1)), _lib.ERR_ARG),
+    (dict(mask_kind=1, params=P(q_offset=2**31 - 300)), _lib.ERR_OVERFLOW),
+    (dict(mask_kind=4, params=P(doc_ids=A, doc_stride=128, q_offset=1)), _lib.ERR_ARG),  # stride < Sq + off
     (dict(mask_kind=-1), _lib.ERR_UNSUPPORTED),
     (dict(mod_kind=3), _lib.ERR_UNSUPPORTED),
     (dict(params=P(dtype=7)), _lib.ERR_UNSUPPORTED),
@@ -140,6 +148,9 @@ def bm_struct(**kw):
     s.Skv = kw.get("Skv", 128)
     s.kv_count = kw.get("kv_count", A)
     s.kv_list = kw.get("kv_list", A)
+    s.window = kw.get("window", 0)
+    s.q_offset = kw.get("q_offset", 0)
+    s.prefix = kw.get("prefix", 0)
     return s
 
 
@@ -149,6 +160,27 @@ def bm_struct(**kw):
 ])
 def test_fwd_rejects_mismatched_block_mask(kw):
     assert call(block_mask=bm_struct(**kw)) == _lib.ERR_BLOCKMASK
+
+
+@pytest.mark.parametrize("mk,params,kw,code", [
+    # the parameters a block mask was built with must match where the mask uses them
+    (3, dict(window=64), dict(window=64), _lib.OK),
+    (3, dict(window=64), dict(window=65), _lib.ERR_BLOCKMASK),
+    (1, dict(q_offset=5), dict(q_offset=5), _lib.OK),
+    (1, dict(q_offset=5), dict(), _lib.ERR_BLOCKMASK),
+    (9, dict(prefix=40), dict(prefix=40), _lib.OK),
+    (9, dict(prefix=40), dict(prefix=41), _lib.ERR_BLOCKMASK),
+    (1, dict(prefix=40), dict(), _lib.OK),            # no PREFIX bit: prefix unused
+    (0, dict(q_offset=5, window=3), dict(), _lib.OK),  # no mask: nothing positional
+])
+def test_block_mask_records_its_params(mk, params, kw, code):
+    bm = bm_struct(mask_kind=mk, **kw)
+    if code == _lib.OK:
+        # a matching mask passes validation; the misaligned output, checked
+        # after the mask, stops the call before any launch
+        assert call(mask_kind=mk, params=P(**params), block_mask=bm, out=A + 2) == _lib.ERR_ALIGN
+    else:
+        assert call(mask_kind=mk, params=P(**params), block_mask=bm) == code
 
 
 def test_build_block_mask_validation():
@@ -161,7 +193,9 @@ def test_build_block_mask_validation():
     assert b(1, None, 1, 256, 256, None, need) == _lib.ERR_NULLPTR
     assert b(1, None, 1, 256, 256, A + 2, need) == _lib.ERR_ALIGN
     assert b(1, None, 1, 256, 256, A, need - 4) == _lib.ERR_ARG
-    assert b(9, None, 1, 256, 256, A, need) == _lib.ERR_UNSUPPORTED
+    assert b(17, None, 1, 256, 256, A, need) == _lib.ERR_UNSUPPORTED
+    assert b(8, None, 1, 256, 256, A, need) == _lib.ERR_ARG          # prefix needs causal
+    assert b(1, P(q_offset=-3), 1, 256, 256, A, need) == _lib.ERR_ARG
     assert b(1, None, 0, 256, 256, A, need) == _lib.ERR_SHAPE
     assert b(2, None, 1, 256, 256, A, need) == _lib.ERR_ARG          # window needs params
     assert b(4, P(), 1, 256, 256, A, need) == _lib.ERR_NULLPTR        # documents need labels

@@ -84,6 +84,24 @@ def test_backward_shapes(shape):
     check(small(D=64, **shape), f"{shape}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(Sq=1, Skv=300, q_offset=299, causal=True),
+    dict(Sq=64, Skv=500, q_offset=436, causal=True, window=100, mod="alibi"),
+    dict(Sq=200, Skv=700, q_offset=500, causal=True, documents=True),
+    dict(Sq=150, Skv=150, q_offset=30, window=40, mod="softcap", softcap=5.0),
+    dict(S=400, causal=True, prefix=150),
+    dict(S=333, causal=True, prefix=129, window=90, documents=True),
+    dict(Sq=100, Skv=600, q_offset=500, causal=True, prefix=256, mod="alibi"),
+], ids=lambda c: ",".join(f"{a}={b}" for a, b in c.items()))
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_offset_and_prefix(case, D):
+    inp = small(D=D, H=4, Hkv=2, doc_range=(40, 300), **case)
+    check(inp, f"D={D} {case}")
+    (a, _), (b, _) = run_bwd(inp, "auto"), run_bwd(inp, None)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), case
+
+
 def test_backward_longer_causal_gqa():
     check(small(B=1, H=4, Hkv=2, S=1100, D=128, causal=True), "S=1100 causal GQA D=128")
 

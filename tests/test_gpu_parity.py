@@ -133,6 +133,50 @@ def test_split_kv_merge_identity():
     assert (Om - O.float()).abs().max().item() < 2e-2
 
 
+# ------------------------------------------------------------------ query offset and prefix-LM
+# Decoding and chunked prefill: Sq queries after Skv - Sq cached keys, so
+# q_offset = Skv - Sq; prefix-LM: keys below the prefix seen by every query.
+OFFSET_CASES = [
+    dict(Sq=1, Skv=300, q_offset=299, causal=True),
+    dict(Sq=5, Skv=1000, q_offset=995, causal=True, mod="alibi"),
+    dict(Sq=64, Skv=777, q_offset=713, causal=True, window=100),
+    dict(Sq=300, Skv=1000, q_offset=700, causal=True, documents=True),
+    dict(Sq=257, Skv=513, q_offset=256, causal=True, mod="softcap", softcap=5.0),
+    dict(Sq=200, Skv=640, q_offset=77, causal=True, window=150, documents=True, mod="alibi"),
+    dict(Sq=130, Skv=130, q_offset=40, window=30),                 # window only, offset
+    dict(S=600, causal=True, prefix=200),
+    dict(S=333, causal=True, prefix=129, window=100),
+    dict(S=500, causal=True, prefix=300, documents=True),
+    dict(S=300, causal=True, prefix=1000, mod="alibi"),            # prefix past the end: dense
+    dict(Sq=100, Skv=700, q_offset=600, causal=True, prefix=256, mod="softcap", softcap=5.0),
+]
+
+
+@pytest.mark.parametrize("case", OFFSET_CASES, ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+@pytest.mark.parametrize("D", [64, 128])
+def test_offset_and_prefix(case, D):
+    inp = small(D=D, doc_range=(40, 300), **case)
+    check_full(inp, what=f"D={D} {case}")
+    # the block mask must not change a single bit
+    O1, L1 = run_gpu(inp)
+    O2, L2 = run_gpu(inp, block_mask=None)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+@pytest.mark.parametrize("case", OFFSET_CASES, ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+def test_block_mask_offset_and_prefix(case):
+    inp = small(doc_range=(40, 300), **case)
+    wl = inp.wl
+    bm = fa.build_block_mask(device_variant(inp), wl.B, wl.Sq, wl.Skv)
+    torch.cuda.synchronize()
+    counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
+    for b in range(counts.shape[0]):
+        doc_row = None if inp.doc_ids is None else inp.doc_ids[b]
+        ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
+                                  doc_row=doc_row, q_offset=wl.q_offset, prefix=wl.prefix)
+        check_pair_lists(counts[b], lists[b], ref, wl.Sq, wl.Skv, doc_row, wl.q_offset)
+
+
 # ------------------------------------------------------------------ block-mask builder
 @pytest.mark.parametrize("case", [
     dict(S=1000, causal=True), dict(S=1000, causal=True, window=300), dict(S=777, window=200),

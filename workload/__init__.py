@@ -40,6 +40,8 @@ class Workload:
     softcap: float = 30.0
     seed: int = 0
     doc_seed: int = 0
+    q_offset: int = 0           # query row i sits at key position i + q_offset
+    prefix: int | None = None   # prefix-LM boundary (with causal), or None
 
     @property
     def Sq(self) -> int:
@@ -164,7 +166,7 @@ def make_inputs(wl: Workload) -> Inputs:
     doc = None
     if wl.documents:
         # batch row b draws its document layout from seed doc_seed + b
-        doc = np.stack([document_ids(document_lengths(max(wl.Sq, wl.Skv), wl.doc_seed + b,
+        doc = np.stack([document_ids(document_lengths(max(wl.Sq + wl.q_offset, wl.Skv), wl.doc_seed + b,
                                                       *wl.doc_len_range))
                         for b in range(wl.B)]).astype(np.int32)
     slopes = alibi_slopes(wl.H) if wl.mod == "alibi" else None
