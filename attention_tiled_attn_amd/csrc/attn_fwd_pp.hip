@@ -84,6 +84,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
+  // document labels of each ring slot's 64 keys (copied with K by wave 0)
+  __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kRing * kBN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,13 +173,30 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   }
   const unsigned my_lds =
       __builtin_amdgcn_readfirstlane(lds_addr(grp ? vbuf : kbuf) + wq * G::kDma * 1024);
+  // document labels: wave 0 also copies the stage's 64 labels (16 lanes x 16
+  // bytes), so it has one more copy in flight per stage than the other waves
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const bool lab_wave = DOCS && __builtin_amdgcn_readfirstlane(wave) == 0;
+  const u32x4 ldesc = make_desc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
+  const unsigned lab_lds = lds_addr(labbuf);
   // group 0 copies K(t), group 1 V(t), into ring slot `ring`
   auto issue_copy = [&](int t, int e, int ring) {
-    const unsigned gbase = static_cast<unsigned>(stage_kv0(t, e)) * RB;
+    const int kv0 = stage_kv0(t, e);
+    const unsigned gbase = static_cast<unsigned>(kv0) * RB;
     const unsigned lbase = my_lds + ring * G::kBufBytes;
 #pragma unroll
     for (int j = 0; j < G::kDma; ++j)
       copy_to_lds(desc, gbase + goff[j], __builtin_amdgcn_readfirstlane(lbase + j * 1024));
+    if constexpr (DOCS) {
+      if (lab_wave && lane < 16)
+        copy_to_lds(ldesc, static_cast<unsigned>(kv0 + 4 * lane) * 4u,
+                    __builtin_amdgcn_readfirstlane(lab_lds + ring * kBN * 4));
+    }
+  };
+  // this wave's copies of the stage before the newest are complete
+  auto wait_prev_stage = [&]() {
+    if (lab_wave) wait_vm<G::kDma + 1>();
+    else wait_vm<G::kDma>();
   };
 
   // ---- running state
@@ -189,8 +208,6 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   using SM = ScoreMod<MOD>;
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
   const typename SM::Lane sml = SM::lane(p.va, h, q_pos);
-  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
-  const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
   bf16x8 pf[4];
@@ -242,7 +259,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   };
 
   // online softmax of one stage: scores -> P^T (bf16) in pf, running max/sum
-  auto softmax = [&](const f32x16 (&s)[2], int kv0, bool full) {
+  auto softmax = [&](const f32x16 (&s)[2], int kv0, bool full, int ring) {
     float t[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -253,22 +270,33 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       }
     const float ninf = -INFINITY;
     if (!full) {
+      // The causal part (with its prefix), the window and the key range each
+      // admit an interval of key positions for this row, so together they
+      // admit keys kk0 + c for c in [lo, hi], where element (kb, i, e) of this
+      // lane is key kk0 + c with c = 32 kb + 8 i + e. Bounds are formed in 64
+      // bits and clamped to the stage, then every element takes two compares
+      // against a constant (and the document test against staged labels).
       const bool causal = p.mask_kind & kMaskCausal;
       const bool window = p.mask_kind & kMaskWindow;
+      const int kk0 = kv0 + 4 * g;
+      const long long d = static_cast<long long>(q_pos) - kk0;
+      long long hi = static_cast<long long>(p.Skv) - 1 - kk0;
+      if (causal) hi = min(hi, max(d, static_cast<long long>(p.va.prefix) - 1 - kk0));
+      const long long lo = window ? d - p.va.window + 1 : 0LL;
+      const int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBN)));
+      const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
+      const int* lab = labbuf + (DOCS ? ring * kBN + 4 * g : 0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int k0 = kv0 + kb * 32 + 8 * i + 4 * g;
-          u32x4 lab = {0u, 0u, 0u, 0u};
-          if constexpr (DOCS) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(k0) * 4u, 0, 0);
+          u32x4 l4 = {0u, 0u, 0u, 0u};
+          if constexpr (DOCS) l4 = *reinterpret_cast<const u32x4*>(lab + kb * 32 + 8 * i);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kidx = k0 + e;
-            bool ok = kidx < p.Skv;
-            ok &= !causal | (q_pos >= kidx) | (kidx < p.va.prefix);
-            ok &= !window | (q_pos - kidx < p.va.window);
-            if constexpr (DOCS) ok &= static_cast<int>(lab[e]) == doc_q;
+            const int c = kb * 32 + 8 * i + e;
+            bool ok = (c >= lo_c) & (c <= hi_c);
+            if constexpr (DOCS) ok &= static_cast<int>(l4[e]) == doc_q;
             mask_in_place(t[kb * 16 + 4 * i + e], ok, ninf);
           }
         }
@@ -375,10 +403,10 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
     // vector slot
     const int e_n2 = ent(u + 2);
-    if (do_s) softmax(s, stage_kv0(u, __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0);
+    if (do_s) softmax(s, stage_kv0(u, __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0, ring);
     if (u + 2 < T) {
       issue_copy(u + 2, __builtin_amdgcn_readfirstlane(e_n2), ring_old);
-      wait_vm<G::kDma>();   // this group's copies of stage u + 1 are complete
+      wait_prev_stage();   // this group's copies of stage u + 1 are complete
     } else {
       wait_vm<0>();
     }

@@ -29,45 +29,42 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (the published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["attention_tiled_attn_amd/csrc/attn_fwd.hip",
+KERNEL_SOURCES = ["attention_tiled_attn_amd/csrc/attn_fwd_pp.hip",
+                  "attention_tiled_attn_amd/csrc/attn_fwd.hip",
+                  "attention_tiled_attn_amd/csrc/device_util.h",
                   "attention_tiled_attn_amd/csrc/variants.h",
                   "attention_tiled_attn_amd/csrc/launch.h"]
 
 
 def admitted_pairs(wl, doc_ids) -> int:
-    """Admitted (query, key) pairs per (batch, head), from closed forms: dense
-    S^2, causal S(S+1)/2, documents under causal and window W: per document of
-    length L, L(L+1)/2 if L <= W else W(W+1)/2 + (L - W) W. Returns the total
-    over batch rows (divide by B for one row)."""
-    S = wl.S
-    if wl.documents:
-        import numpy as np
-        tot = 0
-        for b in range(wl.B):
-            lens = np.diff(np.flatnonzero(np.diff(np.r_[-1, doc_ids[b], -2]) != 0))
-            for L in lens.tolist():
-                if not wl.causal:
-                    tot += L * L if not wl.window else _window_noncausal(L, wl.window)
-                elif wl.window and L > wl.window:
-                    W = wl.window
-                    tot += W * (W + 1) // 2 + (L - W) * W
-                else:
-                    tot += L * (L + 1) // 2
-        return tot
-    if wl.causal and wl.window and wl.window < S:
-        W = wl.window
-        return wl.B * (W * (W + 1) // 2 + (S - W) * W)
-    if wl.causal:
-        return wl.B * S * (S + 1) // 2
-    if wl.window:
-        return wl.B * _window_noncausal(S, wl.window)
-    return wl.B * S * S
+    """Admitted (query, key) pairs per head, summed over batch rows.
 
-
-def _window_noncausal(L: int, W: int) -> int:
-    # pairs with q - k < W over an L x L square: all pairs minus those with q - k >= W
-    n = max(L - W, 0)
-    return L * L - n * (n + 1) // 2
+    For the query at position p every mask admits an interval of keys: the
+    causal part [0, p] (with a prefix P: [0, max(p, P - 1)]), the window part
+    [p - W + 1, inf), the document part the run of positions that carry p's
+    label, and the key range [0, Skv - 1]. Their intersection is an interval,
+    so each row's count is hi - lo + 1 (or 0)."""
+    import numpy as np
+    pos = np.arange(wl.Sq, dtype=np.int64) + wl.q_offset
+    tot = 0
+    for b in range(wl.B):
+        lo = np.zeros_like(pos)
+        hi = np.full_like(pos, wl.Skv - 1)
+        if wl.causal:
+            reach = pos if wl.prefix is None else np.maximum(pos, wl.prefix - 1)
+            hi = np.minimum(hi, reach)
+        if wl.window:
+            lo = np.maximum(lo, pos - wl.window + 1)
+        if wl.documents:
+            lab = np.asarray(doc_ids[b], dtype=np.int64)
+            n = lab.size
+            starts = np.r_[0, np.flatnonzero(np.diff(lab) != 0) + 1]
+            ends = np.r_[starts[1:], n] - 1
+            run = np.repeat(np.arange(starts.size), np.diff(np.r_[starts, n]))
+            lo = np.maximum(lo, starts[run[pos]])
+            hi = np.minimum(hi, ends[run[pos]])
+        tot += int(np.maximum(hi - lo + 1, 0).sum())
+    return tot
 
 
 def kernel_sha() -> str:
@@ -226,7 +223,8 @@ def main(argv=None):
     var = fa.Variant(causal=wl.causal, window=wl.window,
                      doc_ids=torch.from_numpy(inp.doc_ids).to(dev) if inp.doc_ids is not None else None,
                      alibi_slopes=torch.from_numpy(inp.slopes).to(dev) if inp.slopes is not None else None,
-                     softcap=wl.softcap if wl.mod == "softcap" else None)
+                     softcap=wl.softcap if wl.mod == "softcap" else None,
+                     q_offset=wl.q_offset, prefix=wl.prefix)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -322,7 +320,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Hkv": wl.Hkv, "Sq": wl.Sq,
                    "Skv": wl.Skv, "D": wl.D, "causal": wl.causal, "window": wl.window,
-                   "documents": wl.documents, "mod": wl.mod, "seed": wl.seed},
+                   "documents": wl.documents, "mod": wl.mod, "q_offset": wl.q_offset,
+                   "prefix": wl.prefix, "seed": wl.seed},
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attn_kernel_ms": round(kern_avg_ms, 4),
         "attn_kernel_ms_min": round(min(kern_ms), 4),

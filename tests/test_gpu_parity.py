@@ -214,7 +214,8 @@ def test_block_mask_document_workload_full_size():
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 @pytest.mark.parametrize("name", ["dense", "causal_gqa", "causal_gqa_shard8", "doc_swa", "alibi_d64",
-                                  "alibi_d128", "softcap_d64", "softcap_d128"])
+                                  "alibi_d128", "softcap_d64", "softcap_d128", "prefix_lm",
+                                  "chunked_prefill"])
 def test_full_size_sampled(name):
     wl = WORKLOADS[name]
     inp = make_inputs(wl)

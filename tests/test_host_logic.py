@@ -12,13 +12,18 @@ from workload import (WORKLOADS, alibi_slopes, document_ids, document_lengths, d
 
 @pytest.mark.parametrize("kw", [dict(), dict(causal=True), dict(causal=True, window=100),
                                 dict(window=90), dict(documents=True, causal=True, window=64),
-                                dict(documents=True), dict(documents=True, window=40)])
-def test_admitted_pairs_closed_forms_match_counting(kw):
+                                dict(documents=True), dict(documents=True, window=40),
+                                dict(causal=True, prefix=250), dict(causal=True, prefix=90, window=60),
+                                dict(sq=200, q_offset=500, causal=True),
+                                dict(sq=300, q_offset=123, causal=True, window=77, documents=True),
+                                dict(sq=100, q_offset=600, causal=True, prefix=256)])
+def test_admitted_pairs_match_counting(kw):
     wl = WORKLOADS["dense"].with_(B=2, H=1, Hkv=1, S=700, D=64, doc_len_range=(30, 250), **kw)
     inp = make_inputs(wl) if wl.documents else None
     doc = inp.doc_ids if inp is not None else None
-    want = sum(oracle.pair_count(700, 700, causal=wl.causal, window=wl.window or None,
-                                 doc_row=None if doc is None else doc[b]) for b in range(2))
+    want = sum(oracle.pair_count(wl.Sq, wl.Skv, causal=wl.causal, window=wl.window or None,
+                                 doc_row=None if doc is None else doc[b], q_offset=wl.q_offset,
+                                 prefix=wl.prefix) for b in range(2))
     assert bench.admitted_pairs(wl, doc) == want
 
 
@@ -27,6 +32,11 @@ def test_config_pair_counts():
     assert bench.admitted_pairs(c, None) // c.B == 33_558_528
     assert bench.admitted_pairs(WORKLOADS["dense"], None) // 4 == 4096 * 4096
     assert bench.admitted_pairs(WORKLOADS["alibi_d64"], None) == 536_887_296
+    # prefix-LM: S(S+1)/2 + P(P-1)/2 per row; prefill chunk: Sq * off + Sq(Sq+1)/2
+    p = WORKLOADS["prefix_lm"]
+    assert bench.admitted_pairs(p, None) // p.B == 8192 * 8193 // 2 + 2048 * 2047 // 2
+    c = WORKLOADS["chunked_prefill"]
+    assert bench.admitted_pairs(c, None) == 4096 * 28672 + 4096 * 4097 // 2
 
 
 def test_document_lengths_cover_and_range():

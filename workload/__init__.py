@@ -29,7 +29,7 @@ class Workload:
     B: int
     H: int          # query heads
     Hkv: int        # key/value heads (GQA when Hkv < H)
-    S: int          # Sq = Skv
+    S: int          # Skv, and Sq unless `sq` is set
     D: int          # head dimension
     dtype: str      # "bf16" or "fp32" element type of Q/K/V/O
     causal: bool = False
@@ -42,10 +42,11 @@ class Workload:
     doc_seed: int = 0
     q_offset: int = 0           # query row i sits at key position i + q_offset
     prefix: int | None = None   # prefix-LM boundary (with causal), or None
+    sq: int = 0                 # > 0: query rows, when fewer than the keys
 
     @property
     def Sq(self) -> int:
-        return self.S
+        return self.sq or self.S
 
     @property
     def Skv(self) -> int:
@@ -81,6 +82,13 @@ WORKLOADS = {
                             causal=True, mod="softcap", seed=4),
     "softcap_d128": Workload("softcap_d128", B=1, H=32, Hkv=32, S=32768, D=128, dtype="bf16",
                              causal=True, mod="softcap", seed=5),
+    # further variants: prefix-LM (a bidirectional 2048-token prompt, then
+    # causal) on the causal GQA shape, and a 4096-token prefill chunk after
+    # 28672 cached keys (query row i at key position 28672 + i)
+    "prefix_lm": Workload("prefix_lm", B=2, H=32, Hkv=8, S=8192, D=128, dtype="bf16",
+                          causal=True, prefix=2048, seed=6),
+    "chunked_prefill": Workload("chunked_prefill", B=1, H=32, Hkv=8, S=32768, sq=4096,
+                                q_offset=28672, D=128, dtype="bf16", causal=True, seed=7),
 }
 
 
