@@ -36,6 +36,11 @@ Readings where the pages are silent (each also listed in the design notes):
     several masks compose by AND;
   * ALiBi adds slope[h] * (k_idx - q_idx) to the scaled score; soft-capping
     replaces it by c * tanh(s / c);
+  * relative position bias (the PyTorch 2.5 / FlexAttention article names
+    relative position encodings among its variants without a form): a
+    per-head table of 2R + 1 values added to the scaled score, indexed by
+    k_idx - q_idx clipped to [-R, R]; ALiBi is the linear table with R at
+    least the sequence length;
   * grouped heads: query head h reads key/value head h // (H // Hkv).
   * query row i stands at key position i + q_offset (0 by default, so rows and
     keys start together); masks, ALiBi distances and document labels see that
@@ -91,10 +96,19 @@ def admitted(q_idx, k_idx, *, causal: bool = False, window: int | None = None,
 
 
 def modified_scores(s: np.ndarray, h: int, q_idx, k_idx, *, alibi_slopes=None,
-                    softcap: float | None = None) -> np.ndarray:
-    """The score modification applied to already-scaled scores `s`."""
-    if alibi_slopes is not None and softcap is not None:
+                    softcap: float | None = None, rel_bias=None) -> np.ndarray:
+    """The score modification applied to already-scaled scores `s`.
+
+    rel_bias: [H, 2R + 1] table; the bias of a pair is the entry of its
+    relative position k_idx - q_idx clipped to [-R, R] (entry index
+    clip + R)."""
+    if sum(x is not None for x in (alibi_slopes, softcap, rel_bias)) > 1:
         raise ValueError("one score modification at a time")
+    if rel_bias is not None:
+        tab = np.asarray(rel_bias, dtype=np.float64)[h]
+        R = (tab.shape[0] - 1) // 2
+        dist = np.asarray(k_idx, dtype=np.int64) - np.asarray(q_idx, dtype=np.int64)
+        return s + tab[np.clip(dist, -R, R) + R]
     if alibi_slopes is not None:
         slope = float(np.asarray(alibi_slopes, dtype=np.float64)[h])
         dist = np.asarray(k_idx, dtype=np.float64) - np.asarray(q_idx, dtype=np.float64)
@@ -107,7 +121,7 @@ def modified_scores(s: np.ndarray, h: int, q_idx, k_idx, *, alibi_slopes=None,
 
 def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None = None,
               doc_ids=None, alibi_slopes=None, softcap: float | None = None, rows=None,
-              heads=None, q_offset: int = 0, prefix: int | None = None):
+              heads=None, q_offset: int = 0, prefix: int | None = None, rel_bias=None):
     """fp64 attention forward, the definition written out.
 
     q: [B, H, Sq, D], k and v: [B, Hkv, Skv, D] (any real dtype; computed in
@@ -144,7 +158,7 @@ def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None
             kh = kv_head_of(h, H, Hkv)
             s = (q[b, h, rows, :] @ k[b, kh].T) * scale
             s = modified_scores(s, h, pos[:, None], keys[None, :],
-                                alibi_slopes=alibi_slopes, softcap=softcap)
+                                alibi_slopes=alibi_slopes, softcap=softcap, rel_bias=rel_bias)
             s = np.where(keep, s, -np.inf)
             m = np.where(any_kept, s.max(axis=1, initial=-np.inf), 0.0)
             w = np.exp(s - m[:, None])          # exp(-inf) = 0 for masked keys
@@ -160,7 +174,7 @@ def attention(q, k, v, scale: float, *, causal: bool = False, window: int | None
 def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
                        window: int | None = None, doc_ids=None, alibi_slopes=None,
                        softcap: float | None = None, q_offset: int = 0,
-                       prefix: int | None = None):
+                       prefix: int | None = None, rel_bias=None):
     """fp64 gradients of the attention forward: for the loss L = sum(O * dout),
     returns (dQ, dK, dV) with the shapes of q, k and v.
 
@@ -174,7 +188,7 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
         dV    += P^T dout                      (summed over the query heads of a group)
         dP     = dout V^T
         dS'    = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied to dP)
-        dS     = dS' * d s' / d s              (1 for no mod and ALiBi; 1 - tanh^2(s / c) for soft-capping)
+        dS     = dS' * d s' / d s              (1 for no mod, ALiBi and relative bias; 1 - tanh^2(s / c) for soft-capping)
         dQ     = scale * dS K,   dK += scale * dS^T Q
     """
     q = np.asarray(q, dtype=np.float64)
@@ -199,7 +213,7 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False,
             kh = kv_head_of(h, H, Hkv)
             s = (q[b, h] @ k[b, kh].T) * scale
             sm = modified_scores(s, h, pos[:, None], keys[None, :], alibi_slopes=alibi_slopes,
-                                 softcap=softcap)
+                                 softcap=softcap, rel_bias=rel_bias)
             sm = np.where(keep, sm, -np.inf)
             m = np.where(any_kept, sm.max(axis=1, initial=-np.inf), 0.0)
             w = np.exp(sm - m[:, None])

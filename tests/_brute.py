@@ -8,7 +8,7 @@ import math
 
 
 def brute_attention(q, k, v, scale, *, causal=False, window=None, doc_ids=None,
-                    alibi_slopes=None, softcap=None, q_offset=0, prefix=None):
+                    alibi_slopes=None, softcap=None, q_offset=0, prefix=None, rel_bias=None):
     """q: nested lists [B][H][Sq][D]; k, v: [B][Hkv][Skv][D]. Returns nested
     lists O [B][H][Sq][D] and LSE [B][H][Sq]. Query i stands at key position
     i + q_offset; with `prefix` the keys before it are exempt from causality."""
@@ -36,6 +36,11 @@ def brute_attention(q, k, v, scale, *, causal=False, window=None, doc_ids=None,
                     s = dot * scale
                     if alibi_slopes is not None:
                         s = s + alibi_slopes[h] * (j - p)
+                    if rel_bias is not None:
+                        R = (len(rel_bias[h]) - 1) // 2
+                        d = j - p
+                        d = -R if d < -R else (R if d > R else d)
+                        s = s + rel_bias[h][d + R]
                     if softcap is not None:
                         s = softcap * math.tanh(s / softcap)
                     kept.append((j, s))

@@ -22,6 +22,8 @@ VARIANTS = [
     dict(causal=True, prefix=3),
     dict(causal=True, q_offset=-2, alibi=True),
     dict(causal=True, doc=True, q_offset=2, window=5),
+    dict(relbias=2),
+    dict(relbias=1, causal=True, q_offset=1),
 ]
 
 
@@ -43,6 +45,8 @@ def _kw(var, S, H):
         kw["alibi_slopes"] = np.array([0.5, 0.25][:H])
     if "softcap" in var:
         kw["softcap"] = var["softcap"]
+    if "relbias" in var:
+        kw["rel_bias"] = np.random.default_rng(9).standard_normal((H, 2 * var["relbias"] + 1))
     return kw
 
 

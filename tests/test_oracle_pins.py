@@ -244,6 +244,9 @@ BRUTE = [
     dict(docs=True, causal=True, q_offset=1, softcap=2.0),
     dict(causal=True, prefix=4),
     dict(causal=True, prefix=3, window=5, q_offset=2),
+    dict(relbias=3),
+    dict(causal=True, relbias=1, q_offset=2),
+    dict(docs=True, window=4, relbias=6),
 ]
 
 
@@ -261,7 +264,8 @@ def test_matches_scalar_brute_force(kw, shape):
     slopes = alibi_slopes(H).astype(np.float64) if kw.get("alibi") else None
     args = dict(causal=kw.get("causal", False), window=kw.get("window"), doc_ids=doc,
                 alibi_slopes=slopes, softcap=kw.get("softcap"), q_offset=off,
-                prefix=kw.get("prefix"))
+                prefix=kw.get("prefix"),
+                rel_bias=rnd((H, 2 * kw["relbias"] + 1), 41) if "relbias" in kw else None)
     O, L = attention(q, k, v, 0.6, **args)
     Ob, Lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), 0.6,
                              **{a: (b.tolist() if isinstance(b, np.ndarray) else b)
@@ -342,6 +346,39 @@ def test_prefix_lm_closed_forms():
     mask[:, :P] = True
     assert np.abs(attention(q, k, v, 0.7, causal=True, prefix=P)[0]
                   - sdpa_masked(q, k, v, 0.7, mask)).max() < 1e-12
+
+
+def test_relative_bias_linear_table_is_alibi():
+    """A table linear in the clipped distance, with R covering every distance,
+    is ALiBi with that slope (exact)."""
+    B, H, Sq, Skv, D, off = 1, 4, 11, 19, 5, 8
+    q, k, v = rnd((B, H, Sq, D), 72), rnd((B, 2, Skv, D), 73), rnd((B, 2, Skv, D), 74)
+    slopes = alibi_slopes(H).astype(np.float64)
+    R = Sq + Skv + off
+    table = slopes[:, None] * np.arange(-R, R + 1)[None, :]
+    for causal in (False, True):
+        Oa, La = attention(q, k, v, 0.4, causal=causal, q_offset=off, alibi_slopes=slopes)
+        Or, Lr = attention(q, k, v, 0.4, causal=causal, q_offset=off, rel_bias=table)
+        assert np.abs(Oa - Or).max() < 1e-12 and np.abs(La - Lr).max() < 1e-12
+
+
+def test_relative_bias_clipping_and_constant_table():
+    """A constant table moves LSE by the constant only; with R = 0 every pair
+    takes the single entry; beyond R the end entries apply."""
+    S, D = 9, 4
+    q, k, v = rnd((1, 2, S, D), 75), rnd((1, 2, S, D), 76), rnd((1, 2, S, D), 77)
+    O0, L0 = attention(q, k, v, 0.5, causal=True)
+    Oc, Lc = attention(q, k, v, 0.5, causal=True, rel_bias=np.full((2, 7), 1.25))
+    assert np.abs(O0 - Oc).max() < 1e-12 and np.abs(Lc - L0 - 1.25).max() < 1e-12
+    O1, L1 = attention(q, k, v, 0.5, causal=True, rel_bias=np.array([[0.5], [-2.0]]))
+    assert np.abs(O1 - O0).max() < 1e-12
+    assert np.abs(L1[0, 0] - L0[0, 0] - 0.5).max() < 1e-12 and np.abs(L1[0, 1] - L0[0, 1] + 2.0).max() < 1e-12
+    # R = 1 under causal: key == query gets entry 1, every earlier key entry 0
+    tab = np.array([[0.0, 3.0, 7.0], [0.0, 3.0, 7.0]])
+    _, Lr = attention(q, k, v, 0.5, causal=True, rel_bias=tab)
+    s = np.einsum("hd,hjd->hj", q[0, :, 4], k[0]) * 0.5
+    manual = np.log(np.exp(s[:, :4]).sum(-1) + np.exp(s[:, 4] + 3.0))
+    assert np.abs(Lr[0, :, 4] - manual).max() < 1e-12
 
 
 def test_offset_and_prefix_pair_counts():
