@@ -15,7 +15,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_PREFIX, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
-    MOD_SOFTCAP, QTILE, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
+    MOD_RELBIAS, MOD_SOFTCAP, QTILE, REL_MAX, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
     flexattn_build_block_mask, flexattn_bwd, flexattn_fwd, flexattn_last_error, flexattn_strerror,
     flexattn_version, lib,
 )
@@ -40,6 +40,7 @@ class Variant:
     softcap: float | None = None
     q_offset: int = 0                     # query row i sits at key position i + q_offset
     prefix: int | None = None             # with causal: keys below it are seen by every query
+    rel_bias: torch.Tensor | None = None  # float32 [H, 2R + 1] on the device: relative-position bias
 
     @property
     def mask_kind(self) -> int:
@@ -48,8 +49,10 @@ class Variant:
 
     @property
     def mod_kind(self) -> int:
-        if self.alibi_slopes is not None and self.softcap is not None:
+        if sum(x is not None for x in (self.alibi_slopes, self.softcap, self.rel_bias)) > 1:
             raise ValueError("one score modification at a time")
+        if self.rel_bias is not None:
+            return MOD_RELBIAS
         if self.alibi_slopes is not None:
             return MOD_ALIBI
         if self.softcap is not None:
@@ -71,6 +74,11 @@ def make_params(var: Variant, dtype: torch.dtype) -> Params:
     p.softcap = float(var.softcap) if var.softcap is not None else 0.0
     p.alibi_slopes = var.alibi_slopes.data_ptr() if var.alibi_slopes is not None else None
     p.q_offset = int(var.q_offset)
+    if var.rel_bias is not None:
+        if var.rel_bias.dtype != torch.float32 or not var.rel_bias.is_contiguous() or var.rel_bias.dim() != 2:
+            raise TypeError("rel_bias must be a contiguous float32 [H, 2R + 1] tensor")
+        p.rel_bias = var.rel_bias.data_ptr()
+        p.rel_max = (int(var.rel_bias.shape[1]) - 1) // 2
     p.prefix = int(var.prefix) if var.prefix is not None else 0
     if var.doc_ids is not None:
         if var.doc_ids.dtype != torch.int32 or not var.doc_ids.is_contiguous():

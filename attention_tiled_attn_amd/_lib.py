@@ -21,7 +21,8 @@ ERR_NULLPTR, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN = -1, -2, -3, -4
 ERR_BLOCKMASK, ERR_OVERFLOW, ERR_HIP, ERR_ARG = -5, -6, -7, -8
 BF16, FP32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOCUMENT, MASK_PREFIX = 0, 1, 2, 4, 8
-MOD_NONE, MOD_ALIBI, MOD_SOFTCAP = 0, 1, 2
+MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_RELBIAS = 0, 1, 2, 3
+REL_MAX = 1023
 TILE = 128
 QTILE = 256
 
@@ -41,7 +42,8 @@ class FlexAttnError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("window", ctypes.c_int), ("softcap", ctypes.c_float),
                 ("alibi_slopes", ctypes.c_void_p), ("doc_ids", ctypes.c_void_p),
-                ("doc_stride", ctypes.c_int), ("q_offset", ctypes.c_int), ("prefix", ctypes.c_int)]
+                ("doc_stride", ctypes.c_int), ("q_offset", ctypes.c_int), ("prefix", ctypes.c_int),
+                ("rel_bias", ctypes.c_void_p), ("rel_max", ctypes.c_int)]
 
 
 class BlockMask(ctypes.Structure):

@@ -26,7 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0, 0, 0};
+const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0, 0, 0, nullptr, 0};
 
 constexpr int kMaskBits = FLEXATTN_MASK_CAUSAL | FLEXATTN_MASK_WINDOW | FLEXATTN_MASK_DOCUMENT |
                           FLEXATTN_MASK_PREFIX;
@@ -162,7 +162,7 @@ int check_attn_args(const flexattn_params* prm, int B, int H, int Hkv, int Sq, i
   if (st) return st;
   if (D != 64 && D != 128) return FLEXATTN_ERR_UNSUPPORTED;
   if (prm->dtype != FLEXATTN_BF16 && prm->dtype != FLEXATTN_FP32) return FLEXATTN_ERR_UNSUPPORTED;
-  if (mod_kind < FLEXATTN_MOD_NONE || mod_kind > FLEXATTN_MOD_SOFTCAP) return FLEXATTN_ERR_UNSUPPORTED;
+  if (mod_kind < FLEXATTN_MOD_NONE || mod_kind > FLEXATTN_MOD_RELBIAS) return FLEXATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FLEXATTN_ERR_ARG;
   if (mod_kind == FLEXATTN_MOD_ALIBI) {
     if (!prm->alibi_slopes) return FLEXATTN_ERR_NULLPTR;
@@ -170,6 +170,11 @@ int check_attn_args(const flexattn_params* prm, int B, int H, int Hkv, int Sq, i
   }
   if (mod_kind == FLEXATTN_MOD_SOFTCAP && !(prm->softcap > 0.f && std::isfinite(prm->softcap)))
     return FLEXATTN_ERR_ARG;
+  if (mod_kind == FLEXATTN_MOD_RELBIAS) {
+    if (!prm->rel_bias) return FLEXATTN_ERR_NULLPTR;
+    if (!aligned(prm->rel_bias, 16)) return FLEXATTN_ERR_ALIGN;
+    if (prm->rel_max < 0 || prm->rel_max > FLEXATTN_REL_MAX) return FLEXATTN_ERR_ARG;
+  }
   // 32-bit limits: in-kernel position arithmetic is int; tensor offsets are size_t.
   const long long nq = ceil_div(Sq, FLEXATTN_QTILE);
   const long long nk = ceil_div(Skv, FLEXATTN_TILE);
@@ -208,6 +213,8 @@ void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, 
   va.doc = prm->doc_ids;
   va.doc_stride = prm->doc_stride;
   va.q_offset = prm->q_offset;
+  va.rel_bias = mod_kind == FLEXATTN_MOD_RELBIAS ? prm->rel_bias : nullptr;
+  va.rel_max = mod_kind == FLEXATTN_MOD_RELBIAS ? prm->rel_max : 0;
   va.prefix = (mask_kind & FLEXATTN_MASK_PREFIX) ? prm->prefix : 0;
 }
 

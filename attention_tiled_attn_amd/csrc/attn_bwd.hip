@@ -113,8 +113,13 @@ __device__ inline unsigned trans_off(int lane, int db, int j) {
 
 // Modified score in log2 units, and d s'/d s for the chain rule.
 template <int MOD>
-__device__ inline float mod_score(float s, const VariantArgs& va, float slope2, int dk, float& dmod) {
-  if constexpr (MOD == kModAlibi) {
+__device__ inline float mod_score(float s, const VariantArgs& va, float slope2, lds_cf32* tab, int dk,
+                                 float& dmod) {
+  if constexpr (MOD == kModRelBias) {
+    dmod = 1.f;
+    const int d = min(max(dk, -va.rel_max), va.rel_max);
+    return __builtin_fmaf(tab[d], kLog2e, s * va.c1);
+  } else if constexpr (MOD == kModAlibi) {
     dmod = 1.f;
     return __builtin_fmaf(s, va.c1, slope2 * static_cast<float>(dk));
   } else if constexpr (MOD == kModSoftcap) {
@@ -138,6 +143,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
+  __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -196,6 +202,8 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
   const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
   for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : (i << 4);
+  if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
+  lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
   int T = 2 * n_entries;
   if (n_entries > 0) {
     const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
@@ -266,7 +274,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
           const int r = r0 + 2 * jj + x;
           const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           float dmod;
-          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, kidx - q_pos, dmod);
+          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, tab, kidx - q_pos, dmod);
           if (!full) {
             bool ok = kidx < p.Skv;
             ok &= !(p.mask_kind & kMaskCausal) | (q_pos >= kidx) | (kidx < p.va.prefix);
@@ -331,6 +339,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(16))) float lbuf[kRing * kStage];
   __shared__ __attribute__((aligned(16))) float dbuf[kRing * kStage];
+  __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
+  lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -446,6 +456,14 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
     if (window) full = full && (q_last + off - k_lo < p.va.window);
     float slope2 = 0.f;
     if constexpr (MOD == kModAlibi) slope2 = p.va.slopes[hh] * kLog2e;
+    if constexpr (MOD == kModRelBias) {
+      // a new query head: its table replaces the last head's, whose last
+      // reader finished before the previous stage's closing barrier
+      if (u % ns == 0) {
+        stage_rel_table(p.va, hh, (lds_f32*)(rtab), tid, kThreads);
+        __syncthreads();
+      }
+    }
 
     // S = Q K^T and dP = dO V^T: two 32-row query blocks
     f32x16 s[2], dp[2];
@@ -484,7 +502,7 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
           const int qrow = r0 + ql0 + x;
           float dmod;
           const int qpos = qrow + off;
-          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, k_row - qpos, dmod);
+          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, tab, k_row - qpos, dmod);
           if (!full) {
             bool ok = k_ok && qrow < p.Sq;
             ok &= !causal | (qpos >= k_row) | (k_row < p.va.prefix);
@@ -567,6 +585,7 @@ hipError_t launch_mod(const BwdLaunch& p, hipStream_t stream) {
     case kModNone: return launch_t<D, kModNone, DOCS>(p, stream);
     case kModAlibi: return launch_t<D, kModAlibi, DOCS>(p, stream);
     case kModSoftcap: return launch_t<D, kModSoftcap, DOCS>(p, stream);
+    case kModRelBias: return launch_t<D, kModRelBias, DOCS>(p, stream);
   }
   return hipErrorInvalidValue;
 }

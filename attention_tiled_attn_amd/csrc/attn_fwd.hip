@@ -144,6 +144,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   constexpr int DC = D / 16;          // 16-wide d chunks (QK^T k-steps)
   constexpr int DB = D / 32;          // 32-wide d blocks of O^T
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * G::stage];
+  __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,7 +276,12 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
 
   using SM = ScoreMod<MOD>;
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
-  const typename SM::Lane sml = SM::lane(p.va, h, q_pos);
+  if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
+  const typename SM::Lane sml = [&] {
+    typename SM::Lane L = SM::lane(p.va, h, q_pos);
+    if constexpr (MOD == kModRelBias) L.tab = (lds_cf32*)(rtab) + p.va.rel_max;
+    return L;
+  }();
   // document labels of this batch row (document-mask kernels only)
   const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
@@ -470,6 +476,7 @@ hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
     case kModNone: return launch_t<D, kModNone, F32, DOCS>(p, stream);
     case kModAlibi: return launch_t<D, kModAlibi, F32, DOCS>(p, stream);
     case kModSoftcap: return launch_t<D, kModSoftcap, F32, DOCS>(p, stream);
+    case kModRelBias: return launch_t<D, kModRelBias, F32, DOCS>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -86,6 +86,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   __shared__ int ents[kPairMaxKeyTiles];
   // document labels of each ring slot's 64 keys (copied with K by wave 0)
   __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kRing * kBN : 4];
+  __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,6 +135,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
   const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
   for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : ((i << 4) | 0x5);
+  if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   int n_stages = 2 * n_entries;
   if (n_entries > 0) {
     const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
@@ -207,7 +209,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   float l_run = 0.f;
   using SM = ScoreMod<MOD>;
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
-  const typename SM::Lane sml = SM::lane(p.va, h, q_pos);
+  const typename SM::Lane sml = [&] {
+    typename SM::Lane L = SM::lane(p.va, h, q_pos);
+    if constexpr (MOD == kModRelBias) L.tab = (lds_cf32*)(rtab) + p.va.rel_max;
+    return L;
+  }();
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
   bf16x8 pf[4];
@@ -261,13 +267,31 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // online softmax of one stage: scores -> P^T (bf16) in pf, running max/sum
   auto softmax = [&](const f32x16 (&s)[2], int kv0, bool full, int ring) {
     float t[32];
+    // Relative bias: when every distance of the stage, over the wave's 32
+    // rows, lies beyond the clip distance, all scores take the same end entry
+    // of the table (one wave-uniform LDS read instead of one per score).
+    bool clipped = false;
+    float clip_add = 0.f;
+    if constexpr (MOD == kModRelBias) {
+      const int qw = __builtin_amdgcn_readfirstlane(q_pos);   // lane 0 holds the wave's first row
+      const int R = p.va.rel_max;
+      const bool below = kv0 + kBN - 1 - qw < -R;   // largest distance below -R
+      const bool above = kv0 - (qw + 31) > R;       // smallest distance above R
+      clipped = below || above;
+      if (clipped) clip_add = sml.tab[below ? -R : R] * kLog2e;
+    }
+    if (clipped) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 32; ++i) t[i] = __builtin_fmaf(s[i >> 4][i & 15], p.va.c1, clip_add);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_pos);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_pos);
+        }
+    }
     const float ninf = -INFINITY;
     if (!full) {
       // The causal part (with its prefix), the window and the key range each
@@ -466,6 +490,7 @@ hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
     case kModNone: return launch_t<D, kModNone, DOCS>(p, stream);
     case kModAlibi: return launch_t<D, kModAlibi, DOCS>(p, stream);
     case kModSoftcap: return launch_t<D, kModSoftcap, DOCS>(p, stream);
+    case kModRelBias: return launch_t<D, kModRelBias, DOCS>(p, stream);
   }
   return hipErrorInvalidValue;
 }

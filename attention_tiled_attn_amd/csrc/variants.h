@@ -23,7 +23,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum : int { kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 4, kMaskPrefix = 8 };
-enum : int { kModNone = 0, kModAlibi = 1, kModSoftcap = 2 };
+enum : int { kModNone = 0, kModAlibi = 1, kModSoftcap = 2, kModRelBias = 3 };
+constexpr int kRelMax = 1023;                 // largest clip distance of a bias table
+constexpr int kRelCap = 2 * kRelMax + 2;      // table entries kept in LDS
+
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef const __attribute__((address_space(3))) float lds_cf32;
 
 // Per-call constants the functors read. Filled on the host.
 struct VariantArgs {
@@ -36,6 +41,8 @@ struct VariantArgs {
   int doc_stride;
   int q_offset;      // position of query row 0 in the key sequence
   int prefix;        // causal part admits keys below it too (0 = plain causal)
+  const float* rel_bias;   // relative-bias tables [H][2 rel_max + 1]
+  int rel_max;             // clip distance R
 };
 
 // ---------------------------------------------------------------- score_mod
@@ -82,6 +89,28 @@ struct ScoreMod<kModSoftcap> {
     return th * a.sc_out;
   }
 };
+
+// Relative position bias: s' = scale*q.k + table_h[clip(k_idx - q_idx, -R, R)].
+// The kernels stage head h's table in LDS (stage_rel_table) and point `tab`
+// at its distance-0 entry.
+template <>
+struct ScoreMod<kModRelBias> {
+  static constexpr bool kFoldScale = false;
+  struct Lane { lds_cf32* tab; };
+  __device__ static Lane lane(const VariantArgs&, int, int) { return {nullptr}; }
+  __device__ static float apply(float s, const VariantArgs& a, const Lane& L, int dk) {
+    const int d = min(max(dk, -a.rel_max), a.rel_max);
+    return __builtin_fmaf(L.tab[d], kLog2e, s * a.c1);
+  }
+};
+
+// Copy head h's relative-bias table (2R + 1 floats) to `dst` in LDS; every
+// thread of the workgroup takes part; the caller synchronises before use.
+__device__ inline void stage_rel_table(const VariantArgs& a, int h, lds_f32* dst, int tid, int nthreads) {
+  const int n = 2 * a.rel_max + 1;
+  const float* src = a.rel_bias + static_cast<size_t>(h) * n;
+  for (int i = tid; i < n; i += nthreads) dst[i] = src[i];
+}
 
 // ---------------------------------------------------------------- mask_mod
 // The kernels evaluate the per-element predicate inline on partial tiles, on

@@ -111,7 +111,9 @@ def cpu_baseline(inp, budget_s: float = 15.0):
     wl = inp.wl
     kw = dict(causal=wl.causal, window=wl.window or None,
               alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
-              softcap=wl.softcap if wl.mod == "softcap" else None)
+              softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
+              prefix=wl.prefix,
+              rel_bias=None if inp.rel_bias is None else inp.rel_bias.astype(np.float64))
     t0 = time.perf_counter()
     done_pairs = rows_done = heads_done = 0
     chunk = 512
@@ -167,7 +169,9 @@ def cpu_baseline_bwd(inp, dout, budget_s: float = 15.0):
             doc = None if inp.doc_ids is None else inp.doc_ids[b:b + 1]
             kw = dict(causal=wl.causal, window=wl.window or None, doc_ids=doc,
                       alibi_slopes=None if inp.slopes is None else inp.slopes[h:h + 1].astype(np.float64),
-                      softcap=wl.softcap if wl.mod == "softcap" else None)
+                      softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
+                      prefix=wl.prefix,
+                      rel_bias=None if inp.rel_bias is None else inp.rel_bias[h:h + 1].astype(np.float64))
             oracle.attention_backward(q, k, v, g, wl.scale, **kw)
             slices += 1
             done_pairs += _pairs_in_rows(wl, np.arange(wl.Sq), None if doc is None else doc[0])
@@ -189,8 +193,9 @@ def _pairs_in_rows(wl, rows, doc_row) -> int:
     keys = np.arange(wl.Skv)
     for r0 in range(0, rows.size, 256):
         r = rows[r0:r0 + 256]
-        tot += int(oracle.admitted(r[:, None], keys[None, :], causal=wl.causal,
-                                   window=wl.window or None, doc_row=doc_row).sum())
+        tot += int(oracle.admitted(r[:, None] + wl.q_offset, keys[None, :], causal=wl.causal,
+                                   window=wl.window or None, doc_row=doc_row,
+                                   prefix=wl.prefix).sum())
     return tot
 
 
@@ -224,7 +229,8 @@ def main(argv=None):
                      doc_ids=torch.from_numpy(inp.doc_ids).to(dev) if inp.doc_ids is not None else None,
                      alibi_slopes=torch.from_numpy(inp.slopes).to(dev) if inp.slopes is not None else None,
                      softcap=wl.softcap if wl.mod == "softcap" else None,
-                     q_offset=wl.q_offset, prefix=wl.prefix)
+                     q_offset=wl.q_offset, prefix=wl.prefix,
+                     rel_bias=torch.from_numpy(inp.rel_bias).to(dev) if inp.rel_bias is not None else None)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -321,7 +327,7 @@ def main(argv=None):
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Hkv": wl.Hkv, "Sq": wl.Sq,
                    "Skv": wl.Skv, "D": wl.D, "causal": wl.causal, "window": wl.window,
                    "documents": wl.documents, "mod": wl.mod, "q_offset": wl.q_offset,
-                   "prefix": wl.prefix, "seed": wl.seed},
+                   "prefix": wl.prefix, "rel_max": wl.rel_max, "seed": wl.seed},
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attn_kernel_ms": round(kern_avg_ms, 4),
         "attn_kernel_ms_min": round(min(kern_ms), 4),

@@ -93,8 +93,21 @@ enum flexattn_mask_kind {
 
 /* score_mod kinds, applied to the scaled score s = scale * q.k:
  *   ALIBI   : s + alibi_slopes[h] * (k_idx - q_idx)      (positions, as above)
- *   SOFTCAP : softcap * tanh(s / softcap)                                       */
-enum flexattn_mod_kind { FLEXATTN_MOD_NONE = 0, FLEXATTN_MOD_ALIBI = 1, FLEXATTN_MOD_SOFTCAP = 2 };
+ *   SOFTCAP : softcap * tanh(s / softcap)
+ *   RELBIAS : s + rel_bias[h][clip(k_idx - q_idx, -R, R) + R], R = rel_max
+ *             (relative position bias: a per-head table over the clipped
+ *             relative position; the pages name relative position encodings
+ *             among FlexAttention's variants, PyTorch 2.5 / FlexAttention
+ *             article, overview)                                                */
+enum flexattn_mod_kind {
+  FLEXATTN_MOD_NONE = 0,
+  FLEXATTN_MOD_ALIBI = 1,
+  FLEXATTN_MOD_SOFTCAP = 2,
+  FLEXATTN_MOD_RELBIAS = 3
+};
+
+/* Largest clip distance R of a relative-bias table (tables are staged in LDS). */
+#define FLEXATTN_REL_MAX 1023
 
 /* Parameters of the variants. Host struct, read during the call only.
  * A NULL params pointer means: dtype BF16, no window, no documents, no mods,
@@ -110,6 +123,9 @@ typedef struct flexattn_params {
                                 >= max(Sq + q_offset, Skv)                            */
   int q_offset;              /* >= 0: position of query row 0 (see "Positions")       */
   int prefix;                /* >= 0 when the mask has FLEXATTN_MASK_PREFIX           */
+  const float* rel_bias;     /* device float32 [H][2 * rel_max + 1], 16-byte aligned,
+                                when mod_kind is FLEXATTN_MOD_RELBIAS                  */
+  int rel_max;               /* R in [0, FLEXATTN_REL_MAX] for FLEXATTN_MOD_RELBIAS   */
 } flexattn_params;
 
 /* Block mask: for every query tile of FLEXATTN_QTILE rows, the ascending list

@@ -89,6 +89,7 @@ def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
         softcap=wl.softcap if wl.mod == "softcap" else None,
         q_offset=wl.q_offset,
         prefix=wl.prefix,
+        rel_bias=torch.from_numpy(inp.rel_bias).to(device) if inp.rel_bias is not None else None,
     )
 
 
@@ -108,7 +109,8 @@ def oracle_kwargs(inp: Inputs) -> dict:
     return dict(causal=wl.causal, window=wl.window or None, doc_ids=inp.doc_ids,
                 alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
                 softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
-                prefix=wl.prefix)
+                prefix=wl.prefix,
+                rel_bias=None if inp.rel_bias is None else inp.rel_bias.astype(np.float64))
 
 
 def run_oracle(inp: Inputs, rows=None, heads=None):
@@ -155,16 +157,17 @@ def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0) ->
 
 def small(name="t", *, B=1, H=2, Hkv=None, S=200, Sq=None, Skv=None, D=64, dtype="bf16",
           causal=False, window=0, documents=False, mod="none", softcap=30.0, seed=7,
-          doc_range=(16, 96), q_offset=0, prefix=None) -> Inputs:
+          doc_range=(16, 96), q_offset=0, prefix=None, rel_max=0) -> Inputs:
     """Small seeded inputs (Sq and Skv may differ; query row i at key
     position i + q_offset)."""
-    from workload import alibi_slopes, as_element_type, document_ids, document_lengths, draw_qkv
+    from workload import (alibi_slopes, as_element_type, document_ids, document_lengths, draw_qkv,
+                          rel_bias_table)
     Hkv = Hkv or H
     Sq = Sq or S
     Skv = Skv or S
     wl = Workload(name, B=B, H=H, Hkv=Hkv, S=S, D=D, dtype=dtype, causal=causal, window=window,
                   documents=documents, mod=mod, softcap=softcap, seed=seed, doc_seed=seed,
-                  doc_len_range=doc_range, q_offset=q_offset, prefix=prefix)
+                  doc_len_range=doc_range, q_offset=q_offset, prefix=prefix, rel_max=rel_max)
     q, k, v = draw_qkv(B, H, Hkv, Sq, Skv, D, seed)
     q, k, v = (as_element_type(t, dtype) for t in (q, k, v))
     doc = None
@@ -172,7 +175,8 @@ def small(name="t", *, B=1, H=2, Hkv=None, S=200, Sq=None, Skv=None, D=64, dtype
         n = max(Sq + q_offset, Skv)
         doc = np.stack([document_ids(document_lengths(n, seed + b, *doc_range)) for b in range(B)])
     slopes = alibi_slopes(H) if mod == "alibi" else None
-    return Inputs(_SqSkv(wl, Sq, Skv), q, k, v, doc, slopes)
+    rel = rel_bias_table(H, rel_max, seed) if mod == "relbias" else None
+    return Inputs(_SqSkv(wl, Sq, Skv), q, k, v, doc, slopes, rel_bias=rel)
 
 
 class _SqSkv:

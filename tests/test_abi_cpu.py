@@ -85,6 +85,8 @@ def P(**kw):
     p.doc_stride = kw.get("doc_stride", 0)
     p.q_offset = kw.get("q_offset", 0)
     p.prefix = kw.get("prefix", 0)
+    p.rel_bias = kw.get("rel_bias")
+    p.rel_max = kw.get("rel_max", 0)
     return p
 
 
@@ -109,7 +111,11 @@ def P(**kw):
     (dict(mask_kind=1, params=P(q_offset=2**31 - 300)), _lib.ERR_OVERFLOW),
     (dict(mask_kind=4, params=P(doc_ids=A, doc_stride=128, q_offset=1)), _lib.ERR_ARG),  # stride < Sq + off
     (dict(mask_kind=-1), _lib.ERR_UNSUPPORTED),
-    (dict(mod_kind=3), _lib.ERR_UNSUPPORTED),
+    (dict(mod_kind=4), _lib.ERR_UNSUPPORTED),
+    (dict(mod_kind=3, params=P()), _lib.ERR_NULLPTR),                     # relative bias, no table
+    (dict(mod_kind=3, params=P(rel_bias=A + 4)), _lib.ERR_ALIGN),
+    (dict(mod_kind=3, params=P(rel_bias=A, rel_max=-1)), _lib.ERR_ARG),
+    (dict(mod_kind=3, params=P(rel_bias=A, rel_max=1024)), _lib.ERR_ARG),
     (dict(params=P(dtype=7)), _lib.ERR_UNSUPPORTED),
     (dict(scale=float("nan")), _lib.ERR_ARG),
     (dict(scale=float("inf")), _lib.ERR_ARG),

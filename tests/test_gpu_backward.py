@@ -66,6 +66,7 @@ VARIANTS = [
     dict(documents=True), dict(documents=True, causal=True, window=64),
     dict(mod="alibi", causal=True), dict(mod="softcap", softcap=5.0),
     dict(mod="softcap", softcap=5.0, causal=True),
+    dict(mod="relbias", rel_max=7), dict(mod="relbias", rel_max=1023, causal=True, window=90),
 ]
 
 
@@ -92,6 +93,7 @@ def test_backward_shapes(shape):
     dict(S=400, causal=True, prefix=150),
     dict(S=333, causal=True, prefix=129, window=90, documents=True),
     dict(Sq=100, Skv=600, q_offset=500, causal=True, prefix=256, mod="alibi"),
+    dict(Sq=200, Skv=450, q_offset=250, causal=True, mod="relbias", rel_max=64),
 ], ids=lambda c: ",".join(f"{a}={b}" for a, b in c.items()))
 @pytest.mark.parametrize("D", [64, 128])
 def test_backward_offset_and_prefix(case, D):

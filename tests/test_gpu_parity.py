@@ -49,6 +49,8 @@ VARIANTS = [
     dict(documents=True), dict(documents=True, causal=True, window=40),
     dict(causal=True, mod="alibi"), dict(mod="alibi"), dict(mod="softcap", softcap=5.0),
     dict(causal=True, mod="softcap", softcap=30.0), dict(documents=True, mod="alibi", causal=True),
+    dict(mod="relbias", rel_max=5), dict(causal=True, mod="relbias", rel_max=1023),
+    dict(documents=True, causal=True, window=40, mod="relbias", rel_max=17),
 ]
 
 
@@ -66,6 +68,14 @@ def test_dtypes_and_head_dims(dtype, D):
 
 
 # ------------------------------------------------------------------ GPU-side invariants
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("R", [0, 3, 1023])
+def test_relative_bias_fp32_path(D, R):
+    """fp32 inputs run the 128-row kernel; its bias table is staged the same way."""
+    inp = small(S=300, D=D, dtype="fp32", causal=True, mod="relbias", rel_max=R)
+    check_full(inp, what=f"fp32 relbias D={D} R={R}")
+
+
 def test_null_block_mask_is_bitwise_equal():
     for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict()):
         inp = small(S=520, D=128, **var)
@@ -149,6 +159,7 @@ OFFSET_CASES = [
     dict(S=500, causal=True, prefix=300, documents=True),
     dict(S=300, causal=True, prefix=1000, mod="alibi"),            # prefix past the end: dense
     dict(Sq=100, Skv=700, q_offset=600, causal=True, prefix=256, mod="softcap", softcap=5.0),
+    dict(Sq=64, Skv=500, q_offset=436, causal=True, mod="relbias", rel_max=100),
 ]
 
 
@@ -215,7 +226,7 @@ def test_block_mask_document_workload_full_size():
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 @pytest.mark.parametrize("name", ["dense", "causal_gqa", "causal_gqa_shard8", "doc_swa", "alibi_d64",
                                   "alibi_d128", "softcap_d64", "softcap_d128", "prefix_lm",
-                                  "chunked_prefill"])
+                                  "chunked_prefill", "relbias"])
 def test_full_size_sampled(name):
     wl = WORKLOADS[name]
     inp = make_inputs(wl)

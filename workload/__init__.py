@@ -36,13 +36,14 @@ class Workload:
     window: int = 0             # 0 = no sliding window; else q - k < window
     documents: bool = False     # document-packing mask
     doc_len_range: tuple = (512, 4096)
-    mod: str = "none"           # "none" | "alibi" | "softcap"
+    mod: str = "none"           # "none" | "alibi" | "softcap" | "relbias"
     softcap: float = 30.0
     seed: int = 0
     doc_seed: int = 0
     q_offset: int = 0           # query row i sits at key position i + q_offset
     prefix: int | None = None   # prefix-LM boundary (with causal), or None
     sq: int = 0                 # > 0: query rows, when fewer than the keys
+    rel_max: int = 0            # clip distance R of the relative-bias table (mod "relbias")
 
     @property
     def Sq(self) -> int:
@@ -89,6 +90,10 @@ WORKLOADS = {
                           causal=True, prefix=2048, seed=6),
     "chunked_prefill": Workload("chunked_prefill", B=1, H=32, Hkv=8, S=32768, sq=4096,
                                 q_offset=28672, D=128, dtype="bf16", causal=True, seed=7),
+    # relative-position bias (a per-head table over distances clipped to
+    # +-1023) on the causal GQA shape
+    "relbias": Workload("relbias", B=2, H=32, Hkv=8, S=8192, D=128, dtype="bf16", causal=True,
+                        mod="relbias", rel_max=1023, seed=8),
 }
 
 
@@ -109,6 +114,14 @@ def draw_dout(B: int, H: int, Sq: int, D: int, seed: int) -> torch.Tensor:
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed) + 1000)
     return torch.randn((B, H, Sq, D), generator=g, dtype=torch.float32)
+
+
+def rel_bias_table(H: int, R: int, seed: int) -> np.ndarray:
+    """Relative-bias table [H, 2R + 1] as float32: N(0, 1) from a torch CPU
+    generator seeded with `seed` + 2000."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 2000)
+    return torch.randn((H, 2 * R + 1), generator=g, dtype=torch.float32).numpy()
 
 
 def as_element_type(x: torch.Tensor, dtype: str) -> torch.Tensor:
@@ -166,6 +179,7 @@ class Inputs:
     doc_ids: np.ndarray | None  # int32 [B, S] or None
     slopes: np.ndarray | None   # float32 [H] or None
     extra: dict = field(default_factory=dict)
+    rel_bias: np.ndarray | None = None   # float32 [H, 2R + 1] or None
 
 
 def make_inputs(wl: Workload) -> Inputs:
@@ -178,4 +192,5 @@ def make_inputs(wl: Workload) -> Inputs:
                                                       *wl.doc_len_range))
                         for b in range(wl.B)]).astype(np.int32)
     slopes = alibi_slopes(wl.H) if wl.mod == "alibi" else None
-    return Inputs(wl, q, k, v, doc, slopes)
+    rel = rel_bias_table(wl.H, wl.rel_max, wl.seed) if wl.mod == "relbias" else None
+    return Inputs(wl, q, k, v, doc, slopes, rel_bias=rel)
