@@ -65,6 +65,16 @@ def mask_kind_of(causal: bool, window: int, documents: bool, prefix: bool = Fals
             | (MASK_DOCUMENT if documents else 0) | (MASK_PREFIX if prefix else 0))
 
 
+def set_layout(p: Params, q, k, v, out) -> None:
+    """Element strides {batch, head, row} of [B, H, S, D] tensors whose last
+    dimension is contiguous (views of other layouts, e.g. [B, S, H, D]
+    transposed, need no copy)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out)):
+        if t.stride(3) != 1:
+            raise TypeError(f"{name}: the last dimension must be contiguous")
+        getattr(p, f"{name}_stride")[:] = [t.stride(0), t.stride(1), t.stride(2)]
+
+
 def make_params(var: Variant, dtype: torch.dtype) -> Params:
     p = Params()
     if dtype not in _DTYPES:
@@ -123,7 +133,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
               scale: float | None = None, block_mask: BuiltBlockMask | None | str = "auto",
               out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
               with_lse: bool = True, stream=None):
-    """O (and LSE) of the attention forward for [B, H, S, D] tensors.
+    """O (and LSE) of the attention forward for [B, H, S, D] tensors (any
+    strides with a contiguous last dimension; `out` defaults to q's layout).
 
     block_mask: "auto" builds one for the variant; None visits every key tile
     with the per-element mask; or a BuiltBlockMask from build_block_mask().
@@ -132,8 +143,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
     B, H, Sq, D = q.shape
     _, Hkv, Skv, _ = k.shape
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise TypeError("q, k, v must be contiguous device tensors of one dtype")
+        if not t.is_cuda or t.dtype != q.dtype or t.dim() != 4:
+            raise TypeError("q, k, v must be 4-D device tensors of one dtype")
     if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("shape mismatch between q, k and v")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -143,9 +154,10 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if isinstance(block_mask, str):
         block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
+    params = make_params(var, q.dtype)
+    set_layout(params, q, k, v, out)
     flexattn_fwd(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, var.mask_kind, var.mod_kind,
-                 make_params(var, q.dtype), block_mask.struct if block_mask is not None else None,
-                 stream)
+                 params, block_mask.struct if block_mask is not None else None, stream)
     return out, lse
 
 

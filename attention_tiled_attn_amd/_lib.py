@@ -43,7 +43,9 @@ class Params(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("window", ctypes.c_int), ("softcap", ctypes.c_float),
                 ("alibi_slopes", ctypes.c_void_p), ("doc_ids", ctypes.c_void_p),
                 ("doc_stride", ctypes.c_int), ("q_offset", ctypes.c_int), ("prefix", ctypes.c_int),
-                ("rel_bias", ctypes.c_void_p), ("rel_max", ctypes.c_int)]
+                ("rel_bias", ctypes.c_void_p), ("rel_max", ctypes.c_int),
+                ("q_stride", ctypes.c_longlong * 3), ("k_stride", ctypes.c_longlong * 3),
+                ("v_stride", ctypes.c_longlong * 3), ("o_stride", ctypes.c_longlong * 3)]
 
 
 class BlockMask(ctypes.Structure):

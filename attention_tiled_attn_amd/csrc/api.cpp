@@ -26,7 +26,32 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0, 0, 0, nullptr, 0};
+const flexattn_params kDefaultParams = {FLEXATTN_BF16, 0, 0.f, nullptr, nullptr, 0, 0, 0, nullptr, 0,
+                                        {0, 0, 0}, {0, 0, 0}, {0, 0, 0}, {0, 0, 0}};
+
+// Effective strides {batch, head, row} of one tensor: the given ones, or the
+// contiguous layout [heads][rows][D] per batch when all three are zero.
+struct Strides {
+  long long b, h, r;
+};
+Strides strides_of(const long long (&s)[3], int heads, int rows, int D) {
+  if (s[0] == 0 && s[1] == 0 && s[2] == 0)
+    return {static_cast<long long>(heads) * rows * D, static_cast<long long>(rows) * D, D};
+  return {s[0], s[1], s[2]};
+}
+bool is_contiguous(const Strides& s, int heads, int rows, int D) {
+  return s.b == static_cast<long long>(heads) * rows * D && s.h == static_cast<long long>(rows) * D && s.r == D;
+}
+// Checks of one tensor's layout: element strides, 16-byte alignment of every
+// row, and 32-bit byte offsets within one (batch, head) slice including one
+// query tile of rows past the end, which the kernels read as zeros.
+int check_layout(const Strides& s, int rows, int D, long long esz) {
+  if (s.b < 0 || s.h < 0 || s.r < D) return FLEXATTN_ERR_ARG;
+  const long long q16 = 16 / esz;
+  if (s.b % q16 || s.h % q16 || s.r % q16) return FLEXATTN_ERR_ALIGN;
+  if ((static_cast<long long>(rows) + FLEXATTN_QTILE) * s.r * esz > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+  return FLEXATTN_OK;
+}
 
 constexpr int kMaskBits = FLEXATTN_MASK_CAUSAL | FLEXATTN_MASK_WINDOW | FLEXATTN_MASK_DOCUMENT |
                           FLEXATTN_MASK_PREFIX;
@@ -249,6 +274,20 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.mask_kind = mask_kind;
   p.mod_kind = mod_kind;
   fill_variant(p.va, prm, scale, mask_kind, mod_kind);
+  {
+    const long long esz = p.is_fp32 ? 4 : 2;
+    const Strides qs = strides_of(prm->q_stride, H, Sq, D), ks = strides_of(prm->k_stride, Hkv, Skv, D);
+    const Strides vs = strides_of(prm->v_stride, Hkv, Skv, D), os = strides_of(prm->o_stride, H, Sq, D);
+    int ls = check_layout(qs, Sq, D, esz);
+    if (!ls) ls = check_layout(ks, Skv, D, esz);
+    if (!ls) ls = check_layout(vs, Skv, D, esz);
+    if (!ls) ls = check_layout(os, Sq, D, esz);
+    if (ls) return ls;
+    p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
+    p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);
+    p.v_sb = vs.b; p.v_sh = vs.h; p.v_sr = static_cast<int>(vs.r);
+    p.o_sb = os.b; p.o_sh = os.h; p.o_sr = static_cast<int>(os.r);
+  }
   p.kv_count = block_mask ? block_mask->kv_count : nullptr;
   p.kv_list = block_mask ? block_mask->kv_list : nullptr;
   p.nq = ceil_div(Sq, FLEXATTN_QTILE);
@@ -271,6 +310,11 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   if (st) return st;
   if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
   if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
+  if (!is_contiguous(strides_of(prm->q_stride, H, Sq, D), H, Sq, D) ||
+      !is_contiguous(strides_of(prm->k_stride, Hkv, Skv, D), Hkv, Skv, D) ||
+      !is_contiguous(strides_of(prm->v_stride, Hkv, Skv, D), Hkv, Skv, D) ||
+      !is_contiguous(strides_of(prm->o_stride, H, Sq, D), H, Sq, D))
+    return FLEXATTN_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return FLEXATTN_ERR_ALIGN;

@@ -165,16 +165,17 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   const int b = bh / p.H;
   const int kvh = h / (p.H / p.Hkv);
 
-  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
-  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE rows
 
   constexpr unsigned esz = F32 ? 4u : 2u;
-  const char* qbase = static_cast<const char*>(p.q) + q_head * D * esz;
-  const char* kbase = static_cast<const char*>(p.k) + kv_head * D * esz;
-  const char* vbase = static_cast<const char*>(p.v) + kv_head * D * esz;
-  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq) * D * esz);
-  const rsrc_t rk = make_rsrc(kbase, static_cast<unsigned>(p.Skv) * D * esz);
-  const rsrc_t rv = make_rsrc(vbase, static_cast<unsigned>(p.Skv) * D * esz);
+  // a (batch, head) slice spans rows 0 .. S - 1 (row strides in elements),
+  // so rows past the end read as zero
+  const char* qbase = static_cast<const char*>(p.q) + (b * p.q_sb + h * p.q_sh) * esz;
+  const char* kbase = static_cast<const char*>(p.k) + (b * p.k_sb + kvh * p.k_sh) * esz;
+  const char* vbase = static_cast<const char*>(p.v) + (b * p.v_sb + kvh * p.v_sh) * esz;
+  const rsrc_t rq = make_rsrc(qbase, (static_cast<unsigned>(p.Sq - 1) * p.q_sr + D) * esz);
+  const rsrc_t rk = make_rsrc(kbase, (static_cast<unsigned>(p.Skv - 1) * p.k_sr + D) * esz);
+  const rsrc_t rv = make_rsrc(vbase, (static_cast<unsigned>(p.Skv - 1) * p.v_sr + D) * esz);
 
   // ---- this wave's 32 query rows; lane owns row q_row
   const int q_row = qt * kBM + wave * 32 + l32;
@@ -185,7 +186,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   bf16x8 qf[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c)
-    qf[c] = __builtin_bit_cast(bf16x8, buf_load8<F32>(rq, static_cast<unsigned>(q_row) * D + c * 16 + g * 8));
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load8<F32>(rq, static_cast<unsigned>(q_row) * p.q_sr + c * 16 + g * 8));
 
   // ---- key-tile schedule
   const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
@@ -227,14 +228,14 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
       const int ci = tid + i * kThreads;
       const int row = ci / (D / 8);
       const int col = (ci % (D / 8)) * 8;
-      u32x4 r = buf_load8<F32>(rk, static_cast<unsigned>(kv0 + row) * D + col);
+      u32x4 r = buf_load8<F32>(rk, static_cast<unsigned>(kv0 + row) * p.k_sr + col);
 #pragma unroll
       for (int j = 0; j < 4; ++j) kreg[i][j] = r[j];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = kv0 + vr * 4 + i;
-      buf_loadN<F32, G::vCols>(rv, static_cast<unsigned>(row) * D + vc * G::vCols, vreg[i]);
+      buf_loadN<F32, G::vCols>(rv, static_cast<unsigned>(row) * p.v_sr + vc * G::vCols, vreg[i]);
     }
   };
 
@@ -436,7 +437,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok) {
-    const size_t orow = (q_head + q_row) * D;
+    const size_t orow = b * p.o_sb + h * p.o_sh + static_cast<size_t>(q_row) * p.o_sr;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll

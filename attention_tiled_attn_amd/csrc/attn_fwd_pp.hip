@@ -108,13 +108,16 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int kvh = h / (p.H / p.Hkv);
-  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
-  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
-  const __bf16* qbase = static_cast<const __bf16*>(p.q) + q_head * D;
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + kv_head * D;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + kv_head * D;
-  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq) * RB);
-  const unsigned kv_bytes = static_cast<unsigned>(p.Skv) * RB;
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE rows
+  // row strides in bytes; a (batch, head) slice spans rows 0 .. S - 1, so
+  // rows past the end read as zero
+  const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u;
+  const unsigned grb = static_cast<unsigned>(grp ? p.v_sr : p.k_sr) * 2u;   // this group's K or V
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh;
+  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq - 1) * qrb + RB);
+  const unsigned kv_bytes = static_cast<unsigned>(p.Skv - 1) * grb + RB;
   const u32x4 desc = grp ? make_desc(vbase, kv_bytes) : make_desc(kbase, kv_bytes);
 
   const int q_row = qp * kBM + grp * kPairHalf + wq * 32 + l32;
@@ -125,7 +128,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
   for (int c = 0; c < DC; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-        rq, static_cast<unsigned>(q_row) * RB + (c * 16 + g * 8) * 2, 0, 0));
+        rq, static_cast<unsigned>(q_row) * qrb + (c * 16 + g * 8) * 2, 0, 0));
 
   // ---- key-tile list of this 256-row tile, into LDS. Entry:
   // (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0 (half 0 = rows
@@ -171,7 +174,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     const int s = (wq * G::kDma + j) * 64 + lane;
     const int r = s / G::kCpr, pos = s % G::kCpr;
     const int c = pos ^ (grp ? vswz<D>(r) : kswz<D>(r));
-    goff[j] = r * RB + c * 16;
+    goff[j] = r * grb + c * 16;
   }
   const unsigned my_lds =
       __builtin_amdgcn_readfirstlane(lds_addr(grp ? vbuf : kbuf) + wq * G::kDma * 1024);
@@ -184,7 +187,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // group 0 copies K(t), group 1 V(t), into ring slot `ring`
   auto issue_copy = [&](int t, int e, int ring) {
     const int kv0 = stage_kv0(t, e);
-    const unsigned gbase = static_cast<unsigned>(kv0) * RB;
+    const unsigned gbase = static_cast<unsigned>(kv0) * grb;
     const unsigned lbase = my_lds + ring * G::kBufBytes;
 #pragma unroll
     for (int j = 0; j < G::kDma; ++j)
@@ -459,7 +462,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok) {
-    const size_t orow = (q_head + q_row) * D;
+    __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
+    const size_t orow = static_cast<size_t>(q_row) * p.o_sr;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -467,7 +471,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         const int d0 = db * 32 + 8 * i + 4 * g;
         const u32x2 vv = {pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
                           pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv)};
-        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.out) + orow + d0) = vv;
+        *reinterpret_cast<u32x2*>(obase + orow + d0) = vv;
       }
     if (p.lse && g == 0)
       p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;

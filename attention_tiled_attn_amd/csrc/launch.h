@@ -26,6 +26,9 @@ struct FwdLaunch {
   int mask_kind;
   int mod_kind;
   VariantArgs va;
+  // element strides of q, k, v, out: batch and head (64-bit) and row
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sr, k_sr, v_sr, o_sr;
   // block mask (kv_count == nullptr: visit every key tile as partial);
   // nq counts 256-row query tiles
   const int* kv_count;

@@ -126,6 +126,15 @@ typedef struct flexattn_params {
   const float* rel_bias;     /* device float32 [H][2 * rel_max + 1], 16-byte aligned,
                                 when mod_kind is FLEXATTN_MOD_RELBIAS                  */
   int rel_max;               /* R in [0, FLEXATTN_REL_MAX] for FLEXATTN_MOD_RELBIAS   */
+  /* Layout of q, k, v and out: element strides {batch, head, row}; the last
+   * (D) dimension is always contiguous. All three zero (the default) means the
+   * contiguous [B][H][S][D] layout; e.g. a [B][S][H][D] buffer viewed as
+   * [B][H][S][D] has strides {S*H*D, D, H*D}. Strides are >= 0, a row stride
+   * is >= D, and each stride times the element size is a multiple of 16
+   * bytes (else FLEXATTN_ERR_ALIGN). Rows of out must not overlap. LSE is
+   * always contiguous [B][H][Sq]. flexattn_bwd takes the contiguous layout
+   * only (FLEXATTN_ERR_UNSUPPORTED otherwise).                               */
+  long long q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } flexattn_params;
 
 /* Block mask: for every query tile of FLEXATTN_QTILE rows, the ascending list

@@ -87,6 +87,9 @@ def P(**kw):
     p.prefix = kw.get("prefix", 0)
     p.rel_bias = kw.get("rel_bias")
     p.rel_max = kw.get("rel_max", 0)
+    for name in ("q", "k", "v", "o"):
+        if name + "_stride" in kw:
+            getattr(p, name + "_stride")[:] = kw[name + "_stride"]
     return p
 
 
@@ -140,6 +143,24 @@ def P(**kw):
 ])
 def test_fwd_validation(over, code):
     assert call(**over) == code
+
+
+# layouts: GOOD is B=1, H=2, S=128, D=64 in bf16 (16 bytes = 8 elements)
+@pytest.mark.parametrize("stride,code", [
+    ((64 * 128, 64, 64 * 2), _lib.ERR_ALIGN),       # ok up to here? see below
+    ((2 * 128 * 64, 128 * 64, 63), _lib.ERR_ARG),    # row stride below D
+    ((2 * 128 * 64, 128 * 64, 68), _lib.ERR_ALIGN),  # rows not 16-byte aligned
+    ((-8, 128 * 64, 64), _lib.ERR_ARG),              # negative
+    ((2 * 128 * 64, 4, 64), _lib.ERR_ALIGN),         # head stride not 16-byte aligned
+    ((0, 0, 2**26), _lib.ERR_OVERFLOW),              # a slice beyond 32-bit byte offsets
+])
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_fwd_layout_validation(stride, code, which):
+    if stride == (64 * 128, 64, 64 * 2):
+        # a valid [B, S, H, D] view: stops at the misaligned output instead
+        assert call(params=P(**{which + "_stride": stride}), out=A + 2) == _lib.ERR_ALIGN
+        return
+    assert call(params=P(**{which + "_stride": stride})) == code
 
 
 def bm_struct(**kw):
@@ -217,6 +238,14 @@ def test_error_raises_with_message():
 # ------------------------------------------------------------------ backward validation
 BGOOD = dict(q=A, k=A, v=A, out=A, lse=A, dout=A, dq=A, dk=A, dv=A, delta=A, B=1, H=2, Hkv=2,
              Sq=128, Skv=128, D=64, scale=0.125, mask_kind=0, mod_kind=0)
+
+
+def test_bwd_rejects_strided_layouts():
+    # the backward takes the contiguous layout only (explicit contiguous strides are fine)
+    bshd = (128 * 2 * 64, 64, 2 * 64)
+    for which in ("q", "k", "v", "o"):
+        assert bcall(params=P(**{which + "_stride": bshd})) == _lib.ERR_UNSUPPORTED
+    assert bcall(params=P(q_stride=(2 * 128 * 64, 128 * 64, 64)), dq=A + 2) == _lib.ERR_ALIGN
 
 
 def bcall(**over):

@@ -241,3 +241,49 @@ def test_full_size_sampled(name):
     say(f"[parity] {name}: {stats}")
     # every element written (outputs were NaN-filled)
     assert not torch.isnan(O).any().item() and not torch.isnan(L).any().item()
+
+
+# ------------------------------------------------------------------ strided layouts
+def _bshd(t: torch.Tensor) -> torch.Tensor:
+    """The same values in a [B, S, H, D] buffer, viewed as [B, H, S, D]."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("case", [
+    dict(S=300, D=64), dict(S=257, D=128, causal=True),
+    dict(B=2, H=4, Hkv=2, S=333, D=128, causal=True, window=100),
+    dict(B=2, H=4, Hkv=1, S=200, D=64, documents=True, mod="alibi"),
+    dict(Sq=70, Skv=400, q_offset=330, D=128, causal=True, mod="relbias", rel_max=50),
+    dict(S=190, D=64, dtype="fp32", causal=True), dict(S=260, D=128, dtype="fp32"),
+], ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+def test_strided_layouts_match_contiguous_bitwise(case):
+    """[B, S, H, D] buffers viewed as [B, H, S, D] (q, k, v and out) give the
+    contiguous call's bits, and the oracle's values."""
+    inp = small(doc_range=(30, 150), **case)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    O1, L1 = run_gpu(inp, qkv=(q, k, v))
+    qs, ks, vs = _bshd(q), _bshd(k), _bshd(v)
+    assert not qs.is_contiguous() and qs.stride(3) == 1
+    out = _bshd(torch.full_like(q, float("nan")))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    fa.attention(qs, ks, vs, device_variant(inp), scale=inp.wl.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, O1) and torch.equal(lse, L1)
+    Oref, Lref = run_oracle(inp)
+    compare(to_np(out), to_np(lse), Oref, Lref, f"strided {case}")
+
+
+def test_strided_kv_shared_across_batch():
+    """Batch stride 0 for K and V: every batch row reads the same keys."""
+    inp = small(B=3, H=2, S=150, D=64, causal=True)
+    q = inp.q.cuda()
+    k1, v1 = inp.k[:1].cuda(), inp.v[:1].cuda()
+    kb, vb = k1.expand(3, -1, -1, -1), v1.expand(3, -1, -1, -1)
+    assert kb.stride(0) == 0
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa.attention(q, kb, vb, fa.Variant(causal=True), scale=inp.wl.scale, out=out, lse=lse)
+    ref_out, ref_lse = fa.attention(q, kb.contiguous(), vb.contiguous(), fa.Variant(causal=True),
+                                    scale=inp.wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
