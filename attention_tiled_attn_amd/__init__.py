@@ -16,7 +16,8 @@ import torch
 from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_PREFIX, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
     MOD_RELBIAS, MOD_SOFTCAP, QTILE, REL_MAX, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
-    flexattn_build_block_mask, flexattn_bwd, flexattn_fwd, flexattn_last_error, flexattn_strerror,
+    flexattn_build_block_mask, flexattn_bwd, flexattn_decode, flexattn_decode_splits,
+    flexattn_decode_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_strerror,
     flexattn_version, lib,
 )
 
@@ -24,6 +25,7 @@ __all__ = [
     "QTILE", "TILE", "flexattn_fwd", "flexattn_bwd", "flexattn_build_block_mask", "flexattn_block_mask_bytes", "flexattn_strerror",
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
     "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError", "attention_backward",
+    "flexattn_decode", "flexattn_decode_splits", "flexattn_decode_workspace_bytes", "decode",
 ]
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
@@ -158,6 +160,40 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
     set_layout(params, q, k, v, out)
     flexattn_fwd(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, var.mask_kind, var.mod_kind,
                  params, block_mask.struct if block_mask is not None else None, stream)
+    return out, lse
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | None = None, *,
+           scale: float | None = None, block_mask: BuiltBlockMask | None | str = "auto",
+           splits: int | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, with_lse: bool = True,
+           workspace: torch.Tensor | None = None, stream=None):
+    """attention() for few query rows per key/value head (decoding, short
+    prefill chunks; bf16): the query heads of a group share a workgroup and the
+    key range is split `splits` ways (default flexattn_decode_splits). The
+    split results need a float32 workspace, allocated here unless given."""
+    var = var or Variant()
+    B, H, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    for t in (q, k, v):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise TypeError("q, k, v must be 4-D bf16 device tensors")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    splits = flexattn_decode_splits(B, Hkv, Skv) if splits is None else int(splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    nbytes = flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    if isinstance(block_mask, str):
+        block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
+    params = make_params(var, q.dtype)
+    set_layout(params, q, k, v, out)
+    flexattn_decode(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, var.mask_kind, var.mod_kind,
+                    params, block_mask.struct if block_mask is not None else None, splits,
+                    workspace, workspace.numel() * 4 if workspace is not None else 0, stream)
     return out, lse
 
 

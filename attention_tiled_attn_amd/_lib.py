@@ -27,7 +27,8 @@ TILE = 128
 QTILE = 256
 
 EXPORTS = ("flexattn_version", "flexattn_strerror", "flexattn_last_error",
-           "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd", "flexattn_bwd")
+           "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd", "flexattn_bwd",
+           "flexattn_decode_workspace_bytes", "flexattn_decode_splits", "flexattn_decode")
 
 
 class FlexAttnError(RuntimeError):
@@ -83,6 +84,14 @@ def lib() -> ctypes.CDLL:
         L.flexattn_fwd.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_float, c_int, c_int, ctypes.POINTER(Params),
                                    ctypes.POINTER(BlockMask), vp]
+        L.flexattn_decode_workspace_bytes.restype = sz
+        L.flexattn_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+        L.flexattn_decode_splits.restype = c_int
+        L.flexattn_decode_splits.argtypes = [c_int, c_int, c_int]
+        L.flexattn_decode.restype = c_int
+        L.flexattn_decode.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_float, c_int, c_int, ctypes.POINTER(Params),
+                                      ctypes.POINTER(BlockMask), c_int, vp, sz, vp]
         L.flexattn_bwd.restype = c_int
         L.flexattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int,
                                    c_int, c_int, c_int, c_float, c_int, c_int,
@@ -156,6 +165,28 @@ def flexattn_fwd(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: int,
                             _stream(stream, q))
     if check:
         _check(st, "flexattn_fwd")
+    return st
+
+
+def flexattn_decode_workspace_bytes(B: int, H: int, Hkv: int, Sq: int, D: int, splits: int) -> int:
+    return int(lib().flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits))
+
+
+def flexattn_decode_splits(B: int, Hkv: int, Skv: int) -> int:
+    return int(lib().flexattn_decode_splits(B, Hkv, Skv))
+
+
+def flexattn_decode(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: int, D: int,
+                    scale: float, mask_kind: int, mod_kind: int, params: Params | None = None,
+                    block_mask: BlockMask | None = None, splits: int = 1, workspace=None,
+                    workspace_bytes: int = 0, stream=None, *, check: bool = True) -> int:
+    st = lib().flexattn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq, Skv,
+                               D, scale, mask_kind, mod_kind,
+                               ctypes.byref(params) if params else None,
+                               ctypes.byref(block_mask) if block_mask else None, splits,
+                               _ptr(workspace), workspace_bytes, _stream(stream, q))
+    if check:
+        _check(st, "flexattn_decode")
     return st
 
 

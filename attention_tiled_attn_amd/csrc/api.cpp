@@ -298,6 +298,96 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   return FLEXATTN_OK;
 }
 
+size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || Sq < 1 || (D != 64 && D != 128) || splits < 1 || splits > 64)
+    return 0;
+  if (splits == 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * H * Sq;   // = B * Hkv * (rep * Sq)
+  return static_cast<size_t>(splits) * rows * (static_cast<size_t>(D) + 1) * sizeof(float);
+}
+
+int flexattn_decode_splits(int B, int Hkv, int Skv) {
+  if (B < 1 || Hkv < 1 || Skv < 1) return 1;
+  const long long tiles = ceil_div(Skv, FLEXATTN_TILE);
+  const long long groups = static_cast<long long>(B) * Hkv;
+  long long s = (2 * 256 + groups - 1) / groups;   // about two workgroups per CU
+  s = std::min<long long>(s, std::max<long long>(1, tiles / 4));
+  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, 64)));
+}
+
+int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                    const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const flexattn_params* prm = params ? params : &kDefaultParams;
+  if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
+  int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
+  if (st) return st;
+  if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
+  const int rep = H / Hkv;
+  if (static_cast<long long>(rep) * Sq > FLEXATTN_QTILE) return FLEXATTN_ERR_UNSUPPORTED;
+  if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
+  if (mod_kind == FLEXATTN_MOD_RELBIAS &&
+      static_cast<long long>(rep) * (2LL * prm->rel_max + 1) > fa::kRelCap)
+    return FLEXATTN_ERR_UNSUPPORTED;
+  if (splits < 1 || splits > 64) return FLEXATTN_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
+  if (splits > 1) {
+    if (!workspace) return FLEXATTN_ERR_NULLPTR;
+    if (!aligned(workspace, 16)) return FLEXATTN_ERR_ALIGN;
+    if (workspace_bytes < flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits)) return FLEXATTN_ERR_ARG;
+  }
+
+  fa::FwdLaunch p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = D;
+  p.is_fp32 = 0;
+  p.mask_kind = mask_kind;
+  p.mod_kind = mod_kind;
+  fill_variant(p.va, prm, scale, mask_kind, mod_kind);
+  {
+    const Strides qs = strides_of(prm->q_stride, H, Sq, D), ks = strides_of(prm->k_stride, Hkv, Skv, D);
+    const Strides vs = strides_of(prm->v_stride, Hkv, Skv, D), os = strides_of(prm->o_stride, H, Sq, D);
+    int ls = check_layout(qs, Sq, D, 2);
+    if (!ls) ls = check_layout(ks, Skv, D, 2);
+    if (!ls) ls = check_layout(vs, Skv, D, 2);
+    if (!ls) ls = check_layout(os, Sq, D, 2);
+    if (ls) return ls;
+    // the rows of a group's rep query heads are addressed from its first head
+    // with 32-bit byte offsets
+    if (((rep - 1) * qs.h + static_cast<long long>(Sq + FLEXATTN_QTILE) * qs.r) * 2 > INT_MAX)
+      return FLEXATTN_ERR_OVERFLOW;
+    p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
+    p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);
+    p.v_sb = vs.b; p.v_sh = vs.h; p.v_sr = static_cast<int>(vs.r);
+    p.o_sb = os.b; p.o_sh = os.h; p.o_sr = static_cast<int>(os.r);
+  }
+  p.kv_count = block_mask ? block_mask->kv_count : nullptr;
+  p.kv_list = block_mask ? block_mask->kv_list : nullptr;
+  p.nq = ceil_div(Sq, FLEXATTN_QTILE);
+  p.nk = ceil_div(Skv, FLEXATTN_TILE);
+  p.bm_num_b = block_mask ? block_mask->num_b : 1;
+  p.splits = splits;
+  if (splits > 1) {
+    const size_t rows = static_cast<size_t>(B) * H * Sq;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + static_cast<size_t>(splits) * rows * D;
+  }
+  hipError_t e = fa::launch_attn_decode(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return FLEXATTN_OK;
+}
+
 int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
                  int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,

@@ -74,7 +74,10 @@ __device__ inline int kswz(int r) { return (r / (128 / D)) % (D / 8); }
 template <int D>
 __device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-template <int D, int MOD, bool DOCS>
+// PACK (decode mode): a workgroup owns the rep = H / Hkv query heads of one
+// key/value head, packed as rows r = head_in_group * Sq + q_row (at most 256),
+// and one of p.splits contiguous parts of the key-tile list of query tile 0.
+template <int D, int MOD, bool DOCS, bool PACK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = PGeo<D>;
@@ -96,39 +99,50 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // ---- workgroup -> (b, h, 256-row tile): XCD-contiguous, heavy tiles first
-  const int np = (p.Sq + kBM - 1) / kBM;
-  const int total = p.B * p.H * np;
+  // ---- workgroup -> (b, h, 256-row tile): XCD-contiguous, heavy tiles first;
+  // decode mode: (b, key/value head, split)
+  const int rep = p.H / p.Hkv;
+  const int np = PACK ? 1 : (p.Sq + kBM - 1) / kBM;
+  const int total = PACK ? p.B * p.Hkv * p.splits : p.B * p.H * np;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int wg = blockIdx.x;
   const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
   if (lin >= total) return;
-  const int qp = np - 1 - (lin % np);
-  const int bh = lin / np;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
-  const int kvh = h / (p.H / p.Hkv);
+  const int qp = PACK ? 0 : np - 1 - (lin % np);
+  const int split = PACK ? lin % p.splits : 0;
+  const int b = PACK ? lin / p.splits / p.Hkv : lin / np / p.H;
+  const int kvh = PACK ? (lin / p.splits) % p.Hkv : ((lin / np) % p.H) / rep;
+  // this lane's row: packed index r (decode mode), its query head and row
+  const int r_lane = grp * kPairHalf + wq * 32 + l32;
+  const int hl = PACK ? min(r_lane / p.Sq, rep - 1) : 0;
+  const int h = PACK ? kvh * rep + hl : (lin / np) % p.H;   // lane-varying in decode mode
+  const int q_row = PACK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
+  const bool q_ok = PACK ? r_lane < rep * p.Sq : q_row < p.Sq;
   const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE rows
   // row strides in bytes; a (batch, head) slice spans rows 0 .. S - 1, so
-  // rows past the end read as zero
+  // rows past the end read as zero (decode mode: the slices of the group's
+  // heads, from its first head)
   const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u;
   const unsigned grb = static_cast<unsigned>(grp ? p.v_sr : p.k_sr) * 2u;   // this group's K or V
-  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.q_sb + (PACK ? kvh * rep : h) * p.q_sh;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh;
-  const rsrc_t rq = make_rsrc(qbase, static_cast<unsigned>(p.Sq - 1) * qrb + RB);
+  const unsigned q_bytes = PACK ? static_cast<unsigned>((rep - 1) * p.q_sh * 2 + (p.Sq - 1) * qrb + RB)
+                                : static_cast<unsigned>(p.Sq - 1) * qrb + RB;
+  const rsrc_t rq = make_rsrc(qbase, q_bytes);
   const unsigned kv_bytes = static_cast<unsigned>(p.Skv - 1) * grb + RB;
   const u32x4 desc = grp ? make_desc(vbase, kv_bytes) : make_desc(kbase, kv_bytes);
 
-  const int q_row = qp * kBM + grp * kPairHalf + wq * 32 + l32;
-  const bool q_ok = q_row < p.Sq;
-
-  // Q^T fragments (B operand of S^T): rows past Sq read as zero
+  // Q^T fragments (B operand of S^T): rows past Sq (and, in decode mode,
+  // packed rows past the group) read as zero
+  const unsigned q_off = !q_ok ? 0x80000000u
+                         : PACK ? static_cast<unsigned>(hl * p.q_sh * 2) + static_cast<unsigned>(q_row) * qrb
+                                : static_cast<unsigned>(q_row) * qrb;
   bf16x8 qf[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-        rq, static_cast<unsigned>(q_row) * qrb + (c * 16 + g * 8) * 2, 0, 0));
+        rq, q_off + (c * 16 + g * 8) * 2, 0, 0));
 
   // ---- key-tile list of this 256-row tile, into LDS. Entry:
   // (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0 (half 0 = rows
@@ -136,12 +150,34 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // both halves partial.
   const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
-  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
-  for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : ((i << 4) | 0x5);
-  if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
+  int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
+  int e_first = 0;
+  if constexpr (PACK) {
+    // this split's part of the list; every packed row lies in query tile 0,
+    // so a tile is visited when either half admits a pair, and skips the
+    // per-element mask only when both halves are full (half 1 has no rows
+    // when Sq <= 128)
+    const int n_all = n_entries;
+    e_first = static_cast<int>(static_cast<long long>(n_all) * split / p.splits);
+    n_entries = static_cast<int>(static_cast<long long>(n_all) * (split + 1) / p.splits) - e_first;
+    for (int i = tid; i < n_entries; i += kThreads) {
+      const int e = list ? list[e_first + i] : (((e_first + i) << 4) | 0x5);
+      const bool full = (e & 2) && ((e & 8) || p.Sq <= kPairHalf);
+      ents[i] = (e & ~15) | ((e & 5) ? (full ? 0xF : 0x5) : 0);
+    }
+  } else {
+    for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : ((i << 4) | 0x5);
+  }
+  if constexpr (MOD == kModRelBias) {
+    // decode mode: the tables of all rep heads of the group, one after another
+    const int n_tab = 2 * p.va.rel_max + 1;
+    const int h0 = PACK ? kvh * rep : __builtin_amdgcn_readfirstlane(h);
+    for (int j = 0; j < (PACK ? rep : 1); ++j)
+      stage_rel_table(p.va, h0 + j, (lds_f32*)(rtab) + j * n_tab, tid, kThreads);
+  }
   int n_stages = 2 * n_entries;
   if (n_entries > 0) {
-    const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
+    const int last = list ? (list[e_first + n_entries - 1] >> 4) : (e_first + n_entries - 1);
     if (last * kTile + kBN >= p.Skv) n_stages -= 1;   // last tile has a single 64-key stage
   }
   __syncthreads();
@@ -214,7 +250,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
   const typename SM::Lane sml = [&] {
     typename SM::Lane L = SM::lane(p.va, h, q_pos);
-    if constexpr (MOD == kModRelBias) L.tab = (lds_cf32*)(rtab) + p.va.rel_max;
+    if constexpr (MOD == kModRelBias) L.tab = (lds_cf32*)(rtab) + hl * (2 * p.va.rel_max + 1) + p.va.rel_max;
     return L;
   }();
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
@@ -276,10 +312,13 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     bool clipped = false;
     float clip_add = 0.f;
     if constexpr (MOD == kModRelBias) {
-      const int qw = __builtin_amdgcn_readfirstlane(q_pos);   // lane 0 holds the wave's first row
+      // the wave's rows lie in [qw, qw + span]: lane 0 holds the first of 32
+      // consecutive rows; in decode mode any row of query tile 0
+      const int qw = PACK ? p.va.q_offset : __builtin_amdgcn_readfirstlane(q_pos);
+      const int span = PACK ? p.Sq - 1 : 31;
       const int R = p.va.rel_max;
       const bool below = kv0 + kBN - 1 - qw < -R;   // largest distance below -R
-      const bool above = kv0 - (qw + 31) > R;       // smallest distance above R
+      const bool above = kv0 - (qw + span) > R;     // smallest distance above R
       clipped = below || above;
       if (clipped) clip_add = sml.tab[below ? -R : R] * kLog2e;
     }
@@ -461,7 +500,24 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // ---- epilogue: normalise, LSE, store
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (q_ok) {
+  if (PACK && p.splits > 1) {
+    // this split's normalised rows and LSE, merged by attn_decode_merge_kernel
+    if (q_ok) {
+      const int rows = rep * p.Sq;
+      const size_t wrow = ((static_cast<size_t>(split) * p.B + b) * p.Hkv + kvh) * rows + r_lane;
+      float* const wo = p.ws_o + wrow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + 8 * i + 4 * g;
+          const f32x4 vv = {o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                            o[db][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4*>(wo + d0) = vv;
+        }
+      if (g == 0) p.ws_lse[wrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else if (q_ok) {
     __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
     const size_t orow = static_cast<size_t>(q_row) * p.o_sr;
 #pragma unroll
@@ -478,34 +534,82 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   }
 }
 
-template <int D, int MOD, bool DOCS>
+template <int D, int MOD, bool DOCS, bool PACK>
 hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const int np = (p.Sq + kBM - 1) / kBM;
-  const long long total = static_cast<long long>(p.B) * p.H * np;
+  const long long total = PACK ? static_cast<long long>(p.B) * p.Hkv * p.splits
+                               : static_cast<long long>(p.B) * p.H * np;
   const long long per = (total + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS, PACK>), dim3(static_cast<unsigned>(per * kXcds)),
                      dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
   return hipGetLastError();
 }
 
-template <int D, bool DOCS>
+template <int D, bool DOCS, bool PACK>
 hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
   switch (p.mod_kind) {
-    case kModNone: return launch_t<D, kModNone, DOCS>(p, stream);
-    case kModAlibi: return launch_t<D, kModAlibi, DOCS>(p, stream);
-    case kModSoftcap: return launch_t<D, kModSoftcap, DOCS>(p, stream);
-    case kModRelBias: return launch_t<D, kModRelBias, DOCS>(p, stream);
+    case kModNone: return launch_t<D, kModNone, DOCS, PACK>(p, stream);
+    case kModAlibi: return launch_t<D, kModAlibi, DOCS, PACK>(p, stream);
+    case kModSoftcap: return launch_t<D, kModSoftcap, DOCS, PACK>(p, stream);
+    case kModRelBias: return launch_t<D, kModRelBias, DOCS, PACK>(p, stream);
   }
   return hipErrorInvalidValue;
 }
 
+template <bool PACK>
+hipError_t launch_dims(const FwdLaunch& p, hipStream_t stream) {
+  const bool docs = p.mask_kind & kMaskDocument;
+  if (p.D == 128) return docs ? launch_mod<128, true, PACK>(p, stream) : launch_mod<128, false, PACK>(p, stream);
+  if (p.D == 64) return docs ? launch_mod<64, true, PACK>(p, stream) : launch_mod<64, false, PACK>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+// Merge of the decode splits: for every (b, head, row) the split results
+// (O_s normalised, LSE_s) combine as LSE = log sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s (a row no split admitted anything for keeps
+// O = 0, LSE = -inf). One thread per 4 values of d.
+__global__ __launch_bounds__(256) void attn_decode_merge_kernel(FwdLaunch p) {
+  const int rep = p.H / p.Hkv, rows = rep * p.Sq, dq = p.D / 4;
+  const long long n = static_cast<long long>(p.B) * p.Hkv * rows * dq;
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int d0 = static_cast<int>(t % dq) * 4;
+  const long long grow = t / dq;   // (b, kvh, r)
+  const int r = static_cast<int>(grow % rows);
+  const long long bk = grow / rows;
+  const int kvh = static_cast<int>(bk % p.Hkv), b = static_cast<int>(bk / p.Hkv);
+  const size_t split_rows = static_cast<size_t>(p.B) * p.Hkv * rows;
+  float mx = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.ws_lse[s * split_rows + grow]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx > -INFINITY) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = __expf(p.ws_lse[s * split_rows + grow] - mx);
+      tot += w;
+      acc += w * *reinterpret_cast<const f32x4*>(p.ws_o + (s * split_rows + grow) * p.D + d0);
+    }
+    acc *= 1.0f / tot;
+  }
+  const int hl = r / p.Sq, q_row = r - hl * p.Sq, h = kvh * rep + hl;
+  __bf16* const orow = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh + static_cast<size_t>(q_row) * p.o_sr;
+  const u32x2 vv = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  *reinterpret_cast<u32x2*>(orow + d0) = vv;
+  if (p.lse && d0 == 0)
+    p.lse[(static_cast<size_t>(b) * p.H + h) * p.Sq + q_row] = mx > -INFINITY ? mx + __logf(tot) : -INFINITY;
+}
+
 }  // namespace
 
-hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) {
-  const bool docs = p.mask_kind & kMaskDocument;
-  if (p.D == 128) return docs ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
-  if (p.D == 64) return docs ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
-  return hipErrorInvalidValue;
+hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<false>(p, stream); }
+
+hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
+  hipError_t e = launch_dims<true>(p, stream);
+  if (e != hipSuccess || p.splits <= 1) return e;
+  const long long n = static_cast<long long>(p.B) * p.Hkv * (p.H / p.Hkv) * p.Sq * (p.D / 4);
+  hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -34,9 +34,18 @@ struct FwdLaunch {
   const int* kv_count;
   const int* kv_list;
   int nq, nk, bm_num_b;
+  // decode mode (launch_attn_decode): the H/Hkv query heads of a key/value
+  // head share a workgroup (rep * Sq <= 256 packed rows) and the key-tile list
+  // is split over `splits` workgroups; with splits > 1 each writes its rows'
+  // normalised O (float32) and LSE to ws_o [splits][B][Hkv][rows][D] and
+  // ws_lse [splits][B][Hkv][rows], merged by a second kernel
+  int splits;
+  float* ws_o;
+  float* ws_lse;
 };
 
 hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream);
+hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream);
 // bf16 inputs with nk <= kPairMaxKeyTiles (256-row ping-pong kernel)
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream);
 

@@ -257,6 +257,12 @@ def main(argv=None):
         delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
+    splits = workspace = None
+    if wl.decode:
+        splits = fa.flexattn_decode_splits(wl.B, wl.Hkv, wl.Skv)
+        nbytes = fa.flexattn_decode_workspace_bytes(wl.B, wl.H, wl.Hkv, wl.Sq, wl.D, splits)
+        workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=dev)
+
     def step(ev=None):
         bm = fa.build_block_mask(var, wl.B, wl.Sq, wl.Skv, dev)
         if ev is not None:
@@ -264,6 +270,9 @@ def main(argv=None):
         if bwd:
             fa.attention_backward(q, k, v, out, lse, dout, var, scale=wl.scale, block_mask=bm,
                                   dq=dq, dk=dk, dv=dv, delta=delta)
+        elif wl.decode:
+            fa.decode(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse,
+                      splits=splits, workspace=workspace)
         else:
             fa.attention(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse)
         if ev is not None:
@@ -309,6 +318,20 @@ def main(argv=None):
     if bwd:   # also reads dO and O, writes dQ, dK, dV and delta
         bytes_alg += (2 * q.numel() + q.numel() + k.numel() + v.numel()) * q.element_size() + lse.numel() * 4
     traffic = None if bwd else traffic_from_profile(wl.name)
+    if wl.decode:
+        # HBM-bound: K and V are read once, Q read and O, LSE written once
+        roof = {"bound": "hbm", "achieved": round(bytes_alg / (kern_avg_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(bytes_alg / (kern_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": bytes_alg,
+                "kernel": "attn_fwd_pp_kernel (decode mode) + attn_decode_merge_kernel",
+                "splits": splits}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_bytes": bytes_alg,
+                "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkdv_kernel" if bwd else
+                           "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel")}
 
     rec = {
         "metric": ("attention bwd effective TFLOPS (2.5x forward unmasked FLOPs), 1 GPU" if bwd else
@@ -333,17 +356,7 @@ def main(argv=None):
         "attn_kernel_ms_min": round(min(kern_ms), 4),
         "tile_tflops": round(tile_flop / (kern_avg_ms * 1e-3) / 1e12, 2),
         "admitted_pairs_per_head": pairs // wl.B,
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": bytes_alg,
-            "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkdv_kernel" if bwd else
-                       "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel"),
-        },
+        "roofline": roof,
         "kernel_sha": kernel_sha(),
         "gpu": torch.cuda.get_device_name(dev),
     }

@@ -210,6 +210,32 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const flexattn_params* params, const flexattn_block_mask* block_mask,
                  void* stream);
 
+/* Attention forward for few query rows per key/value head: decoding (Sq = 1
+ * with q_offset = Skv - 1) and short prefill chunks. Computes what
+ * flexattn_fwd computes, organised for that shape: the rep = H / Hkv query
+ * heads of a key/value head share a workgroup as rep * Sq packed rows (at most
+ * 256, else FLEXATTN_ERR_UNSUPPORTED), so each K/V element is read once, and
+ * the key tiles are split over `splits` workgroups (1 <= splits <= 64) whose
+ * normalised partial results are merged as O = sum_s exp(LSE_s - LSE) O_s,
+ * LSE = log sum_s exp(LSE_s) by a second kernel on the same stream. bf16
+ * only; every variant and layout of flexattn_fwd; block_mask as there (built
+ * for these Sq, Skv). With FLEXATTN_MOD_RELBIAS the group's tables must fit
+ * together: rep * (2 * rel_max + 1) <= 2 * FLEXATTN_REL_MAX + 2.
+ *   workspace : device memory of flexattn_decode_workspace_bytes(...) bytes,
+ *               16-byte aligned, caller-owned scratch (contents afterwards
+ *               unspecified); may be NULL when splits == 1
+ * Results equal flexattn_fwd's up to float32 rounding in the merge. */
+size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits);
+
+/* A split count for flexattn_decode that gives the chip at least ~2 workgroups
+ * per CU while leaving each at least 4 key tiles (128 keys each). */
+int flexattn_decode_splits(int B, int Hkv, int Skv);
+
+int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                    const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Attention backward: the gradients of L = sum(O * dout) with respect to q, k
  * and v, for O = flexattn_fwd(q, k, v, ...) with the same variant. The pages
  * name a backward pass used in training and a deterministic mode for it

@@ -279,3 +279,45 @@ def bcall(**over):
 ])
 def test_bwd_validation(over, code):
     assert bcall(**over) == code
+
+
+# ------------------------------------------------------------------ decode entry points
+def test_decode_workspace_and_splits():
+    # splits x rows x (D + 1) floats, rows = B * H * Sq; none for one split
+    assert fa.flexattn_decode_workspace_bytes(2, 8, 2, 3, 128, 5) == 5 * (2 * 8 * 3) * 129 * 4
+    assert fa.flexattn_decode_workspace_bytes(2, 8, 2, 3, 128, 1) == 0
+    for bad in [(0, 8, 2, 1, 128, 2), (1, 8, 3, 1, 128, 2), (1, 8, 2, 1, 96, 2), (1, 8, 2, 1, 64, 65)]:
+        assert fa.flexattn_decode_workspace_bytes(*bad) == 0
+    # about two workgroups per CU, at least 4 key tiles each, at most 64
+    assert fa.flexattn_decode_splits(16, 8, 32768) == 4
+    assert fa.flexattn_decode_splits(1, 1, 1 << 20) == 64
+    assert fa.flexattn_decode_splits(1, 8, 1024) == 2
+    assert fa.flexattn_decode_splits(64, 8, 8192) == 1
+
+
+def dcall(**over):
+    a = dict(GOOD, H=8, Hkv=2, Sq=1, Skv=512)
+    params = over.pop("params", None)
+    splits = over.pop("splits", 2)
+    ws = over.pop("ws", A)
+    wsb = over.pop("wsb", 1 << 20)
+    a.update(over)
+    return fa.flexattn_decode(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Hkv"],
+                              a["Sq"], a["Skv"], a["D"], a["scale"], a["mask_kind"], a["mod_kind"],
+                              params, None, splits, ws, wsb, stream=None, check=False)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.ERR_NULLPTR),
+    (dict(params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),     # bf16 only
+    (dict(Sq=65, H=8, Hkv=2), _lib.ERR_UNSUPPORTED),            # 4 x 65 packed rows > 256
+    (dict(splits=0), _lib.ERR_ARG),
+    (dict(splits=65), _lib.ERR_ARG),
+    (dict(ws=None), _lib.ERR_NULLPTR),                           # two splits need a workspace
+    (dict(ws=A + 4), _lib.ERR_ALIGN),
+    (dict(wsb=100), _lib.ERR_ARG),                               # too small
+    (dict(mod_kind=3, params=P(rel_bias=A, rel_max=300)), _lib.ERR_UNSUPPORTED),  # 4 tables of 601 > LDS
+    (dict(splits=1, ws=None, out=A + 2), _lib.ERR_ALIGN),        # one split needs none: reaches the checks after
+])
+def test_decode_validation(over, code):
+    assert dcall(**over) == code

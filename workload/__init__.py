@@ -44,6 +44,7 @@ class Workload:
     prefix: int | None = None   # prefix-LM boundary (with causal), or None
     sq: int = 0                 # > 0: query rows, when fewer than the keys
     rel_max: int = 0            # clip distance R of the relative-bias table (mod "relbias")
+    decode: bool = False        # run through the decode entry point (packed heads, split keys)
 
     @property
     def Sq(self) -> int:
@@ -94,6 +95,10 @@ WORKLOADS = {
     # +-1023) on the causal GQA shape
     "relbias": Workload("relbias", B=2, H=32, Hkv=8, S=8192, D=128, dtype="bf16", causal=True,
                         mod="relbias", rel_max=1023, seed=8),
+    # one decoding step: 16 sequences, each one new query row per head after
+    # 32767 cached keys (GQA 32 query / 8 key-value heads)
+    "decode": Workload("decode", B=16, H=32, Hkv=8, S=32768, sq=1, q_offset=32767, D=128,
+                       dtype="bf16", causal=True, decode=True, seed=9),
 }
 
 
