@@ -122,3 +122,34 @@ def test_backward_null_block_mask_is_bitwise_equal():
         (a, _), (b, _) = run_bwd(inp, "auto"), run_bwd(inp, None)
         for x, y in zip(a, b):
             assert torch.equal(x, y), var
+
+
+# ------------------------------------------------------------------ full size, as the bench runs it
+@pytest.mark.parametrize("name,b,kvh", [("dense", 3, 5), ("causal_gqa", 1, 6)])
+def test_backward_full_size_one_group(name, b, kvh):
+    """The bench's backward (whole workload, block mask, one launch of each
+    kernel), checked on one batch row and one key/value head: the oracle's
+    gradients of that slice (its query heads' dQ, the head's dK and dV) are
+    exact, since no other slice feeds them."""
+    from workload import WORKLOADS, make_inputs
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    say(f"[bwd] full-size {name}: gpu")
+    (dq, dk, dv), dout = run_bwd(inp, seed=wl.seed)
+    rep = wl.H // wl.Hkv
+    heads = list(range(kvh * rep, (kvh + 1) * rep))
+    q = bf16_values(inp.q[b:b + 1, heads])
+    k = bf16_values(inp.k[b:b + 1, kvh:kvh + 1])
+    v = bf16_values(inp.v[b:b + 1, kvh:kvh + 1])
+    g = bf16_values(dout[b:b + 1, heads].cpu())
+    say(f"[bwd] full-size {name}: oracle on batch {b}, kv head {kvh} ({rep} query heads)")
+    ref = oracle.attention_backward(q, k, v, g, wl.scale, causal=wl.causal)
+    got = (to_np(dq[b:b + 1, heads]), to_np(dk[b:b + 1, kvh:kvh + 1]), to_np(dv[b:b + 1, kvh:kvh + 1]))
+    for nm, gt, want in zip(("dq", "dk", "dv"), got, ref):
+        err = np.abs(gt - want)
+        rmax = err.max() / max(np.abs(want).max(), 1e-6)
+        rmean = err.mean() / max(np.abs(want).mean(), 1e-6)
+        say(f"[bwd]   {nm}: max {rmax:.2e} mean {rmean:.2e}")
+        assert rmax <= REL_MAX and rmean <= REL_MEAN, (name, nm, rmax, rmean)
+    for t in (dq, dk, dv):
+        assert not torch.isnan(t).any().item()

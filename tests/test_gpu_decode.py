@@ -84,3 +84,21 @@ def test_decode_agrees_with_forward():
     torch.cuda.synchronize()
     assert (O.float() - Of.float()).abs().max().item() < 1e-2
     assert (L - Lf).abs().max().item() < 1e-4
+
+
+def test_decode_workload_full_size_sampled():
+    """The bench's decode step (16 sequences x 32 heads, 32767 cached keys,
+    the library's split count), checked against the oracle on sampled
+    (batch, head) pairs; every output element written."""
+    from workload import WORKLOADS, make_inputs
+    import oracle
+    from workload import bf16_values
+    wl = WORKLOADS["decode"]
+    inp = make_inputs(wl)
+    O, L = run_decode(inp, None)
+    for b, heads in ((0, [0, 5, 31]), (9, [12, 13]), (15, [31])):
+        q, k, v = (bf16_values(t[b:b + 1]) for t in (inp.q, inp.k, inp.v))
+        Oref, Lref = oracle.attention(q, k, v, wl.scale, causal=True, q_offset=wl.q_offset, heads=heads)
+        compare(to_np(O[b:b + 1, heads]), to_np(L[b:b + 1, heads]), Oref[:, heads], Lref[:, heads],
+                f"decode full size b={b}")
+    assert not torch.isnan(O).any().item() and not torch.isnan(L).any().item()
