@@ -185,7 +185,7 @@ int check_attn_args(const flexattn_params* prm, int B, int H, int Hkv, int Sq, i
   if (H < 1 || Hkv < 1 || H % Hkv != 0) return FLEXATTN_ERR_SHAPE;
   int st = check_mask_args(mask_kind, prm, B, Sq, Skv);
   if (st) return st;
-  if (D != 64 && D != 128) return FLEXATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return FLEXATTN_ERR_UNSUPPORTED;
   if (prm->dtype != FLEXATTN_BF16 && prm->dtype != FLEXATTN_FP32) return FLEXATTN_ERR_UNSUPPORTED;
   if (mod_kind < FLEXATTN_MOD_NONE || mod_kind > FLEXATTN_MOD_RELBIAS) return FLEXATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FLEXATTN_ERR_ARG;
@@ -255,6 +255,9 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
   int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
   if (st) return st;
+  // D = 256 runs on the bf16 ping-pong kernel only
+  if (D == 256 && (prm->dtype != FLEXATTN_BF16 || ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles))
+    return FLEXATTN_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
 
@@ -299,7 +302,8 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
 }
 
 size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits) {
-  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || Sq < 1 || (D != 64 && D != 128) || splits < 1 || splits > 64)
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || Sq < 1 || (D != 64 && D != 128 && D != 256) || splits < 1 ||
+      splits > 64)
     return 0;
   if (splits == 1) return 0;
   const size_t rows = static_cast<size_t>(B) * H * Sq;   // = B * Hkv * (rep * Sq)
@@ -399,6 +403,7 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
   if (st) return st;
   if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
+  if (D == 256) return FLEXATTN_ERR_UNSUPPORTED;   // the backward kernels take D = 64 and 128
   if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
   if (!is_contiguous(strides_of(prm->q_stride, H, Sq, D), H, Sq, D) ||
       !is_contiguous(strides_of(prm->k_stride, Hkv, Skv, D), Hkv, Skv, D) ||

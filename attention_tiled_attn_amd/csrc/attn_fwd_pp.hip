@@ -49,7 +49,7 @@ using namespace dev;
 
 constexpr int kThreads = 512;   // 8 waves: two groups of 4
 constexpr int kBM = 2 * kPairHalf;   // query rows per workgroup
-constexpr int kBN = 64;         // keys per stage
+constexpr int kBNMax = 64;      // keys per stage (32 at D = 256)
 constexpr int kTile = 128;      // key tile of the block mask
 constexpr int kRing = 3;        // stage buffers for K and for V
 constexpr int kXcds = 8;
@@ -58,6 +58,11 @@ constexpr float kSumLimit = 256.0f;   // 2^kRescaleLog2
 
 template <int D>
 struct PGeo {
+  // keys per stage: 64, or 32 at D = 256 so that a K or V stage stays 16 KB
+  static constexpr int kBN = D == 256 ? 32 : 64;
+  static constexpr int kKB = kBN / 32;                 // 32-key blocks of S^T
+  static constexpr int kCH = kBN / 16;                 // 16-key chunks of P^T
+  static constexpr int kSPT = 128 / kBN;               // stages per 128-key tile
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBufBytes = kBN * D * 2;        // one K or V stage
   static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
@@ -70,9 +75,9 @@ struct PGeo {
 // different chunk positions. V: the 4 rows read together by one half-wave of
 // a transposing b64 read hit disjoint groups of 4 chunks.
 template <int D>
-__device__ inline int kswz(int r) { return (r / (128 / D)) % (D / 8); }
+__device__ inline int kswz(int r) { return D == 256 ? r % 16 : (r / (128 / D)) % (D / 8); }
 template <int D>
-__device__ inline int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+__device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // PACK (decode mode): a workgroup owns the rep = H / Hkv query heads of one
 // key/value head, packed as rows r = head_in_group * Sq + q_row (at most 256),
@@ -88,7 +93,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
   // document labels of each ring slot's 64 keys (copied with K by wave 0)
-  __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kRing * kBN : 4];
+  __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kRing * kBNMax : 4];
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
   const int tid = threadIdx.x;
@@ -175,33 +180,42 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     for (int j = 0; j < (PACK ? rep : 1); ++j)
       stage_rel_table(p.va, h0 + j, (lds_f32*)(rtab) + j * n_tab, tid, kThreads);
   }
-  int n_stages = 2 * n_entries;
+  constexpr int kBN = G::kBN, kSPT = G::kSPT;
+  int n_stages = kSPT * n_entries;
   if (n_entries > 0) {
+    // stages of the last tile that start at or past Skv are dropped
     const int last = list ? (list[e_first + n_entries - 1] >> 4) : (e_first + n_entries - 1);
-    if (last * kTile + kBN >= p.Skv) n_stages -= 1;   // last tile has a single 64-key stage
+    const int live = (p.Skv - last * kTile + kBN - 1) / kBN;
+    n_stages -= kSPT - min(live, kSPT);
   }
   __syncthreads();
-  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) >> 1]; };
-  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t & 1) * kBN; };
+  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) / kSPT]; };
+  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t % kSPT) * kBN; };
 
   // ---- per-lane LDS offsets
   // K fragment (S^T A operand): row l32 (+32 kb), chunk 2c + g
-  unsigned koff[DC];
+  // (at D = 256 the offsets are formed as needed: the chunk permutation is an
+  // XOR of low bits, so chunk c's offset is the chunk-0 offset XOR 32 c, and
+  // block db's V offset the block-0 offset XOR 64 db; this saves 23 registers)
+  constexpr bool kXorOff = D == 256;
+  unsigned koff[kXorOff ? 1 : DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) koff[c] = l32 * RB + (((2 * c + g) ^ kswz<D>(l32)) * 16);
+  for (int c = 0; c < (kXorOff ? 1 : DC); ++c) koff[c] = l32 * RB + (((2 * c + g) ^ kswz<D>(l32)) * 16);
+  auto koff_at = [&](int c) -> unsigned { return kXorOff ? koff[0] ^ (c << 5) : koff[c]; };
   // V^T fragment via transposing reads: 16-lane group G, lane sl reads 4 d
   // values of key row 16 ch + 8 j + 4 (G / 2) + sl / 4 starting at
   // d = 32 db + 16 (G % 2) + 4 (sl % 4)
-  unsigned voff[DB];
+  unsigned voff[kXorOff ? 1 : DB];
   {
     const int G16 = lane >> 4, sl = lane & 15;
     const int row0 = 4 * (G16 >> 1) + (sl >> 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < (kXorOff ? 1 : DB); ++db) {
       const int chunk = 4 * db + 2 * (G16 & 1) + ((sl & 3) >> 1);
       voff[db] = row0 * RB + ((chunk ^ vswz<D>(row0)) * 16) + (sl & 1) * 8;
     }
   }
+  auto voff_at = [&](int db) -> unsigned { return kXorOff ? voff[0] ^ (db << 6) : voff[db]; };
   // copies: this wave fills 1 KB runs wq * kDma + j of a stage buffer; lane i
   // writes slot i of the run, i.e. chunk position s % kCpr of row s / kCpr
   unsigned goff[G::kDma];
@@ -229,7 +243,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     for (int j = 0; j < G::kDma; ++j)
       copy_to_lds(desc, gbase + goff[j], __builtin_amdgcn_readfirstlane(lbase + j * 1024));
     if constexpr (DOCS) {
-      if (lab_wave && lane < 16)
+      if (lab_wave && lane < kBN / 4)
         copy_to_lds(ldesc, static_cast<unsigned>(kv0 + 4 * lane) * 4u,
                     __builtin_amdgcn_readfirstlane(lab_lds + ring * kBN * 4));
     }
@@ -255,23 +269,24 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   }();
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
-  bf16x8 pf[4];
+  constexpr int KB = G::kKB, CH = G::kCH;
+  bf16x8 pf[CH];
 
-  // S^T(t) = K(t) Q^T: two 32-key blocks, fragment reads 4 ahead of the MFMAs
-  auto qk = [&](int ring, f32x16 (&s)[2]) {
+  // S^T(t) = K(t) Q^T: KB 32-key blocks, fragment reads 4 ahead of the MFMAs
+  auto qk = [&](int ring, f32x16 (&s)[KB]) {
     const unsigned char* kb_ = kbuf + ring * G::kBufBytes;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff[c] + kb * 32 * RB);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff_at(c) + kb * 32 * RB);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * DC - 4; ++i) {
+    for (int i = 0; i < KB * DC - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
     }
@@ -286,8 +301,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        const unsigned char* a0 = vb + voff[db] + (16 * ch) * RB;
+      for (int ch = 0; ch < CH; ++ch) {
+        const unsigned char* a0 = vb + voff_at(db) + (16 * ch) * RB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * RB));
         const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -296,7 +311,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       }
     __builtin_amdgcn_sched_group_barrier(0x0100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * DB - 4; ++i) {
+    for (int i = 0; i < CH * DB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
     }
@@ -304,8 +319,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   };
 
   // online softmax of one stage: scores -> P^T (bf16) in pf, running max/sum
-  auto softmax = [&](const f32x16 (&s)[2], int kv0, bool full, int ring) {
-    float t[32];
+  auto softmax = [&](const f32x16 (&s)[KB], int kv0, bool full, int ring) {
+    float t[KB * 16];
     // Relative bias: when every distance of the stage, over the wave's 32
     // rows, lies beyond the clip distance, all scores take the same end entry
     // of the table (one wave-uniform LDS read instead of one per score).
@@ -324,10 +339,10 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     }
     if (clipped) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) t[i] = __builtin_fmaf(s[i >> 4][i & 15], p.va.c1, clip_add);
+      for (int i = 0; i < KB * 16; ++i) t[i] = __builtin_fmaf(s[i >> 4][i & 15], p.va.c1, clip_add);
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -353,7 +368,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
       const int* lab = labbuf + (DOCS ? ring * kBN + 4 * g : 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x4 l4 = {0u, 0u, 0u, 0u};
@@ -372,7 +387,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     auto exps = [&](float base) -> float {
       float acc = 0.f;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
+      for (int ch = 0; ch < CH; ++ch) {
         const int kb = ch >> 1, r0 = (ch & 1) * 8;
         unsigned w[4];
 #pragma unroll
@@ -421,7 +436,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     if (need_max) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, t[i]);
+      for (int i = 0; i < KB * 16; ++i) mx = fmaxf(mx, t[i]);
       mx = max_pair32(mx);
       if constexpr (SM::kFoldScale) mx *= p.va.c1;
       if (__any(mx > m_run + grow)) {
@@ -458,7 +473,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // matrix slot. S^T is computed even for a stage this half skips (a
     // conditional product would make the scores a loop phi, which the compiler
     // resolves by copying all 32 of them every stage).
-    f32x16 s[2];
+    f32x16 s[KB];
     __builtin_amdgcn_s_setprio(1);   // the multiplying wave goes first on its SIMD
     qk(ring, s);
     if (do_pv) pv(ring_old);
@@ -559,6 +574,7 @@ hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
 template <bool PACK>
 hipError_t launch_dims(const FwdLaunch& p, hipStream_t stream) {
   const bool docs = p.mask_kind & kMaskDocument;
+  if (p.D == 256) return docs ? launch_mod<256, true, PACK>(p, stream) : launch_mod<256, false, PACK>(p, stream);
   if (p.D == 128) return docs ? launch_mod<128, true, PACK>(p, stream) : launch_mod<128, false, PACK>(p, stream);
   if (p.D == 64) return docs ? launch_mod<64, true, PACK>(p, stream) : launch_mod<64, false, PACK>(p, stream);
   return hipErrorInvalidValue;

@@ -198,7 +198,8 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
  *   k, v  : device [B][Hkv][Skv][D] same dtype
  *   out   : device [B][H][Sq][D]    same dtype; every element is written
  *   lse   : device float32 [B][H][Sq], or NULL to skip it; every element is written
- *   D     : 64 or 128; scale: finite and > 0 (1/sqrt(D) is the usual choice)
+ *   D     : 64, 128 or 256 (256: bf16, Skv <= 2048 * FLEXATTN_TILE); scale:
+ *           finite and > 0 (1/sqrt(D) is the usual choice)
  *   mask_kind, mod_kind, params: the variant (see above)
  *   block_mask: from flexattn_build_block_mask for the same mask_kind, sizes
  *           and params, or NULL to visit every key tile with the per-element
@@ -242,7 +243,8 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
  * (Neuron FA4 explainer, "FlashAttention-4: Built for Blackwell", backward-pass
  * fixes); the gradients follow from the definition above by differentiation.
  *   q, k, v    : as for flexattn_fwd; bf16 only (params->dtype = FLEXATTN_BF16),
- *                Skv <= 2048 * FLEXATTN_TILE (else FLEXATTN_ERR_UNSUPPORTED)
+ *                D = 64 or 128, Skv <= 2048 * FLEXATTN_TILE, contiguous layout
+ *                (else FLEXATTN_ERR_UNSUPPORTED)
  *   out, lse   : the forward's O [B][H][Sq][D] bf16 and LSE [B][H][Sq] float32
  *   dout       : device [B][H][Sq][D] bf16, the gradient arriving at O
  *   dq         : device [B][H][Sq][D] bf16; every element is written

@@ -105,7 +105,10 @@ def P(**kw):
     (dict(Sq=0), _lib.ERR_SHAPE),
     (dict(Skv=-5), _lib.ERR_SHAPE),
     (dict(D=96), _lib.ERR_UNSUPPORTED),
-    (dict(D=256), _lib.ERR_UNSUPPORTED),
+    (dict(D=512), _lib.ERR_UNSUPPORTED),
+    (dict(D=256, params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),   # D = 256 is bf16 only
+    (dict(D=256, Skv=2048 * 128 + 1), _lib.ERR_UNSUPPORTED),
+    (dict(D=256, out=A + 2), _lib.ERR_ALIGN),                          # bf16 D = 256 is accepted
     (dict(mask_kind=16), _lib.ERR_UNSUPPORTED),
     (dict(mask_kind=8), _lib.ERR_ARG),                                   # prefix without causal
     (dict(mask_kind=10, params=P(window=4)), _lib.ERR_ARG),
@@ -264,6 +267,7 @@ def bcall(**over):
       for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "delta")],
     (dict(H=3, Hkv=2), _lib.ERR_SHAPE),
     (dict(D=96), _lib.ERR_UNSUPPORTED),
+    (dict(D=256), _lib.ERR_UNSUPPORTED),                          # forward only
     (dict(params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),     # bf16 only
     (dict(Skv=2048 * 128 + 1), _lib.ERR_UNSUPPORTED),           # key-tile list limit
     (dict(scale=0.0), _lib.ERR_ARG),

@@ -226,7 +226,7 @@ def test_block_mask_document_workload_full_size():
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 @pytest.mark.parametrize("name", ["dense", "causal_gqa", "causal_gqa_shard8", "doc_swa", "alibi_d64",
                                   "alibi_d128", "softcap_d64", "softcap_d128", "prefix_lm",
-                                  "chunked_prefill", "relbias"])
+                                  "chunked_prefill", "relbias", "causal_gqa_d256"])
 def test_full_size_sampled(name):
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
@@ -287,3 +287,35 @@ def test_strided_kv_shared_across_batch():
                                     scale=inp.wl.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+# ------------------------------------------------------------------ head dimension 256
+D256_CASES = [
+    dict(S=1), dict(S=33), dict(S=200), dict(S=333, causal=True),
+    dict(S=513, H=4, Hkv=2, causal=True, window=100), dict(S=300, documents=True, causal=True),
+    dict(S=260, mod="alibi", causal=True), dict(S=260, mod="softcap", softcap=5.0),
+    dict(S=260, mod="relbias", rel_max=50, causal=True), dict(S=290, documents=True, mod="alibi"),
+    dict(Sq=70, Skv=400, q_offset=330, causal=True), dict(S=300, causal=True, prefix=100),
+]
+
+
+@pytest.mark.parametrize("case", D256_CASES, ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+def test_head_dim_256(case):
+    inp = small(D=256, doc_range=(30, 150), **case)
+    check_full(inp, what=f"D=256 {case}")
+    O1, L1 = run_gpu(inp)
+    O2, L2 = run_gpu(inp, block_mask=None)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_head_dim_256_strided_and_decode():
+    inp = small(B=2, H=8, Hkv=2, Sq=3, Skv=700, q_offset=697, D=256, causal=True)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    O1, L1 = run_gpu(inp, qkv=(q, k, v))
+    qs, ks, vs = (_bshd(t) for t in (q, k, v))
+    O2, L2 = fa.attention(qs, ks, vs, device_variant(inp), scale=inp.wl.scale)
+    O3, L3 = fa.decode(q, k, v, device_variant(inp), scale=inp.wl.scale, splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    Oref, Lref = run_oracle(inp)
+    compare(to_np(O3), to_np(L3), Oref, Lref, "D=256 decode")

@@ -95,6 +95,9 @@ WORKLOADS = {
     # +-1023) on the causal GQA shape
     "relbias": Workload("relbias", B=2, H=32, Hkv=8, S=8192, D=128, dtype="bf16", causal=True,
                         mod="relbias", rel_max=1023, seed=8),
+    # head dimension 256 on the causal GQA shape
+    "causal_gqa_d256": Workload("causal_gqa_d256", B=2, H=16, Hkv=8, S=8192, D=256, dtype="bf16",
+                                causal=True, seed=10),
     # one decoding step: 16 sequences, each one new query row per head after
     # 32767 cached keys (GQA 32 query / 8 key-value heads)
     "decode": Workload("decode", B=16, H=32, Hkv=8, S=32768, sq=1, q_offset=32767, D=128,
