@@ -123,6 +123,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int h = PACK ? kvh * rep + hl : (lin / np) % p.H;   // lane-varying in decode mode
   const int q_row = PACK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
   const bool q_ok = PACK ? r_lane < rep * p.Sq : q_row < p.Sq;
+  // decode mode: a wave whose 32 rows all lie past the packed rows only
+  // copies and keeps the barriers (wave-uniform, fixed for the whole loop)
+  const bool live = !PACK || __builtin_amdgcn_readfirstlane(r_lane - l32) < rep * p.Sq;
   const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE rows
   // row strides in bytes; a (batch, head) slice spans rows 0 .. S - 1, so
   // rows past the end read as zero (decode mode: the slices of the group's
@@ -467,15 +470,15 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     const int ring_old = ring == 0 ? kRing - 1 : ring - 1;
     const int ec = __builtin_amdgcn_readfirstlane(e_cur) >> sh;
     const int ep = __builtin_amdgcn_readfirstlane(e_prev) >> sh;
-    const bool do_s = ec & 1;              // this half has admitted pairs in stage u
-    const bool do_pv = u >= 1 && (ep & 1);
+    const bool do_s = live && (ec & 1);    // this half has admitted pairs in stage u
+    const bool do_pv = live && u >= 1 && (ep & 1);
 
     // matrix slot. S^T is computed even for a stage this half skips (a
     // conditional product would make the scores a loop phi, which the compiler
     // resolves by copying all 32 of them every stage).
     f32x16 s[KB];
     __builtin_amdgcn_s_setprio(1);   // the multiplying wave goes first on its SIMD
-    qk(ring, s);
+    if (live) qk(ring, s);
     if (do_pv) pv(ring_old);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -504,7 +507,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   {
     const int ep = __builtin_amdgcn_readfirstlane(e_prev) >> sh;
     __builtin_amdgcn_s_setprio(1);
-    if (T >= 1 && (ep & 1)) pv(ring == 0 ? kRing - 1 : ring - 1);
+    if (live && T >= 1 && (ep & 1)) pv(ring == 0 ? kRing - 1 : ring - 1);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
