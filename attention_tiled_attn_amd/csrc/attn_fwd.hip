@@ -382,7 +382,7 @@ void attn_fwd_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* _
     if constexpr (SM::kFoldScale) mx *= p.va.c1;   // raw -> log2 units (c1 > 0)
 
     // conditional rescale (wave-uniform decision)
-    if (__any(mx > m_run + kRescaleLog2)) {
+    if (__any(q_ok && mx > m_run + kRescaleLog2)) {   // rows past Sq take no part
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;

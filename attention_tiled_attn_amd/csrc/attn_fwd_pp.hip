@@ -53,6 +53,7 @@ constexpr int kBNMax = 64;      // keys per stage (32 at D = 256)
 constexpr int kTile = 128;      // key tile of the block mask
 constexpr int kRing = 3;        // stage buffers for K and for V
 constexpr int kXcds = 8;
+constexpr int kLptMaxTiles = 256;   // longest-first order up to this many query tiles
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 256.0f;   // 2^kRescaleLog2
 
@@ -113,14 +114,59 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int wg = blockIdx.x;
   const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
   if (lin >= total) return;
-  const int qp = PACK ? 0 : np - 1 - (lin % np);
+  int qp = PACK ? 0 : np - 1 - (lin % np);
   const int split = PACK ? lin % p.splits : 0;
-  const int b = PACK ? lin / p.splits / p.Hkv : lin / np / p.H;
-  const int kvh = PACK ? (lin / p.splits) % p.Hkv : ((lin / np) % p.H) / rep;
+  int slice = lin / np;   // (b, h) of the regular kernel
+  // length and first entry of the item's key-tile list when the mapping
+  // below has fetched them (n_head < 0: not fetched)
+  int n_head = -1, e_head = 0;
+  if constexpr (DOCS && !PACK) {
+    // Document masks make the work of a slice's query tiles uneven. When the
+    // slices split evenly over the XCDs, each XCD takes its slices' items
+    // longest first (most key tiles; ties: the later tile), rank-major over
+    // its slices, so the 32 CUs of an XCD finish together. Every item is
+    // computed the same way whichever workgroup takes it. The first entry of
+    // every tile's list is fetched with the counts, so the chosen item's
+    // first copies need no further round trip.
+    const int spx = p.B * p.H / kXcds;
+    if (kv_count && p.nq <= kLptMaxTiles && spx * kXcds == p.B * p.H) {
+      __shared__ int sel[3];
+      const int j = wg / kXcds;
+      const int rank = j / spx;
+      slice = (wg % kXcds) * spx + j % spx;
+      const int row0 = (p.bm_num_b > 1 ? slice / p.H : 0) * p.nq;
+      int* const keys = ents;                  // staged before the key-tile list
+      int* const heads = ents + kLptMaxTiles;
+      if (tid < p.nq) {
+        const int c = kv_count[row0 + tid];
+        heads[tid] = kv_list[static_cast<size_t>(row0 + tid) * p.nk];   // slot 0 exists (nk >= 1)
+        keys[tid] = c * 65536 + tid;
+      }
+      if (tid == 0) sel[0] = sel[1] = sel[2] = 0;
+      __syncthreads();
+      if (tid < p.nq) {
+        const int mine = keys[tid];
+        int above = 0;
+        for (int i = 0; i < p.nq; ++i) above += keys[i] > mine;
+        if (above == rank) {
+          sel[0] = tid;
+          sel[1] = mine >> 16;
+          sel[2] = heads[tid];
+        }
+      }
+      __syncthreads();
+      qp = min(max(__builtin_amdgcn_readfirstlane(sel[0]), 0), np - 1);
+      n_head = min(max(__builtin_amdgcn_readfirstlane(sel[1]), 0), p.nk);
+      e_head = __builtin_amdgcn_readfirstlane(sel[2]);
+      __syncthreads();   // the keys are read before the list overwrites them
+    }
+  }
+  const int b = PACK ? lin / p.splits / p.Hkv : slice / p.H;
+  const int kvh = PACK ? (lin / p.splits) % p.Hkv : (slice % p.H) / rep;
   // this lane's row: packed index r (decode mode), its query head and row
   const int r_lane = grp * kPairHalf + wq * 32 + l32;
   const int hl = PACK ? min(r_lane / p.Sq, rep - 1) : 0;
-  const int h = PACK ? kvh * rep + hl : (lin / np) % p.H;   // lane-varying in decode mode
+  const int h = PACK ? kvh * rep + hl : slice % p.H;   // lane-varying in decode mode
   const int q_row = PACK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
   const bool q_ok = PACK ? r_lane < rep * p.Sq : q_row < p.Sq;
   // decode mode: a wave whose 32 rows all lie past the packed rows only
@@ -141,6 +187,28 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const unsigned kv_bytes = static_cast<unsigned>(p.Skv - 1) * grb + RB;
   const u32x4 desc = grp ? make_desc(vbase, kv_bytes) : make_desc(kbase, kv_bytes);
 
+  // ---- key-tile list of this 256-row tile. Entry:
+  // (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0 (half 0 = rows
+  // 0-127 of the tile, half 1 = rows 128-255). No block mask: every tile,
+  // both halves partial. Its length and first entry are read first (beside
+  // the Q loads), so that the first two stages' copies start one memory
+  // round trip after entry; the row holds nk slots, so its first kThreads
+  // entries are read at the same time.
+  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
+  int n_entries = p.nk;
+  int e_spec = 0;
+  if (PACK || n_head < 0) {
+    if (kv_count) n_entries = kv_count[bm_b * p.nq + qp];
+    if (!PACK && list) {
+      e_head = list[0];
+      if (tid < p.nk) e_spec = list[tid];
+    }
+  } else {
+    n_entries = n_head;
+  }
+  if (!list) e_head = 0x5;
+
   // Q^T fragments (B operand of S^T): rows past Sq (and, in decode mode,
   // packed rows past the group) read as zero
   const unsigned q_off = !q_ok ? 0x80000000u
@@ -152,47 +220,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
         rq, q_off + (c * 16 + g * 8) * 2, 0, 0));
 
-  // ---- key-tile list of this 256-row tile, into LDS. Entry:
-  // (kv_tile << 4) | full1 << 3 | any1 << 2 | full0 << 1 | any0 (half 0 = rows
-  // 0-127 of the tile, half 1 = rows 128-255). No block mask: every tile,
-  // both halves partial.
-  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
-  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
-  int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
-  int e_first = 0;
-  if constexpr (PACK) {
-    // this split's part of the list; every packed row lies in query tile 0,
-    // so a tile is visited when either half admits a pair, and skips the
-    // per-element mask only when both halves are full (half 1 has no rows
-    // when Sq <= 128)
-    const int n_all = n_entries;
-    e_first = static_cast<int>(static_cast<long long>(n_all) * split / p.splits);
-    n_entries = static_cast<int>(static_cast<long long>(n_all) * (split + 1) / p.splits) - e_first;
-    for (int i = tid; i < n_entries; i += kThreads) {
-      const int e = list ? list[e_first + i] : (((e_first + i) << 4) | 0x5);
-      const bool full = (e & 2) && ((e & 8) || p.Sq <= kPairHalf);
-      ents[i] = (e & ~15) | ((e & 5) ? (full ? 0xF : 0x5) : 0);
-    }
-  } else {
-    for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : ((i << 4) | 0x5);
-  }
-  if constexpr (MOD == kModRelBias) {
-    // decode mode: the tables of all rep heads of the group, one after another
-    const int n_tab = 2 * p.va.rel_max + 1;
-    const int h0 = PACK ? kvh * rep : __builtin_amdgcn_readfirstlane(h);
-    for (int j = 0; j < (PACK ? rep : 1); ++j)
-      stage_rel_table(p.va, h0 + j, (lds_f32*)(rtab) + j * n_tab, tid, kThreads);
-  }
   constexpr int kBN = G::kBN, kSPT = G::kSPT;
-  int n_stages = kSPT * n_entries;
-  if (n_entries > 0) {
-    // stages of the last tile that start at or past Skv are dropped
-    const int last = list ? (list[e_first + n_entries - 1] >> 4) : (e_first + n_entries - 1);
-    const int live = (p.Skv - last * kTile + kBN - 1) / kBN;
-    n_stages -= kSPT - min(live, kSPT);
-  }
-  __syncthreads();
-  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) / kSPT]; };
   auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t % kSPT) * kBN; };
 
   // ---- per-lane LDS offsets
@@ -256,6 +284,55 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     if (lab_wave) wait_vm<G::kDma + 1>();
     else wait_vm<G::kDma>();
   };
+
+  // non-decode items: the first two stages (both in the first key tile)
+  // are copied as soon as the list head is known; a second stage past Skv
+  // reads zeros and is never used
+  if (!PACK && n_entries > 0) {
+    issue_copy(0, e_head, 0);
+    issue_copy(1, e_head, 1);
+  }
+
+  int e_first = 0;
+  if constexpr (PACK) {
+    // this split's part of the list; every packed row lies in query tile 0,
+    // so a tile is visited when either half admits a pair, and skips the
+    // per-element mask only when both halves are full (half 1 has no rows
+    // when Sq <= 128)
+    const int n_all = n_entries;
+    e_first = static_cast<int>(static_cast<long long>(n_all) * split / p.splits);
+    n_entries = static_cast<int>(static_cast<long long>(n_all) * (split + 1) / p.splits) - e_first;
+    for (int i = tid; i < n_entries; i += kThreads) {
+      const int e = list ? list[e_first + i] : (((e_first + i) << 4) | 0x5);
+      const bool full = (e & 2) && ((e & 8) || p.Sq <= kPairHalf);
+      ents[i] = (e & ~15) | ((e & 5) ? (full ? 0xF : 0x5) : 0);
+    }
+  } else if (list) {
+    int i = tid;
+    if (n_head < 0) {   // the first kThreads entries are already in flight
+      if (tid < n_entries) ents[tid] = e_spec;
+      i += kThreads;
+    }
+    for (; i < n_entries; i += kThreads) ents[i] = list[i];
+  } else {
+    for (int i = tid; i < n_entries; i += kThreads) ents[i] = (i << 4) | 0x5;
+  }
+  if constexpr (MOD == kModRelBias) {
+    // decode mode: the tables of all rep heads of the group, one after another
+    const int n_tab = 2 * p.va.rel_max + 1;
+    const int h0 = PACK ? kvh * rep : __builtin_amdgcn_readfirstlane(h);
+    for (int j = 0; j < (PACK ? rep : 1); ++j)
+      stage_rel_table(p.va, h0 + j, (lds_f32*)(rtab) + j * n_tab, tid, kThreads);
+  }
+  __syncthreads();
+  int n_stages = kSPT * n_entries;
+  if (n_entries > 0) {
+    // stages of the last tile that start at or past Skv are dropped
+    const int last = ents[n_entries - 1] >> 4;
+    const int kept = (p.Skv - last * kTile + kBN - 1) / kBN;
+    n_stages -= kSPT - min(kept, kSPT);
+  }
+  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) / kSPT]; };
 
   // ---- running state
   f32x16 o[DB];
@@ -367,8 +444,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       long long hi = static_cast<long long>(p.Skv) - 1 - kk0;
       if (causal) hi = min(hi, max(d, static_cast<long long>(p.va.prefix) - 1 - kk0));
       const long long lo = window ? d - p.va.window + 1 : 0LL;
-      const int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBN)));
-      const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
+      int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBN)));
+      int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
+      asm("" : "+v"(hi_c), "+v"(lo_c));   // compare the clamped 32-bit bounds
       const int* lab = labbuf + (DOCS ? ring * kBN + 4 * g : 0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -379,8 +457,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int c = kb * 32 + 8 * i + e;
-            bool ok = (c >= lo_c) & (c <= hi_c);
-            if constexpr (DOCS) ok &= static_cast<int>(l4[e]) == doc_q;
+            uint64_t ok = __builtin_amdgcn_ballot_w64(c >= lo_c) & __builtin_amdgcn_ballot_w64(c <= hi_c);
+            if constexpr (DOCS) ok &= __builtin_amdgcn_ballot_w64(static_cast<int>(l4[e]) == doc_q);
             mask_in_place(t[kb * 16 + 4 * i + e], ok, ninf);
           }
         }
@@ -427,12 +505,16 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // stage. Those take the max first.
     // After a failed check the base moves to the row max whenever it grew at
     // all, so that the following stages pass the check again.
+    // Only rows that exist take part in these wave-wide decisions: a padding
+    // row past Sq sees every key of a full tile but only the keys its mask
+    // admits in a partial one, and must not make the real rows of its wave
+    // rescale in one case and not in the other.
     bool need_max = true;
     float grow = kRescaleLog2;
     if constexpr (MOD == kModSoftcap) {
-      if (!__any(m_run == -INFINITY)) {
-        ls = exps(m_run);
-        need_max = __any(!(ls <= kSumLimit));
+      if (!__any(q_ok && m_run == -INFINITY)) {
+        ls = exps(m_run == -INFINITY ? 0.f : m_run);   // padding rows may have no base yet
+        need_max = __any(q_ok && !(ls <= kSumLimit));
         grow = 0.f;
       }
     }
@@ -442,7 +524,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       for (int i = 0; i < KB * 16; ++i) mx = fmaxf(mx, t[i]);
       mx = max_pair32(mx);
       if constexpr (SM::kFoldScale) mx *= p.va.c1;
-      if (__any(mx > m_run + grow)) {
+      if (__any(q_ok && mx > m_run + grow)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
@@ -457,8 +539,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
   // ---- prologue: stages 0 and 1 (group 0 copies K, group 1 copies V)
   const int T = n_stages;
-  if (T > 0) issue_copy(0, ent(0), 0);
-  if (T > 1) issue_copy(1, ent(1), 1);
+  if (PACK && T > 0) issue_copy(0, ent(0), 0);
+  if (PACK && T > 1) issue_copy(1, ent(1), 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one slot behind
@@ -535,6 +617,42 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         }
       if (g == 0) p.ws_lse[wrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
+  } else if constexpr (!PACK) {
+    // O through LDS: each wave writes its 32 rows row-major into the idle
+    // stage buffers (16-byte chunks XOR-permuted by row, so neither side has
+    // bank conflicts) and stores whole rows, 16 bytes per lane. A store then
+    // covers 64 / CPP complete rows, where a direct store from the O^T
+    // fragments would put 16 bytes into each of 32 rows.
+    constexpr int DP = D < 128 ? D : 128;   // d values staged per pass
+    constexpr int CPP = DP / 8;             // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPP;           // rows per store instruction
+    static_assert(4 * 32 * DP * 2 <= kRing * G::kBufBytes, "output staging fits a stage ring");
+    unsigned char* const stg = (grp ? vbuf : kbuf) + wq * 32 * DP * 2;
+    __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
+    const int row0 = q_row - l32;   // first query row of the wave
+#pragma unroll
+    for (int ps = 0; ps < D / DP; ++ps) {
+#pragma unroll
+      for (int db = ps * DP / 32; db < (ps + 1) * DP / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = (db * 32 - ps * DP) / 8 + i;   // chunk of d = 32 db + 8 i + 4 g
+          const u32x2 vv = {pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
+                            pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv)};
+          *reinterpret_cast<u32x2*>(stg + l32 * DP * 2 + ((c ^ (l32 % CPP)) * 16) + g * 8) = vv;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 32 / RPI; ++j) {
+        const int r = j * RPI + lane / CPP, c = lane % CPP;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + r * DP * 2 + ((c ^ (r % CPP)) * 16));
+        if (row0 + r < p.Sq)
+          *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(row0 + r) * p.o_sr + ps * DP + c * 8) = w;
+      }
+      if (ps + 1 < D / DP) __syncthreads();   // read back before the next pass overwrites
+    }
+    if (p.lse && g == 0 && q_ok)
+      p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
   } else if (q_ok) {
     __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
     const size_t orow = static_cast<size_t>(q_row) * p.o_sr;

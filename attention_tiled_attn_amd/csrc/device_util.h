@@ -70,12 +70,13 @@ __device__ inline void copy_to_lds(u32x4 desc, unsigned voff, unsigned lds_base)
 }
 #pragma clang diagnostic pop
 
-// x = ok ? x : -inf, in x's own register. A plain select would let the
-// masked scores of partial tiles live in other registers than the unmasked
-// scores of full tiles, and the compiler then copies all 32 scores on every
-// stage to merge the two paths.
-__device__ inline void mask_in_place(float& x, bool ok, float ninf) {
-  asm("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(__builtin_amdgcn_ballot_w64(ok)));
+// x = (this lane's bit of m) ? x : -inf, in x's own register. A plain select
+// would let the masked scores of partial tiles live in other registers than
+// the unmasked scores of full tiles, and the compiler then copies all 32
+// scores on every stage to merge the two paths. The caller forms m as a
+// ballot of each compare (one v_cmp each, ANDed on the scalar unit).
+__device__ inline void mask_in_place(float& x, uint64_t m, float ninf) {
+  asm("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(m));
 }
 
 __device__ inline unsigned lds_addr(const void* p) {

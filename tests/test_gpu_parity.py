@@ -77,11 +77,39 @@ def test_relative_bias_fp32_path(D, R):
 
 
 def test_null_block_mask_is_bitwise_equal():
-    for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict()):
-        inp = small(S=520, D=128, **var)
+    # the last two have padding rows past Sq in waves with real rows, beside
+    # full tiles: the padding rows must not sway the rescale of the real ones
+    for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict(),
+                dict(S=1800, documents=True, causal=True, window=300, doc_range=(60, 700)),
+                dict(S=1000, documents=True, mod="softcap", softcap=5.0, doc_range=(60, 700))):
+        var = {"S": 520, **var}
+        inp = small(D=128, **var)
         O1, L1 = run_gpu(inp, block_mask="auto")
         O2, L2 = run_gpu(inp, block_mask=None)
         assert torch.equal(O1, O2) and torch.equal(L1, L2), var
+
+
+LONGEST_FIRST_CASES = [
+    # document masks with B*H a multiple of 8 take their query tiles longest
+    # first within each XCD; uneven documents give the tiles uneven work
+    dict(B=1, H=8, S=1800, D=128, causal=True, window=300),
+    dict(B=2, H=4, Hkv=2, S=1100, D=64),
+    dict(B=4, H=4, S=600, D=128, causal=True),
+    dict(B=1, H=8, S=900, D=256, causal=True, mod="alibi"),
+]
+
+
+@pytest.mark.parametrize("case", LONGEST_FIRST_CASES,
+                         ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+def test_document_items_longest_first(case):
+    """Every query tile is computed exactly once under the reordered mapping
+    (outputs start as NaN), matches the oracle, and is bitwise equal to the
+    unordered mapping that runs without a block mask."""
+    inp = small(documents=True, doc_range=(60, 700), **case)
+    check_full(inp, what=f"longest-first {case}")
+    O1, L1 = run_gpu(inp, block_mask="auto")
+    O2, L2 = run_gpu(inp, block_mask=None)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
 def test_repeat_runs_are_bitwise_equal():
