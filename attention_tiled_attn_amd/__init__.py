@@ -205,25 +205,37 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                        dv: torch.Tensor | None = None, delta: torch.Tensor | None = None,
                        stream=None):
     """(dQ, dK, dV) for the loss sum(out * dout), with out and lse from
-    attention() on the same inputs and variant (bf16 tensors). `delta` is the
-    [B, H, Sq] float32 scratch the call needs (allocated here if not given)."""
+    attention() on the same inputs and variant (bf16 tensors). The tensors may
+    be strided views (last dimension contiguous), e.g. [B, S, H, D] buffers
+    transposed; each gradient has the layout of its input (dq of q, dk of k,
+    dv of v, dout of out), and gradients allocated here follow that rule.
+    `delta` is the [B, H, Sq] float32 scratch the call needs (allocated here
+    if not given)."""
     var = var or Variant()
     B, H, Sq, D = q.shape
     _, Hkv, Skv, _ = k.shape
     for t in (q, k, v, out, dout):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
-            raise TypeError("q, k, v, out, dout must be contiguous bf16 device tensors")
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise TypeError("q, k, v, out, dout must be bf16 device tensors")
     if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+
+    def like(t):
+        return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+
+    dq = like(q) if dq is None else dq
+    dk = like(k) if dk is None else dk
+    dv = like(v) if dv is None else dv
+    for name, grad, ref in (("dout", dout, out), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if grad.shape != ref.shape or grad.stride() != ref.stride() or grad.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16 with the shape and strides of the tensor it belongs to")
     if delta is None:
         delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if isinstance(block_mask, str):
         block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
+    p = make_params(var, q.dtype)
+    set_layout(p, q, k, v, out)
     flexattn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, B, H, Hkv, Sq, Skv, D, scale,
-                 var.mask_kind, var.mod_kind, make_params(var, q.dtype),
-                 block_mask.struct if block_mask is not None else None, stream)
+                 var.mask_kind, var.mod_kind, p, block_mask.struct if block_mask is not None else None, stream)
     return dq, dk, dv

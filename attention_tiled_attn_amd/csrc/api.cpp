@@ -39,9 +39,6 @@ Strides strides_of(const long long (&s)[3], int heads, int rows, int D) {
     return {static_cast<long long>(heads) * rows * D, static_cast<long long>(rows) * D, D};
   return {s[0], s[1], s[2]};
 }
-bool is_contiguous(const Strides& s, int heads, int rows, int D) {
-  return s.b == static_cast<long long>(heads) * rows * D && s.h == static_cast<long long>(rows) * D && s.r == D;
-}
 // Checks of one tensor's layout: element strides, 16-byte alignment of every
 // row, and 32-bit byte offsets within one (batch, head) slice including one
 // query tile of rows past the end, which the kernels read as zeros.
@@ -405,11 +402,15 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
   if (D == 256) return FLEXATTN_ERR_UNSUPPORTED;   // the backward kernels take D = 64 and 128
   if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
-  if (!is_contiguous(strides_of(prm->q_stride, H, Sq, D), H, Sq, D) ||
-      !is_contiguous(strides_of(prm->k_stride, Hkv, Skv, D), Hkv, Skv, D) ||
-      !is_contiguous(strides_of(prm->v_stride, Hkv, Skv, D), Hkv, Skv, D) ||
-      !is_contiguous(strides_of(prm->o_stride, H, Sq, D), H, Sq, D))
-    return FLEXATTN_ERR_UNSUPPORTED;
+  const Strides qs = strides_of(prm->q_stride, H, Sq, D), ks = strides_of(prm->k_stride, Hkv, Skv, D);
+  const Strides vs = strides_of(prm->v_stride, Hkv, Skv, D), os = strides_of(prm->o_stride, H, Sq, D);
+  {
+    int ls = check_layout(qs, Sq, D, 2);
+    if (!ls) ls = check_layout(ks, Skv, D, 2);
+    if (!ls) ls = check_layout(vs, Skv, D, 2);
+    if (!ls) ls = check_layout(os, Sq, D, 2);
+    if (ls) return ls;
+  }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return FLEXATTN_ERR_ALIGN;
@@ -441,6 +442,10 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   p.nq = ceil_div(Sq, FLEXATTN_QTILE);
   p.nk = ceil_div(Skv, FLEXATTN_TILE);
   p.bm_num_b = block_mask ? block_mask->num_b : 1;
+  p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
+  p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);
+  p.v_sb = vs.b; p.v_sh = vs.h; p.v_sr = static_cast<int>(vs.r);
+  p.o_sb = os.b; p.o_sh = os.h; p.o_sr = static_cast<int>(os.r);
   hipError_t e = fa::launch_attn_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return FLEXATTN_OK;

@@ -71,16 +71,17 @@ __device__ inline unsigned row_off(int r, int chunk) {
 }
 
 // Copy 64 rows of D bf16 starting at byte `gbase` of the slice behind `desc`
-// into a stage buffer: this wave fills 1 KB runs wq * kDma + j; lane i writes
-// slot i, i.e. row s / kCpr at chunk position s % kCpr.
+// (rows `grb` bytes apart) into a stage buffer: this wave fills 1 KB runs
+// wq * kDma + j; lane i writes slot i, i.e. row s / kCpr at chunk position
+// s % kCpr.
 template <int D>
-__device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned lds_base, int wq, int lane) {
+__device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned grb, unsigned lds_base, int wq, int lane) {
   using G = BGeo<D>;
 #pragma unroll
   for (int j = 0; j < G::kDma; ++j) {
     const int s = (wq * G::kDma + j) * 64 + lane;
     const int r = s / G::kCpr, pos = s % G::kCpr;
-    const unsigned goff = static_cast<unsigned>(r * G::kRowBytes + ((pos ^ swz<D>(r)) * 16));
+    const unsigned goff = static_cast<unsigned>(r) * grb + static_cast<unsigned>((pos ^ swz<D>(r)) * 16);
     copy_to_lds(desc, gbase + goff,
                 __builtin_amdgcn_readfirstlane(lds_base + (wq * G::kDma + j) * 1024));
   }
@@ -158,15 +159,21 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int bh = lin / nq;
   const int h = bh % p.H, b = bh / p.H;
   const int kvh = h / (p.H / p.Hkv);
-  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;
-  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
-  const unsigned qbytes = static_cast<unsigned>(p.Sq) * RB;
-  const rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + q_head * D, qbytes);
-  const rsrc_t ro = make_rsrc(static_cast<const __bf16*>(p.out) + q_head * D, qbytes);
-  const rsrc_t rdo = make_rsrc(static_cast<const __bf16*>(p.dout) + q_head * D, qbytes);
-  const unsigned kvbytes = static_cast<unsigned>(p.Skv) * RB;
-  const u32x4 kdesc = make_desc(static_cast<const __bf16*>(p.k) + kv_head * D, kvbytes);
-  const u32x4 vdesc = make_desc(static_cast<const __bf16*>(p.v) + kv_head * D, kvbytes);
+  const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE and delta rows
+  // row strides in bytes; each slice's resource ends after its last row, so
+  // rows past the end read as zero
+  const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u, orb = static_cast<unsigned>(p.o_sr) * 2u;
+  const unsigned krb = static_cast<unsigned>(p.k_sr) * 2u, vrb = static_cast<unsigned>(p.v_sr) * 2u;
+  const rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh,
+                              static_cast<unsigned>(p.Sq - 1) * qrb + RB);
+  const rsrc_t ro = make_rsrc(static_cast<const __bf16*>(p.out) + b * p.o_sb + h * p.o_sh,
+                              static_cast<unsigned>(p.Sq - 1) * orb + RB);
+  const rsrc_t rdo = make_rsrc(static_cast<const __bf16*>(p.dout) + b * p.o_sb + h * p.o_sh,
+                               static_cast<unsigned>(p.Sq - 1) * orb + RB);
+  const u32x4 kdesc = make_desc(static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh,
+                                static_cast<unsigned>(p.Skv - 1) * krb + RB);
+  const u32x4 vdesc = make_desc(static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh,
+                                static_cast<unsigned>(p.Skv - 1) * vrb + RB);
 
   const int q_row = qt * kRows + wave * 32 + l32;
   const bool q_ok = q_row < p.Sq;
@@ -176,10 +183,12 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   float delta = 0.f;
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    const unsigned off = static_cast<unsigned>(q_row) * RB + (c * 16 + g * 8) * 2;
-    qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    dof[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
-    const bf16x8 of = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+    const unsigned col = (c * 16 + g * 8) * 2;
+    const unsigned qo = q_ok ? static_cast<unsigned>(q_row) * qrb + col : 0x80000000u;
+    const unsigned oo = q_ok ? static_cast<unsigned>(q_row) * orb + col : 0x80000000u;
+    qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 0));
+    dof[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, oo, 0, 0));
+    const bf16x8 of = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0));
 #pragma unroll
     for (int e = 0; e < 8; ++e) delta = __builtin_fmaf(static_cast<float>(dof[c][e]), static_cast<float>(of[e]), delta);
   }
@@ -224,9 +233,9 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 
   const unsigned kl = lds_addr(kbuf), vl = lds_addr(vbuf);
   auto copy_stage = [&](int t, int ring) {
-    const unsigned gb = static_cast<unsigned>(stage_kv0(t, __builtin_amdgcn_readfirstlane(ent(t)))) * RB;
-    copy_tile<D>(kdesc, gb, kl + ring * G::kBufBytes, wave, lane);
-    copy_tile<D>(vdesc, gb, vl + ring * G::kBufBytes, wave, lane);
+    const unsigned kv0 = static_cast<unsigned>(stage_kv0(t, __builtin_amdgcn_readfirstlane(ent(t))));
+    copy_tile<D>(kdesc, kv0 * krb, krb, kl + ring * G::kBufBytes, wave, lane);
+    copy_tile<D>(vdesc, kv0 * vrb, vrb, vl + ring * G::kBufBytes, wave, lane);
   };
 
   if (T > 0) copy_stage(0, 0);
@@ -315,7 +324,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   }
 
   if (q_ok) {
-    const size_t orow = (q_head + q_row) * D;
+    __bf16* const drow = static_cast<__bf16*>(p.dq) + b * p.q_sb + h * p.q_sh + static_cast<size_t>(q_row) * p.q_sr;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -323,7 +332,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
         const int d0 = db * 32 + 8 * i + 4 * g;
         const u32x2 vv = {pack_bf16(dq[db][4 * i] * p.scale, dq[db][4 * i + 1] * p.scale),
                           pack_bf16(dq[db][4 * i + 2] * p.scale, dq[db][4 * i + 3] * p.scale)};
-        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dq) + orow + d0) = vv;
+        *reinterpret_cast<u32x2*>(drow + d0) = vv;
       }
   }
 }
@@ -355,10 +364,13 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   const int bkh = lin / nk;
   const int kvh = bkh % p.Hkv, b = bkh / p.Hkv;
   const int rep = p.H / p.Hkv;
-  const size_t kv_head = (static_cast<size_t>(b) * p.Hkv + kvh) * p.Skv;
-  const unsigned kvbytes = static_cast<unsigned>(p.Skv) * RB;
-  const rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + kv_head * D, kvbytes);
-  const rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + kv_head * D, kvbytes);
+  // row strides in bytes; resources end after the slice's last row
+  const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u, orb = static_cast<unsigned>(p.o_sr) * 2u;
+  const unsigned krb = static_cast<unsigned>(p.k_sr) * 2u, vrb = static_cast<unsigned>(p.v_sr) * 2u;
+  const rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh,
+                              static_cast<unsigned>(p.Skv - 1) * krb + RB);
+  const rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh,
+                              static_cast<unsigned>(p.Skv - 1) * vrb + RB);
 
   const int k_row = kt * kRows + wave * 32 + l32;
   const bool k_ok = k_row < p.Skv;
@@ -367,9 +379,11 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   bf16x8 kf[DC], vf[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    const unsigned off = static_cast<unsigned>(k_row) * RB + (c * 16 + g * 8) * 2;
-    kf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-    vf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    const unsigned col = (c * 16 + g * 8) * 2;
+    const unsigned ko = k_ok ? static_cast<unsigned>(k_row) * krb + col : 0x80000000u;
+    const unsigned vo = k_ok ? static_cast<unsigned>(k_row) * vrb + col : 0x80000000u;
+    kf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0));
+    vf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
   }
   const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
@@ -406,12 +420,13 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   auto copy_stage = [&](int u, int ring) {
     const int hh = kvh * rep + u / ns;
     const int r0 = (s0 + u % ns) * kStage;
-    const size_t q_head = (static_cast<size_t>(b) * p.H + hh) * p.Sq;
-    const unsigned qbytes = static_cast<unsigned>(p.Sq) * RB;
-    const u32x4 qd = make_desc(static_cast<const __bf16*>(p.q) + q_head * D, qbytes);
-    const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + q_head * D, qbytes);
-    copy_tile<D>(qd, static_cast<unsigned>(r0) * RB, ql + ring * G::kBufBytes, wave, lane);
-    copy_tile<D>(od, static_cast<unsigned>(r0) * RB, ol + ring * G::kBufBytes, wave, lane);
+    const size_t q_head = (static_cast<size_t>(b) * p.H + hh) * p.Sq;   // LSE and delta rows
+    const u32x4 qd = make_desc(static_cast<const __bf16*>(p.q) + b * p.q_sb + hh * p.q_sh,
+                               static_cast<unsigned>(p.Sq - 1) * qrb + RB);
+    const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + b * p.o_sb + hh * p.o_sh,
+                               static_cast<unsigned>(p.Sq - 1) * orb + RB);
+    copy_tile<D>(qd, static_cast<unsigned>(r0) * qrb, qrb, ql + ring * G::kBufBytes, wave, lane);
+    copy_tile<D>(od, static_cast<unsigned>(r0) * orb, orb, ol + ring * G::kBufBytes, wave, lane);
     if (wave == 0 && lane < 16) {
       // 64 floats of LSE and of delta: 16 lanes x 16 bytes each
       const u32x4 lsd = make_desc(p.lse + q_head, static_cast<unsigned>(p.Sq) * 4u);
@@ -546,7 +561,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   }
 
   if (k_ok) {
-    const size_t orow = (kv_head + k_row) * D;
+    __bf16* const dkrow = static_cast<__bf16*>(p.dk) + b * p.k_sb + kvh * p.k_sh + static_cast<size_t>(k_row) * p.k_sr;
+    __bf16* const dvrow = static_cast<__bf16*>(p.dv) + b * p.v_sb + kvh * p.v_sh + static_cast<size_t>(k_row) * p.v_sr;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -556,8 +572,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
                           pack_bf16(dkt[db][4 * i + 2] * p.scale, dkt[db][4 * i + 3] * p.scale)};
         const u32x2 vv = {pack_bf16(dvt[db][4 * i], dvt[db][4 * i + 1]),
                           pack_bf16(dvt[db][4 * i + 2], dvt[db][4 * i + 3])};
-        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dk) + orow + d0) = kk;
-        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.dv) + orow + d0) = vv;
+        *reinterpret_cast<u32x2*>(dkrow + d0) = kk;
+        *reinterpret_cast<u32x2*>(dvrow + d0) = vv;
       }
   }
 }

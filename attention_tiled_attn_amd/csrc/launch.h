@@ -68,6 +68,10 @@ struct BwdLaunch {
   const int* kv_count;   // block mask (256-row query tiles), or nullptr
   const int* kv_list;
   int nq, nk, bm_num_b;
+  // element strides {batch, head} and row strides: q and dq share q's, k and
+  // dk k's, v and dv v's, out and dout out's (LSE and delta are contiguous)
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sr, k_sr, v_sr, o_sr;
 };
 
 // dQ (and delta) first, then dK/dV, both on `stream`

@@ -132,8 +132,9 @@ typedef struct flexattn_params {
    * [B][H][S][D] has strides {S*H*D, D, H*D}. Strides are >= 0, a row stride
    * is >= D, and each stride times the element size is a multiple of 16
    * bytes (else FLEXATTN_ERR_ALIGN). Rows of out must not overlap. LSE is
-   * always contiguous [B][H][Sq]. flexattn_bwd takes the contiguous layout
-   * only (FLEXATTN_ERR_UNSUPPORTED otherwise).                               */
+   * always contiguous [B][H][Sq]. flexattn_bwd applies the same strides to
+   * the gradients: dq takes q_stride, dk k_stride, dv v_stride and dout
+   * o_stride; rows of dq, dk and dv must not overlap.                        */
   long long q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } flexattn_params;
 
@@ -243,8 +244,9 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
  * (Neuron FA4 explainer, "FlashAttention-4: Built for Blackwell", backward-pass
  * fixes); the gradients follow from the definition above by differentiation.
  *   q, k, v    : as for flexattn_fwd; bf16 only (params->dtype = FLEXATTN_BF16),
- *                D = 64 or 128, Skv <= 2048 * FLEXATTN_TILE, contiguous layout
- *                (else FLEXATTN_ERR_UNSUPPORTED)
+ *                D = 64 or 128, Skv <= 2048 * FLEXATTN_TILE (else
+ *                FLEXATTN_ERR_UNSUPPORTED); layouts as given by params (see
+ *                flexattn_params: each gradient takes its input's strides)
  *   out, lse   : the forward's O [B][H][Sq][D] bf16 and LSE [B][H][Sq] float32
  *   dout       : device [B][H][Sq][D] bf16, the gradient arriving at O
  *   dq         : device [B][H][Sq][D] bf16; every element is written

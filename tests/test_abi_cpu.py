@@ -243,12 +243,20 @@ BGOOD = dict(q=A, k=A, v=A, out=A, lse=A, dout=A, dq=A, dk=A, dv=A, delta=A, B=1
              Sq=128, Skv=128, D=64, scale=0.125, mask_kind=0, mod_kind=0)
 
 
-def test_bwd_rejects_strided_layouts():
-    # the backward takes the contiguous layout only (explicit contiguous strides are fine)
-    bshd = (128 * 2 * 64, 64, 2 * 64)
-    for which in ("q", "k", "v", "o"):
-        assert bcall(params=P(**{which + "_stride": bshd})) == _lib.ERR_UNSUPPORTED
-    assert bcall(params=P(q_stride=(2 * 128 * 64, 128 * 64, 64)), dq=A + 2) == _lib.ERR_ALIGN
+@pytest.mark.parametrize("stride,code", [
+    ((64 * 128, 64, 64 * 2), _lib.ERR_ALIGN),       # a valid [B, S, H, D] view; see below
+    ((2 * 128 * 64, 128 * 64, 63), _lib.ERR_ARG),    # row stride below D
+    ((2 * 128 * 64, 128 * 64, 68), _lib.ERR_ALIGN),  # rows not 16-byte aligned
+    ((-8, 128 * 64, 64), _lib.ERR_ARG),              # negative
+    ((0, 0, 2**26), _lib.ERR_OVERFLOW),              # a slice beyond 32-bit byte offsets
+])
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_bwd_layout_validation(stride, code, which):
+    # the backward takes the forward's layouts (gradients share their input's strides)
+    if stride == (64 * 128, 64, 64 * 2):
+        assert bcall(params=P(**{which + "_stride": stride}), dq=A + 2) == _lib.ERR_ALIGN
+        return
+    assert bcall(params=P(**{which + "_stride": stride})) == code
 
 
 def bcall(**over):

@@ -124,6 +124,51 @@ def test_backward_null_block_mask_is_bitwise_equal():
             assert torch.equal(x, y), var
 
 
+# ------------------------------------------------------------------ strided layouts
+def _bshd(t):
+    """The same values in a [B, S, H, D] buffer, viewed as [B, H, S, D]."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+def _packed(*ts):
+    """The tensors' values side by side in one [B, S, n, H, D + 8] buffer (a
+    packed projection output with padded rows), each viewed as [B, H, S, D]."""
+    B, H, S, D = ts[0].shape
+    buf = torch.zeros((B, S, len(ts), H, D + 8), dtype=ts[0].dtype, device=ts[0].device)
+    views = []
+    for i, t in enumerate(ts):
+        buf[:, :, i, :, :D] = t.transpose(1, 2)
+        views.append(buf[:, :, i, :, :D].transpose(1, 2))
+    return views
+
+
+@pytest.mark.parametrize("var", [dict(causal=True), dict(documents=True, causal=True, window=64),
+                                 dict(mod="relbias", rel_max=7)],
+                         ids=lambda v: ",".join(f"{a}={b}" for a, b in v.items()))
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_strided_layouts(var, D):
+    """Gradients of strided views ([B, S, H, D] buffers; q and the output
+    gradient packed with padded rows) equal those of contiguous tensors bit
+    for bit, and take the layout of their inputs."""
+    say(f"[bwd] strided {var} D={D}")
+    inp = small(B=2, H=4, Hkv=2, S=300, D=D, **var)
+    wl = inp.wl
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    dout = draw_dout(wl.B, wl.H, wl.Sq, wl.D, 11).to(torch.bfloat16).cuda()
+    dv_ = device_variant(inp)
+    out, lse = fa.attention(q, k, v, dv_, scale=wl.scale)
+    ref = fa.attention_backward(q, k, v, out, lse, dout, dv_, scale=wl.scale)
+    qs, dos = _packed(q, dout)
+    ks, vs = _bshd(k), _bshd(v)
+    outs = torch.empty_strided(dos.shape, dos.stride(), dtype=out.dtype, device=out.device)
+    outs.copy_(out)
+    got = fa.attention_backward(qs, ks, vs, outs, lse, dos, dv_, scale=wl.scale)
+    torch.cuda.synchronize()
+    for name, a, b, like in zip(("dq", "dk", "dv"), ref, got, (qs, ks, vs)):
+        assert b.stride() == like.stride(), name
+        assert torch.equal(a, b), name
+
+
 # ------------------------------------------------------------------ full size, as the bench runs it
 @pytest.mark.parametrize("name,b,kvh", [("dense", 3, 5), ("causal_gqa", 1, 6)])
 def test_backward_full_size_one_group(name, b, kvh):
