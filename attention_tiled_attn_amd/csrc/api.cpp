@@ -400,7 +400,6 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
   if (st) return st;
   if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
-  if (D == 256) return FLEXATTN_ERR_UNSUPPORTED;   // the backward kernels take D = 64 and 128
   if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
   const Strides qs = strides_of(prm->q_stride, H, Sq, D), ks = strides_of(prm->k_stride, Hkv, Skv, D);
   const Strides vs = strides_of(prm->v_stride, Hkv, Skv, D), os = strides_of(prm->o_stride, H, Sq, D);

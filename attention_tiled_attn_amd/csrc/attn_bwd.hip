@@ -40,15 +40,20 @@ using namespace dev;
 
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kRows = 128;      // query rows (dq) or keys (dkdv) per workgroup
-constexpr int kStage = 64;      // keys (dq) or query rows (dkdv) per stage
 constexpr int kTile = 128;      // key tile of the block mask
 constexpr int kRing = 3;
 constexpr int kXcds = 8;
 
 template <int D>
 struct BGeo {
+  // keys (dq) or query rows (dkdv) per stage: 64, or 32 at D = 256 so that a
+  // stage tile stays 16 KB and each ring of three 48 KB
+  static constexpr int kStage = D == 256 ? 32 : 64;
+  static constexpr int kKB = kStage / 32;              // 32-row blocks of a stage
+  static constexpr int kCH = kStage / 16;              // 16-row chunks of a stage
+  static constexpr int kSPT = kTile / kStage;          // stages per 128-key tile
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kBufBytes = kStage * D * 2;     // one 64-row tile
+  static constexpr int kBufBytes = kStage * D * 2;     // one stage tile
   static constexpr int kCpr = D / 8;                   // 16-byte chunks per row
   static constexpr int kDma = kBufBytes / 1024 / 4;    // 1 KB copies per wave and tile
   static_assert(kDma >= 1 && kBufBytes % 4096 == 0, "stage geometry");
@@ -58,9 +63,11 @@ struct BGeo {
 // quarter-wave reads in one b128 row-fragment read hit 16 different chunk
 // positions, and the 4 consecutive rows a half-wave reads in one transposing
 // read hit 4 different aligned groups of 4 chunks.
+// (Banks repeat every 16 chunks, so D = 256 rows take D = 128's permutation
+// of the low four chunk bits.)
 template <int D>
 __device__ inline int swz(int r) {
-  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  if constexpr (D >= 128) return 4 * (r & 3) + ((r >> 2) & 3);
   const int pr = r >> 1;
   return 4 * (pr & 1) + ((pr >> 1) & 3);
 }
@@ -70,7 +77,7 @@ __device__ inline unsigned row_off(int r, int chunk) {
   return static_cast<unsigned>(r * BGeo<D>::kRowBytes + ((chunk ^ swz<D>(r)) * 16));
 }
 
-// Copy 64 rows of D bf16 starting at byte `gbase` of the slice behind `desc`
+// Copy one stage of rows of D bf16 starting at byte `gbase` of the slice behind `desc`
 // (rows `grb` bytes apart) into a stage buffer: this wave fills 1 KB runs
 // wq * kDma + j; lane i writes slot i, i.e. row s / kCpr at chunk position
 // s % kCpr.
@@ -141,6 +148,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = BGeo<D>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
+  constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH, SPT = G::kSPT;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
@@ -213,23 +221,31 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : (i << 4);
   if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
-  int T = 2 * n_entries;
+  int T = SPT * n_entries;
   if (n_entries > 0) {
+    // stages of the last tile that start at or past Skv are dropped
     const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
-    if (last * kTile + kStage >= p.Skv) T -= 1;
+    const int kept = (p.Skv - last * kTile + kStage - 1) / kStage;
+    T -= SPT - min(kept, SPT);
   }
   __syncthreads();
-  auto ent = [&](int t) -> int { return ents[min(t, max(T - 1, 0)) >> 1]; };
-  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t & 1) * kStage; };
+  auto ent = [&](int t) -> int { return ents[min(t, max(T - 1, 0)) / SPT]; };
+  auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t % SPT) * kStage; };
 
-  unsigned koff[DC];
+  // fragment offsets; at D = 256 formed as needed (the chunk permutation
+  // XORs low bits only, so chunk c's row offset is chunk 0's XOR 32 c and
+  // block db's transposed offset block 0's XOR 64 db)
+  constexpr bool kXor = D == 256;
+  unsigned koff[kXor ? 1 : DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) koff[c] = row_off<D>(l32, 2 * c + g);
-  unsigned toff[DB][2];
+  for (int c = 0; c < (kXor ? 1 : DC); ++c) koff[c] = row_off<D>(l32, 2 * c + g);
+  auto koff_at = [&](int c) -> unsigned { return kXor ? koff[0] ^ (c << 5) : koff[c]; };
+  unsigned toff[kXor ? 1 : DB][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < (kXor ? 1 : DB); ++db)
 #pragma unroll
     for (int j = 0; j < 2; ++j) toff[db][j] = trans_off<D>(lane, db, j);
+  auto toff_at = [&](int db, int j) -> unsigned { return kXor ? toff[0][j] ^ (db << 6) : toff[db][j]; };
 
   const unsigned kl = lds_addr(kbuf), vl = lds_addr(vbuf);
   auto copy_stage = [&](int t, int ring) {
@@ -256,23 +272,24 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
     const unsigned char* vb_ = vbuf + ring * G::kBufBytes;
 
     // S^T = K Q^T and dP^T = V dO^T
-    f32x16 s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = f32x16{};
 #pragma unroll
     for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff[c] + kb * 32 * RB);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff_at(c) + kb * 32 * RB);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vb_ + koff[c] + kb * 32 * RB);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vb_ + koff_at(c) + kb * 32 * RB);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[c], dp[kb], 0, 0, 0);
       }
 
     // dS^T = P^T (dP^T - delta) ds'/ds, packed to bf16 in the key order of
     // the B operand (element 16 kb + r is key kv0 + 32 kb + 8 (r / 4) + 4 g + r % 4)
-    bf16x8 dsf[4];
+    bf16x8 dsf[CH];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < CH; ++ch) {
       const int kb = ch >> 1, r0 = (ch & 1) * 8;
       unsigned w[4];
 #pragma unroll
@@ -307,8 +324,8 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(kb_, toff[db][0], toff[db][1], ch),
+      for (int ch = 0; ch < CH; ++ch)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(kb_, toff_at(db, 0), toff_at(db, 1), ch),
                                                          dsf[ch], dq[db], 0, 0, 0);
 
     // stage t + 2 into the slot stage t - 1 used; retire stage t + 1
@@ -344,10 +361,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void attn_bwd_dkdv_kernel(BwdLaunch p) {
   using G = BGeo<D>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
+  constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH;
   __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing * G::kBufBytes];
-  __shared__ __attribute__((aligned(16))) float lbuf[kRing * kStage];
-  __shared__ __attribute__((aligned(16))) float dbuf[kRing * kStage];
+  __shared__ __attribute__((aligned(16))) float lbuf[kRing * BGeo<D>::kStage];
+  __shared__ __attribute__((aligned(16))) float dbuf[kRing * BGeo<D>::kStage];
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
 
@@ -405,18 +423,22 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   const int ns = q_end > q_first ? (q_end + kStage - 1) / kStage - s0 : 0;
   const int T = rep * ns;
 
-  unsigned qoff[DC];
+  // fragment offsets, formed as needed at D = 256 (as in the dQ kernel)
+  constexpr bool kXor = D == 256;
+  unsigned qoff[kXor ? 1 : DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) qoff[c] = row_off<D>(l32, 2 * c + g);
-  unsigned toff[DB][2];
+  for (int c = 0; c < (kXor ? 1 : DC); ++c) qoff[c] = row_off<D>(l32, 2 * c + g);
+  auto qoff_at = [&](int c) -> unsigned { return kXor ? qoff[0] ^ (c << 5) : qoff[c]; };
+  unsigned toff[kXor ? 1 : DB][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < (kXor ? 1 : DB); ++db)
 #pragma unroll
     for (int j = 0; j < 2; ++j) toff[db][j] = trans_off<D>(lane, db, j);
+  auto toff_at = [&](int db, int j) -> unsigned { return kXor ? toff[0][j] ^ (db << 6) : toff[db][j]; };
 
   const unsigned ql = lds_addr(qbuf), ol = lds_addr(obuf);
   const unsigned ll = lds_addr(lbuf), dl = lds_addr(dbuf);
-  // stage u: query head rep kvh + u / ns, rows 64 (s0 + u % ns) ..
+  // stage u: query head rep kvh + u / ns, rows kStage (s0 + u % ns) ..
   auto copy_stage = [&](int u, int ring) {
     const int hh = kvh * rep + u / ns;
     const int r0 = (s0 + u % ns) * kStage;
@@ -427,8 +449,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
                                static_cast<unsigned>(p.Sq - 1) * orb + RB);
     copy_tile<D>(qd, static_cast<unsigned>(r0) * qrb, qrb, ql + ring * G::kBufBytes, wave, lane);
     copy_tile<D>(od, static_cast<unsigned>(r0) * orb, orb, ol + ring * G::kBufBytes, wave, lane);
-    if (wave == 0 && lane < 16) {
-      // 64 floats of LSE and of delta: 16 lanes x 16 bytes each
+    if (wave == 0 && lane < kStage / 4) {
+      // kStage floats of LSE and of delta, 16 bytes per lane
       const u32x4 lsd = make_desc(p.lse + q_head, static_cast<unsigned>(p.Sq) * 4u);
       const u32x4 dld = make_desc(p.delta + q_head, static_cast<unsigned>(p.Sq) * 4u);
       copy_to_lds(lsd, static_cast<unsigned>(r0) * 4u + lane * 16u,
@@ -480,24 +502,25 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
       }
     }
 
-    // S = Q K^T and dP = dO V^T: two 32-row query blocks
-    f32x16 s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    // S = Q K^T and dP = dO V^T: KB 32-row query blocks
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int qb = 0; qb < KB; ++qb) s[qb] = dp[qb] = f32x16{};
 #pragma unroll
     for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qb_ + qoff[c] + qb * 32 * RB);
+      for (int qb = 0; qb < KB; ++qb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qb_ + qoff_at(c) + qb * 32 * RB);
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[c], s[qb], 0, 0, 0);
-        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ob_ + qoff[c] + qb * 32 * RB);
+        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ob_ + qoff_at(c) + qb * 32 * RB);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[c], dp[qb], 0, 0, 0);
       }
 
     // P and dS in the query order of the B operand (element 16 qb + i is row
     // r0 + 32 qb + 8 (i / 4) + 4 g + i % 4)
-    bf16x8 pf[4], dsf[4];
+    bf16x8 pf[CH], dsf[CH];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < CH; ++ch) {
       const int qb = ch >> 1, i0 = (ch & 1) * 8;
       unsigned wp[4], wd[4];
 #pragma unroll
@@ -545,10 +568,10 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(ob_, toff[db][0], toff[db][1], ch),
+      for (int ch = 0; ch < CH; ++ch) {
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(ob_, toff_at(db, 0), toff_at(db, 1), ch),
                                                           pf[ch], dvt[db], 0, 0, 0);
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qb_, toff[db][0], toff[db][1], ch),
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qb_, toff_at(db, 0), toff_at(db, 1), ch),
                                                           dsf[ch], dkt[db], 0, 0, 0);
       }
 
@@ -611,6 +634,7 @@ hipError_t launch_mod(const BwdLaunch& p, hipStream_t stream) {
 hipError_t launch_attn_bwd(const BwdLaunch& p, hipStream_t stream) {
   if (p.nk > kPairMaxKeyTiles) return hipErrorInvalidValue;
   const bool docs = p.mask_kind & kMaskDocument;
+  if (p.D == 256) return docs ? launch_mod<256, true>(p, stream) : launch_mod<256, false>(p, stream);
   if (p.D == 128) return docs ? launch_mod<128, true>(p, stream) : launch_mod<128, false>(p, stream);
   if (p.D == 64) return docs ? launch_mod<64, true>(p, stream) : launch_mod<64, false>(p, stream);
   return hipErrorInvalidValue;

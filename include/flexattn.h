@@ -244,7 +244,7 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
  * (Neuron FA4 explainer, "FlashAttention-4: Built for Blackwell", backward-pass
  * fixes); the gradients follow from the definition above by differentiation.
  *   q, k, v    : as for flexattn_fwd; bf16 only (params->dtype = FLEXATTN_BF16),
- *                D = 64 or 128, Skv <= 2048 * FLEXATTN_TILE (else
+ *                D = 64, 128 or 256, Skv <= 2048 * FLEXATTN_TILE (else
  *                FLEXATTN_ERR_UNSUPPORTED); layouts as given by params (see
  *                flexattn_params: each gradient takes its input's strides)
  *   out, lse   : the forward's O [B][H][Sq][D] bf16 and LSE [B][H][Sq] float32

@@ -275,7 +275,6 @@ def bcall(**over):
       for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "delta")],
     (dict(H=3, Hkv=2), _lib.ERR_SHAPE),
     (dict(D=96), _lib.ERR_UNSUPPORTED),
-    (dict(D=256), _lib.ERR_UNSUPPORTED),                          # forward only
     (dict(params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),     # bf16 only
     (dict(Skv=2048 * 128 + 1), _lib.ERR_UNSUPPORTED),           # key-tile list limit
     (dict(scale=0.0), _lib.ERR_ARG),

@@ -71,7 +71,7 @@ VARIANTS = [
 
 
 @pytest.mark.parametrize("var", VARIANTS, ids=lambda v: ",".join(f"{a}={b}" for a, b in v.items()) or "dense")
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_backward_variants(var, D):
     check(small(S=200, D=D, **var), f"S=200 D={D} {var}")
 
@@ -95,7 +95,7 @@ def test_backward_shapes(shape):
     dict(Sq=100, Skv=600, q_offset=500, causal=True, prefix=256, mod="alibi"),
     dict(Sq=200, Skv=450, q_offset=250, causal=True, mod="relbias", rel_max=64),
 ], ids=lambda c: ",".join(f"{a}={b}" for a, b in c.items()))
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_backward_offset_and_prefix(case, D):
     inp = small(D=D, H=4, Hkv=2, doc_range=(40, 300), **case)
     check(inp, f"D={D} {case}")
@@ -106,6 +106,12 @@ def test_backward_offset_and_prefix(case, D):
 
 def test_backward_longer_causal_gqa():
     check(small(B=1, H=4, Hkv=2, S=1100, D=128, causal=True), "S=1100 causal GQA D=128")
+
+
+def test_backward_head_dim_256_ragged():
+    """D = 256 runs 32-row stages: a ragged tail, grouped heads and documents."""
+    check(small(B=2, H=4, Hkv=2, S=333, D=256, causal=True, window=100), "S=333 D=256 causal window")
+    check(small(B=1, H=2, S=290, D=256, documents=True, mod="alibi", doc_range=(30, 150)), "S=290 D=256 docs alibi")
 
 
 def test_backward_is_reproducible():
@@ -145,7 +151,7 @@ def _packed(*ts):
 @pytest.mark.parametrize("var", [dict(causal=True), dict(documents=True, causal=True, window=64),
                                  dict(mod="relbias", rel_max=7)],
                          ids=lambda v: ",".join(f"{a}={b}" for a, b in v.items()))
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_backward_strided_layouts(var, D):
     """Gradients of strided views ([B, S, H, D] buffers; q and the output
     gradient packed with padded rows) equal those of contiguous tensors bit
