@@ -400,6 +400,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
   // online softmax of one stage: scores -> P^T (bf16) in pf, running max/sum
   auto softmax = [&](const f32x16 (&s)[KB], int kv0, bool full, int ring) {
+    // u = t - base0: the modified scores in log2 units, measured from this
+    // lane's exponent base at the start of the stage (0 while it has none);
+    // each score mod folds the base into a per-stage constant
+    const float base0 = (m_run == -INFINITY) ? 0.f : m_run;
+    const int dk0 = kv0 + 4 * g - q_pos;   // key kv0 + 4 g + c is at distance dk0 + c
     float t[KB * 16];
     // Relative bias: when every distance of the stage, over the wave's 32
     // rows, lies beyond the clip distance, all scores take the same end entry
@@ -418,16 +423,16 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       if (clipped) clip_add = sml.tab[below ? -R : R] * kLog2e;
     }
     if (clipped) {
+      const float cb = clip_add - base0;
 #pragma unroll
-      for (int i = 0; i < KB * 16; ++i) t[i] = __builtin_fmaf(s[i >> 4][i & 15], p.va.c1, clip_add);
+      for (int i = 0; i < KB * 16; ++i) t[i] = __builtin_fmaf(s[i >> 4][i & 15], p.va.c1, cb);
     } else {
+      const typename SM::Stage st = SM::stage(p.va, sml, dk0, base0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          t[kb * 16 + r] = SM::apply(s[kb][r], p.va, sml, kidx - q_pos);
-        }
+        for (int r = 0; r < 16; ++r)
+          t[kb * 16 + r] = SM::shifted(s[kb][r], p.va, sml, st, kb * 32 + 8 * (r >> 2) + (r & 3));
     }
     const float ninf = -INFINITY;
     if (!full) {
@@ -463,9 +468,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
           }
         }
     }
-    // P = exp2(t - base) rounded to bf16 into pf; returns this lane's fp32 sum
-    // of the unrounded values
-    auto exps = [&](float base) -> float {
+    // P = exp2(t) rounded to bf16 into pf; returns this lane's fp32 sum of
+    // the unrounded values
+    auto exps = [&]() -> float {
       float acc = 0.f;
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
@@ -473,14 +478,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         unsigned w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float p0, p1;
-          if constexpr (SM::kFoldScale) {
-            p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j], p.va.c1, -base));
-            p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb * 16 + r0 + 2 * j + 1], p.va.c1, -base));
-          } else {
-            p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j] - base);
-            p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1] - base);
-          }
+          const float p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j]);
+          const float p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1]);
           w[j] = pack_bf16(p0, p1);
           acc += p0 + p1;
         }
@@ -493,13 +492,13 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // Exponent base. Any base gives the same O / l and base + log2 l in exact
     // arithmetic; the base is raised to the row max only when some score of
     // the stage exceeds it by more than 2^kRescaleLog2 (the conditional
-    // rescaling of the FA4 forward-pass fixes). Without ALiBi the stage is
-    // first computed against the current base and checked afterwards: every
-    // weight is at most the lane's row sum, so a sum <= 2^kRescaleLog2 (which
-    // also rules out inf) proves no weight overflowed the bound, and the max
-    // is computed only when the check fails or no base exists yet. This pays
-    // off with soft-capping, whose tanh already keeps the vector ALU busy;
-    // without a score mod the denser exponential stream slows the other
+    // rescaling of the FA4 forward-pass fixes). With soft-capping the stage
+    // is first computed against the current base and checked afterwards:
+    // every weight is at most the lane's row sum, so a sum <= 2^kRescaleLog2
+    // (which also rules out inf) proves no weight overflowed the bound, and
+    // the max is computed only when the check fails or no base exists yet.
+    // This pays off with soft-capping, whose tanh already keeps the vector
+    // ALU busy; without it the denser exponential stream slows the other
     // wave's matrix products more than the skipped max saves, and with ALiBi
     // the bias grows with the key position so the max rises nearly every
     // stage. Those take the max first.
@@ -513,7 +512,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     float grow = kRescaleLog2;
     if constexpr (MOD == kModSoftcap) {
       if (!__any(q_ok && m_run == -INFINITY)) {
-        ls = exps(m_run == -INFINITY ? 0.f : m_run);   // padding rows may have no base yet
+        ls = exps();
         need_max = __any(q_ok && !(ls <= kSumLimit));
         grow = 0.f;
       }
@@ -522,17 +521,19 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < KB * 16; ++i) mx = fmaxf(mx, t[i]);
-      mx = max_pair32(mx);
-      if constexpr (SM::kFoldScale) mx *= p.va.c1;
-      if (__any(q_ok && mx > m_run + grow)) {
-        const float m_new = fmaxf(m_run, mx);
+      mx = max_pair32(mx);   // the row max, relative to base0
+      if (__any(q_ok && mx > (m_run == -INFINITY ? -INFINITY : grow))) {
+        const float m_new = fmaxf(m_run, mx + base0);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        const float shift = (m_new == -INFINITY) ? 0.f : m_new - base0;
+#pragma unroll
+        for (int i = 0; i < KB * 16; ++i) t[i] -= shift;
         m_run = m_new;
       }
-      ls = exps((m_run == -INFINITY) ? 0.f : m_run);
+      ls = exps();
     }
     l_run += ls;
   };

@@ -13,6 +13,11 @@
 // units, because the softmax exponential is evaluated as exp2 (the unit the
 // pages name as the forward-pass wall: Zadouri tweet; Neuron FA4 explainer,
 // "FlashAttention-4: Built for Blackwell").
+//
+// Each also has a per-stage form for the bf16 kernel: stage() prepares, per
+// lane, what depends only on the lane's row, the stage's first key kk0 and
+// the exponent base b; shifted() then gives u = t - b for the key kk0 + c (c
+// a compile-time column), so that the base costs nothing per score.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,6 +64,11 @@ struct ScoreMod<kModNone> {
   struct Lane {};
   __device__ static Lane lane(const VariantArgs&, int /*h*/, int /*q*/) { return {}; }
   __device__ static float apply(float s, const VariantArgs&, const Lane&, int /*dk*/) { return s; }
+  struct Stage { float nb; };
+  __device__ static Stage stage(const VariantArgs&, const Lane&, int /*dk0*/, float base) { return {-base}; }
+  __device__ static float shifted(float s, const VariantArgs& a, const Lane&, const Stage& st, int /*c*/) {
+    return __builtin_fmaf(s, a.c1, st.nb);
+  }
 };
 
 // ALiBi: s' = scale*q.k + slope[h] * (k_idx - q_idx). The per-lane part
@@ -72,6 +82,14 @@ struct ScoreMod<kModAlibi> {
   }
   __device__ static float apply(float s, const VariantArgs& a, const Lane& L, int dk) {
     return __builtin_fmaf(s, a.c1, L.sl * static_cast<float>(dk));
+  }
+  // the bias is linear in the key: slope * (dk0 + c) - b = fma(slope, c, B)
+  struct Stage { float B; };
+  __device__ static Stage stage(const VariantArgs&, const Lane& L, int dk0, float base) {
+    return {__builtin_fmaf(L.sl, static_cast<float>(dk0), -base)};
+  }
+  __device__ static float shifted(float s, const VariantArgs& a, const Lane& L, const Stage& st, int c) {
+    return __builtin_fmaf(s, a.c1, __builtin_fmaf(L.sl, static_cast<float>(c), st.B));
   }
 };
 
@@ -88,6 +106,15 @@ struct ScoreMod<kModSoftcap> {
     const float th = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
     return th * a.sc_out;
   }
+  // cap * tanh(x) - b = (cap - b) - 2 cap / (exp(2x) + 1): one fma after the rcp
+  struct Stage { float cb; };
+  __device__ static Stage stage(const VariantArgs& a, const Lane&, int /*dk0*/, float base) {
+    return {a.sc_out - base};
+  }
+  __device__ static float shifted(float s, const VariantArgs& a, const Lane&, const Stage& st, int /*c*/) {
+    const float e = __builtin_amdgcn_exp2f(s * a.sc_in);
+    return __builtin_fmaf(__builtin_amdgcn_rcpf(e + 1.0f), -2.0f * a.sc_out, st.cb);
+  }
 };
 
 // Relative position bias: s' = scale*q.k + table_h[clip(k_idx - q_idx, -R, R)].
@@ -101,6 +128,12 @@ struct ScoreMod<kModRelBias> {
   __device__ static float apply(float s, const VariantArgs& a, const Lane& L, int dk) {
     const int d = min(max(dk, -a.rel_max), a.rel_max);
     return __builtin_fmaf(L.tab[d], kLog2e, s * a.c1);
+  }
+  struct Stage { float nb; int dk0; };
+  __device__ static Stage stage(const VariantArgs&, const Lane&, int dk0, float base) { return {-base, dk0}; }
+  __device__ static float shifted(float s, const VariantArgs& a, const Lane& L, const Stage& st, int c) {
+    const int d = min(max(st.dk0 + c, -a.rel_max), a.rel_max);
+    return __builtin_fmaf(L.tab[d], kLog2e, __builtin_fmaf(s, a.c1, st.nb));
   }
 };
 
