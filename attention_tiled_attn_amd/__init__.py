@@ -17,8 +17,8 @@ from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_PREFIX, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
     MOD_RELBIAS, MOD_SOFTCAP, QTILE, REL_MAX, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
     flexattn_build_block_mask, flexattn_bwd, flexattn_decode, flexattn_decode_splits,
-    flexattn_decode_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_strerror,
-    flexattn_version, lib,
+    flexattn_decode_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_split_count,
+    flexattn_strerror, flexattn_version, lib,
 )
 
 __all__ = [
@@ -26,6 +26,7 @@ __all__ = [
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
     "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError", "attention_backward",
     "flexattn_decode", "flexattn_decode_splits", "flexattn_decode_workspace_bytes", "decode",
+    "flexattn_split_count",
 ]
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
@@ -168,10 +169,12 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | Non
            splits: int | None = None, out: torch.Tensor | None = None,
            lse: torch.Tensor | None = None, with_lse: bool = True,
            workspace: torch.Tensor | None = None, stream=None):
-    """attention() for few query rows per key/value head (decoding, short
-    prefill chunks; bf16): the query heads of a group share a workgroup and the
-    key range is split `splits` ways (default flexattn_decode_splits). The
-    split results need a float32 workspace, allocated here unless given."""
+    """attention() with the key range split `splits` ways (bf16; default
+    flexattn_split_count). With few query rows per key/value head (decoding,
+    short prefill chunks) the query heads of a group share a workgroup; with
+    more, every 256-row query tile's key list is split, which fills the chip
+    when heads are few. The split results need a float32 workspace, allocated
+    here unless given."""
     var = var or Variant()
     B, H, Sq, D = q.shape
     _, Hkv, Skv, _ = k.shape
@@ -179,7 +182,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | Non
         if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4:
             raise TypeError("q, k, v must be 4-D bf16 device tensors")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    splits = flexattn_decode_splits(B, Hkv, Skv) if splits is None else int(splits)
+    splits = flexattn_split_count(B, H, Hkv, Sq, Skv) if splits is None else int(splits)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:

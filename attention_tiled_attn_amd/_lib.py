@@ -28,7 +28,8 @@ QTILE = 256
 
 EXPORTS = ("flexattn_version", "flexattn_strerror", "flexattn_last_error",
            "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd", "flexattn_bwd",
-           "flexattn_decode_workspace_bytes", "flexattn_decode_splits", "flexattn_decode")
+           "flexattn_decode_workspace_bytes", "flexattn_decode_splits", "flexattn_split_count",
+           "flexattn_decode")
 
 
 class FlexAttnError(RuntimeError):
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.flexattn_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
         L.flexattn_decode_splits.restype = c_int
         L.flexattn_decode_splits.argtypes = [c_int, c_int, c_int]
+        L.flexattn_split_count.restype = c_int
+        L.flexattn_split_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
         L.flexattn_decode.restype = c_int
         L.flexattn_decode.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_float, c_int, c_int, ctypes.POINTER(Params),
@@ -174,6 +177,10 @@ def flexattn_decode_workspace_bytes(B: int, H: int, Hkv: int, Sq: int, D: int, s
 
 def flexattn_decode_splits(B: int, Hkv: int, Skv: int) -> int:
     return int(lib().flexattn_decode_splits(B, Hkv, Skv))
+
+
+def flexattn_split_count(B: int, H: int, Hkv: int, Sq: int, Skv: int) -> int:
+    return int(lib().flexattn_split_count(B, H, Hkv, Sq, Skv))
 
 
 def flexattn_decode(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: int, D: int,

@@ -293,6 +293,7 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.nq = ceil_div(Sq, FLEXATTN_QTILE);
   p.nk = ceil_div(Skv, FLEXATTN_TILE);
   p.bm_num_b = block_mask ? block_mask->num_b : 1;
+  p.splits = 1;   // whole key lists, output written directly
   hipError_t e = fa::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return FLEXATTN_OK;
@@ -316,6 +317,17 @@ int flexattn_decode_splits(int B, int Hkv, int Skv) {
   return static_cast<int>(std::max<long long>(1, std::min<long long>(s, 64)));
 }
 
+int flexattn_split_count(int B, int H, int Hkv, int Sq, int Skv) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv || Sq < 1 || Skv < 1) return 1;
+  if (static_cast<long long>(H / Hkv) * Sq <= FLEXATTN_QTILE) return flexattn_decode_splits(B, Hkv, Skv);
+  const long long items = static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_QTILE);
+  if (items >= 2 * 256) return 1;   // already about two workgroups per CU
+  const long long tiles = ceil_div(Skv, FLEXATTN_TILE);
+  long long s = (2 * 256 + items - 1) / items;
+  s = std::min<long long>(s, std::max<long long>(1, tiles / 8));   // >= 8 key tiles per split of a full list
+  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, 64)));
+}
+
 int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                     int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
                     const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
@@ -326,12 +338,14 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
   if (st) return st;
   if (prm->dtype != FLEXATTN_BF16) return FLEXATTN_ERR_UNSUPPORTED;
   const int rep = H / Hkv;
-  if (static_cast<long long>(rep) * Sq > FLEXATTN_QTILE) return FLEXATTN_ERR_UNSUPPORTED;
+  // packed: the rows of a group's rep query heads fit one workgroup
+  const bool packed = static_cast<long long>(rep) * Sq <= FLEXATTN_QTILE;
   if (ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles) return FLEXATTN_ERR_UNSUPPORTED;
-  if (mod_kind == FLEXATTN_MOD_RELBIAS &&
+  if (packed && mod_kind == FLEXATTN_MOD_RELBIAS &&
       static_cast<long long>(rep) * (2LL * prm->rel_max + 1) > fa::kRelCap)
     return FLEXATTN_ERR_UNSUPPORTED;
   if (splits < 1 || splits > 64) return FLEXATTN_ERR_ARG;
+  if (static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_QTILE) * splits > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
   if (splits > 1) {
@@ -364,9 +378,9 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
     if (!ls) ls = check_layout(vs, Skv, D, 2);
     if (!ls) ls = check_layout(os, Sq, D, 2);
     if (ls) return ls;
-    // the rows of a group's rep query heads are addressed from its first head
-    // with 32-bit byte offsets
-    if (((rep - 1) * qs.h + static_cast<long long>(Sq + FLEXATTN_QTILE) * qs.r) * 2 > INT_MAX)
+    // packed: the rows of a group's rep query heads are addressed from its
+    // first head with 32-bit byte offsets
+    if (packed && ((rep - 1) * qs.h + static_cast<long long>(Sq + FLEXATTN_QTILE) * qs.r) * 2 > INT_MAX)
       return FLEXATTN_ERR_OVERFLOW;
     p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
     p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);

@@ -109,14 +109,16 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // decode mode: (b, key/value head, split)
   const int rep = p.H / p.Hkv;
   const int np = PACK ? 1 : (p.Sq + kBM - 1) / kBM;
-  const int total = PACK ? p.B * p.Hkv * p.splits : p.B * p.H * np;
+  const int total = (PACK ? p.B * p.Hkv : p.B * p.H * np) * p.splits;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int wg = blockIdx.x;
   const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
   if (lin >= total) return;
-  int qp = PACK ? 0 : np - 1 - (lin % np);
-  const int split = PACK ? lin % p.splits : 0;
-  int slice = lin / np;   // (b, h) of the regular kernel
+  // split-KV (p.splits > 1): the splits of one item are consecutive
+  const int split = lin % p.splits;
+  const int item = lin / p.splits;
+  int qp = PACK ? 0 : np - 1 - (item % np);
+  int slice = item / np;   // (b, h) of the regular kernel
   // length and first entry of the item's key-tile list when the mapping
   // below has fetched them (n_head < 0: not fetched)
   int n_head = -1, e_head = 0;
@@ -129,7 +131,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // every tile's list is fetched with the counts, so the chosen item's
     // first copies need no further round trip.
     const int spx = p.B * p.H / kXcds;
-    if (kv_count && p.nq <= kLptMaxTiles && spx * kXcds == p.B * p.H) {
+    if (kv_count && p.splits == 1 && p.nq <= kLptMaxTiles && spx * kXcds == p.B * p.H) {
       __shared__ int sel[3];
       const int j = wg / kXcds;
       const int rank = j / spx;
@@ -161,8 +163,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       __syncthreads();   // the keys are read before the list overwrites them
     }
   }
-  const int b = PACK ? lin / p.splits / p.Hkv : slice / p.H;
-  const int kvh = PACK ? (lin / p.splits) % p.Hkv : (slice % p.H) / rep;
+  const int b = PACK ? item / p.Hkv : slice / p.H;
+  const int kvh = PACK ? item % p.Hkv : (slice % p.H) / rep;
   // this lane's row: packed index r (decode mode), its query head and row
   const int r_lane = grp * kPairHalf + wq * 32 + l32;
   const int hl = PACK ? min(r_lane / p.Sq, rep - 1) : 0;
@@ -198,9 +200,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
   int n_entries = p.nk;
   int e_spec = 0;
-  if (PACK || n_head < 0) {
+  // the whole list, from its head: the first copies start before it is staged
+  const bool early = !PACK && p.splits == 1;
+  if (!early || n_head < 0) {
     if (kv_count) n_entries = kv_count[bm_b * p.nq + qp];
-    if (!PACK && list) {
+    if (early && list) {
       e_head = list[0];
       if (tid < p.nk) e_spec = list[tid];
     }
@@ -285,23 +289,25 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     else wait_vm<G::kDma>();
   };
 
-  // non-decode items: the first two stages (both in the first key tile)
-  // are copied as soon as the list head is known; a second stage past Skv
-  // reads zeros and is never used
-  if (!PACK && n_entries > 0) {
+  // whole lists: the first two stages (both in the first key tile) are
+  // copied as soon as the list head is known; a second stage past Skv reads
+  // zeros and is never used
+  if (early && n_entries > 0) {
     issue_copy(0, e_head, 0);
     issue_copy(1, e_head, 1);
   }
 
   int e_first = 0;
-  if constexpr (PACK) {
-    // this split's part of the list; every packed row lies in query tile 0,
-    // so a tile is visited when either half admits a pair, and skips the
-    // per-element mask only when both halves are full (half 1 has no rows
-    // when Sq <= 128)
+  if (p.splits > 1) {
+    // this split's contiguous part of the list
     const int n_all = n_entries;
     e_first = static_cast<int>(static_cast<long long>(n_all) * split / p.splits);
     n_entries = static_cast<int>(static_cast<long long>(n_all) * (split + 1) / p.splits) - e_first;
+  }
+  if constexpr (PACK) {
+    // every packed row lies in query tile 0, so a tile is visited when
+    // either half admits a pair, and skips the per-element mask only when
+    // both halves are full (half 1 has no rows when Sq <= 128)
     for (int i = tid; i < n_entries; i += kThreads) {
       const int e = list ? list[e_first + i] : (((e_first + i) << 4) | 0x5);
       const bool full = (e & 2) && ((e & 8) || p.Sq <= kPairHalf);
@@ -309,13 +315,13 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     }
   } else if (list) {
     int i = tid;
-    if (n_head < 0) {   // the first kThreads entries are already in flight
+    if (early && n_head < 0) {   // the first kThreads entries are already in flight
       if (tid < n_entries) ents[tid] = e_spec;
       i += kThreads;
     }
-    for (; i < n_entries; i += kThreads) ents[i] = list[i];
+    for (; i < n_entries; i += kThreads) ents[i] = list[e_first + i];
   } else {
-    for (int i = tid; i < n_entries; i += kThreads) ents[i] = (i << 4) | 0x5;
+    for (int i = tid; i < n_entries; i += kThreads) ents[i] = ((e_first + i) << 4) | 0x5;
   }
   if constexpr (MOD == kModRelBias) {
     // decode mode: the tables of all rep heads of the group, one after another
@@ -540,8 +546,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
   // ---- prologue: stages 0 and 1 (group 0 copies K, group 1 copies V)
   const int T = n_stages;
-  if (PACK && T > 0) issue_copy(0, ent(0), 0);
-  if (PACK && T > 1) issue_copy(1, ent(1), 1);
+  if (!early && T > 0) issue_copy(0, ent(0), 0);
+  if (!early && T > 1) issue_copy(1, ent(1), 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one slot behind
@@ -601,11 +607,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // ---- epilogue: normalise, LSE, store
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (PACK && p.splits > 1) {
-    // this split's normalised rows and LSE, merged by attn_decode_merge_kernel
+  if (p.splits > 1) {
+    // this split's normalised rows and LSE, merged by attn_decode_merge_kernel;
+    // workspace rows [split][b][h][q_row] (in decode mode h = kvh rep + hl)
     if (q_ok) {
-      const int rows = rep * p.Sq;
-      const size_t wrow = ((static_cast<size_t>(split) * p.B + b) * p.Hkv + kvh) * rows + r_lane;
+      const size_t wrow = ((static_cast<size_t>(split) * p.B + b) * p.H + h) * p.Sq + q_row;
       float* const wo = p.ws_o + wrow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -674,8 +680,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 template <int D, int MOD, bool DOCS, bool PACK>
 hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const int np = (p.Sq + kBM - 1) / kBM;
-  const long long total = PACK ? static_cast<long long>(p.B) * p.Hkv * p.splits
-                               : static_cast<long long>(p.B) * p.H * np;
+  const long long total = (PACK ? static_cast<long long>(p.B) * p.Hkv
+                                : static_cast<long long>(p.B) * p.H * np) * p.splits;
   const long long per = (total + kXcds - 1) / kXcds;
   hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS, PACK>), dim3(static_cast<unsigned>(per * kXcds)),
                      dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
@@ -695,6 +701,7 @@ hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
 
 template <bool PACK>
 hipError_t launch_dims(const FwdLaunch& p, hipStream_t stream) {
+  if (p.splits < 1) return hipErrorInvalidValue;
   const bool docs = p.mask_kind & kMaskDocument;
   if (p.D == 256) return docs ? launch_mod<256, true, PACK>(p, stream) : launch_mod<256, false, PACK>(p, stream);
   if (p.D == 128) return docs ? launch_mod<128, true, PACK>(p, stream) : launch_mod<128, false, PACK>(p, stream);
@@ -741,8 +748,11 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(FwdLaunch p) {
 
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<false>(p, stream); }
 
+// Split-KV: a group's rows packed into one workgroup when they fit (decode
+// mode), else the regular mapping with every query tile's list split.
 hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
-  hipError_t e = launch_dims<true>(p, stream);
+  const bool pack = static_cast<long long>(p.H / p.Hkv) * p.Sq <= kBM;
+  hipError_t e = pack ? launch_dims<true>(p, stream) : launch_dims<false>(p, stream);
   if (e != hipSuccess || p.splits <= 1) return e;
   const long long n = static_cast<long long>(p.B) * p.Hkv * (p.H / p.Hkv) * p.Sq * (p.D / 4);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,

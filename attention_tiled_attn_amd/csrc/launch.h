@@ -34,11 +34,12 @@ struct FwdLaunch {
   const int* kv_count;
   const int* kv_list;
   int nq, nk, bm_num_b;
-  // decode mode (launch_attn_decode): the H/Hkv query heads of a key/value
-  // head share a workgroup (rep * Sq <= 256 packed rows) and the key-tile list
-  // is split over `splits` workgroups; with splits > 1 each writes its rows'
-  // normalised O (float32) and LSE to ws_o [splits][B][Hkv][rows][D] and
-  // ws_lse [splits][B][Hkv][rows], merged by a second kernel
+  // key-tile lists split over `splits` >= 1 workgroups (launch_attn_decode;
+  // 1 for launch_attn_fwd). When rep * Sq <= 256 the H/Hkv query heads of a
+  // key/value head share a workgroup as packed rows (decode mode). With
+  // splits > 1 each writes its rows' normalised O (float32) and LSE to
+  // ws_o [splits][B][H][Sq][D] and ws_lse [splits][B][H][Sq], merged by a
+  // second kernel
   int splits;
   float* ws_o;
   float* ws_lse;

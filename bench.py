@@ -258,8 +258,8 @@ def main(argv=None):
         torch.cuda.synchronize()
 
     splits = workspace = None
-    if wl.decode:
-        splits = fa.flexattn_decode_splits(wl.B, wl.Hkv, wl.Skv)
+    if wl.decode or wl.split:
+        splits = fa.flexattn_split_count(wl.B, wl.H, wl.Hkv, wl.Sq, wl.Skv)
         nbytes = fa.flexattn_decode_workspace_bytes(wl.B, wl.H, wl.Hkv, wl.Sq, wl.D, splits)
         workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=dev)
 
@@ -270,7 +270,7 @@ def main(argv=None):
         if bwd:
             fa.attention_backward(q, k, v, out, lse, dout, var, scale=wl.scale, block_mask=bm,
                                   dq=dq, dk=dk, dv=dv, delta=delta)
-        elif wl.decode:
+        elif wl.decode or wl.split:
             fa.decode(q, k, v, var, scale=wl.scale, block_mask=bm, out=out, lse=lse,
                       splits=splits, workspace=workspace)
         else:
@@ -331,7 +331,10 @@ def main(argv=None):
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_bytes": bytes_alg,
                 "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkdv_kernel" if bwd else
+                           "attn_fwd_pp_kernel (split keys) + attn_decode_merge_kernel" if wl.split else
                            "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel")}
+        if wl.split:
+            roof["splits"] = splits
 
     rec = {
         "metric": ("attention bwd effective TFLOPS (2.5x forward unmasked FLOPs), 1 GPU" if bwd else

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_VERSION 2
+#define FLEXATTN_VERSION 3
 
 /* Block-mask tiles: FLEXATTN_QTILE query rows (two halves of FLEXATTN_TILE
  * rows) by FLEXATTN_TILE keys. */
@@ -212,26 +212,42 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const flexattn_params* params, const flexattn_block_mask* block_mask,
                  void* stream);
 
-/* Attention forward for few query rows per key/value head: decoding (Sq = 1
- * with q_offset = Skv - 1) and short prefill chunks. Computes what
- * flexattn_fwd computes, organised for that shape: the rep = H / Hkv query
- * heads of a key/value head share a workgroup as rep * Sq packed rows (at most
- * 256, else FLEXATTN_ERR_UNSUPPORTED), so each K/V element is read once, and
- * the key tiles are split over `splits` workgroups (1 <= splits <= 64) whose
+/* Split-KV attention forward: what flexattn_fwd computes, with each item's
+ * key tiles split over `splits` workgroups (1 <= splits <= 64) whose
  * normalised partial results are merged as O = sum_s exp(LSE_s - LSE) O_s,
- * LSE = log sum_s exp(LSE_s) by a second kernel on the same stream. bf16
- * only; every variant and layout of flexattn_fwd; block_mask as there (built
- * for these Sq, Skv). With FLEXATTN_MOD_RELBIAS the group's tables must fit
- * together: rep * (2 * rel_max + 1) <= 2 * FLEXATTN_REL_MAX + 2.
+ * LSE = log sum_s exp(LSE_s) by a second kernel on the same stream. Two
+ * organisations, chosen by the shape:
+ *   rep * Sq <= 256 (rep = H / Hkv; decoding, Sq = 1 with q_offset = Skv - 1,
+ *     and short prefill chunks): the rep query heads of a key/value head
+ *     share a workgroup as rep * Sq packed rows, so each K/V element is read
+ *     once; with FLEXATTN_MOD_RELBIAS the group's tables must fit together:
+ *     rep * (2 * rel_max + 1) <= 2 * FLEXATTN_REL_MAX + 2;
+ *   otherwise: flexattn_fwd's 256-row query tiles, each tile's key list cut
+ *     into `splits` contiguous parts, for grids too small to fill the chip
+ *     (few heads, long causal rows).
+ * Faster inference and longer contexts are among the uses the pages give the
+ * method (Neuron FA4 explainer, "Why This Matters for Everyone"); splitting
+ * the keys is how one query row, or a few heads, fill the chip, and the
+ * merge is the log-sum-exp identity of the forward's own LSE output. bf16
+ * only; every variant and layout of flexattn_fwd;
+ * block_mask as there (built for these Sq, Skv); B * H * ceil(Sq / 256) *
+ * splits <= INT_MAX (else FLEXATTN_ERR_OVERFLOW).
  *   workspace : device memory of flexattn_decode_workspace_bytes(...) bytes,
  *               16-byte aligned, caller-owned scratch (contents afterwards
  *               unspecified); may be NULL when splits == 1
  * Results equal flexattn_fwd's up to float32 rounding in the merge. */
 size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits);
 
-/* A split count for flexattn_decode that gives the chip at least ~2 workgroups
- * per CU while leaving each at least 4 key tiles (128 keys each). */
+/* A split count for packed decoding (rep * Sq <= 256) that gives the chip at
+ * least ~2 workgroups per CU while leaving each at least 4 key tiles (128
+ * keys each). */
 int flexattn_decode_splits(int B, int Hkv, int Skv);
+
+/* A split count for flexattn_decode in either organisation: the packed rule
+ * above, else 1 when B * H * ceil(Sq / 256) already gives ~2 workgroups per
+ * CU, otherwise enough splits for that while each split of a whole key list
+ * keeps at least 8 key tiles. Invalid sizes give 1. */
+int flexattn_split_count(int B, int H, int Hkv, int Sq, int Skv);
 
 int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                     int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.flexattn_version() == 2
+    assert fa.flexattn_version() == 3
     for code in range(-8, 1):
         assert fa.flexattn_strerror(code) and fa.flexattn_strerror(code) != "unknown status"
     assert fa.flexattn_strerror(-99) == "unknown status"
@@ -304,6 +304,14 @@ def test_decode_workspace_and_splits():
     assert fa.flexattn_decode_splits(1, 1, 1 << 20) == 64
     assert fa.flexattn_decode_splits(1, 8, 1024) == 2
     assert fa.flexattn_decode_splits(64, 8, 8192) == 1
+    # either organisation: packed decoding takes the rule above; otherwise
+    # ~2 workgroups per CU over B * H * ceil(Sq / 256) items, >= 8 key tiles per split
+    assert fa.flexattn_split_count(16, 32, 8, 1, 32768) == fa.flexattn_decode_splits(16, 8, 32768)
+    assert fa.flexattn_split_count(2, 4, 1, 8192, 8192) == 2      # 256 items
+    assert fa.flexattn_split_count(4, 16, 16, 4096, 4096) == 1    # 1024 items
+    assert fa.flexattn_split_count(1, 4, 4, 4096, 4096) == 4      # 64 items, 32 key tiles
+    assert fa.flexattn_split_count(1, 1, 1, 300, 300) == 1        # 3 key tiles
+    assert fa.flexattn_split_count(1, 3, 2, 300, 300) == 1        # invalid: H % Hkv
 
 
 def dcall(**over):
@@ -321,7 +329,9 @@ def dcall(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), _lib.ERR_NULLPTR),
     (dict(params=P(dtype=_lib.FP32)), _lib.ERR_UNSUPPORTED),     # bf16 only
-    (dict(Sq=65, H=8, Hkv=2), _lib.ERR_UNSUPPORTED),            # 4 x 65 packed rows > 256
+    (dict(Sq=65, H=8, Hkv=2, ws=A + 4), _lib.ERR_ALIGN),        # 4 x 65 rows > 256: split tiles, still checked
+    (dict(Sq=65, H=8, Hkv=2, wsb=100), _lib.ERR_ARG),
+    (dict(Sq=300, mod_kind=3, params=P(rel_bias=A, rel_max=300), ws=A + 4), _lib.ERR_ALIGN),  # not packed: one table
     (dict(splits=0), _lib.ERR_ARG),
     (dict(splits=65), _lib.ERR_ARG),
     (dict(ws=None), _lib.ERR_NULLPTR),                           # two splits need a workspace

@@ -45,6 +45,7 @@ class Workload:
     sq: int = 0                 # > 0: query rows, when fewer than the keys
     rel_max: int = 0            # clip distance R of the relative-bias table (mod "relbias")
     decode: bool = False        # run through the decode entry point (packed heads, split keys)
+    split: bool = False         # run through the split-KV entry point (split key lists, merged)
 
     @property
     def Sq(self) -> int:
@@ -74,6 +75,10 @@ WORKLOADS = {
     # (whole GQA groups: 1 key/value head and its 4 query heads per GPU)
     "causal_gqa_shard8": Workload("causal_gqa_shard8", B=2, H=4, Hkv=1, S=8192, D=128,
                                   dtype="bf16", causal=True, seed=2),
+    # the same shard through the split-KV entry point: 256 query tiles for 256
+    # CUs, each tile's key list split and the parts merged
+    "causal_gqa_shard8_split": Workload("causal_gqa_shard8_split", B=2, H=4, Hkv=1, S=8192, D=128,
+                                        dtype="bf16", causal=True, seed=2, split=True),
     "doc_swa": Workload("doc_swa", B=1, H=16, Hkv=16, S=16384, D=128, dtype="bf16",
                         causal=True, window=1024, documents=True, seed=3, doc_seed=3),
     "alibi_d64": Workload("alibi_d64", B=1, H=32, Hkv=32, S=32768, D=64, dtype="bf16",
