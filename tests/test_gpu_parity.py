@@ -347,3 +347,28 @@ def test_head_dim_256_strided_and_decode():
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
     Oref, Lref = run_oracle(inp)
     compare(to_np(O3), to_np(L3), Oref, Lref, "D=256 decode")
+
+
+# ------------------------------------------------------------------ maximum key-list lengths
+@pytest.mark.parametrize("Skv", [2048 * 128, 2048 * 128 + 77], ids=["2048 tiles", "past 2048 tiles"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_maximum_key_lists(Skv, causal):
+    """The ping-pong kernel's longest key-tile list (2048 tiles of 128 keys)
+    and one key past it, where bf16 inputs go to the 128-row kernel; every
+    query row is compared with the oracle."""
+    Sq = 64
+    inp = small(B=1, H=2, Hkv=1, Sq=Sq, Skv=Skv, D=64, causal=causal,
+                q_offset=(Skv - Sq) if causal else 0)
+    check_full(inp, what=f"Skv={Skv} causal={causal}")
+
+
+def test_decode_maximum_key_list():
+    """Decoding at the longest cache the forward takes (2048 key tiles), the
+    library's split count, against the oracle."""
+    Skv = 2048 * 128
+    inp = small(B=1, H=4, Hkv=1, Sq=1, Skv=Skv, D=128, causal=True, q_offset=Skv - 1)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    O, L = fa.decode(q, k, v, device_variant(inp), scale=inp.wl.scale)
+    torch.cuda.synchronize()
+    Oref, Lref = run_oracle(inp)
+    compare(to_np(O), to_np(L), Oref, Lref, "decode, 2048 key tiles")
