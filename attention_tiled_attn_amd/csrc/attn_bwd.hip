@@ -44,11 +44,10 @@ constexpr int kTile = 128;      // key tile of the block mask
 constexpr int kRing = 3;
 constexpr int kXcds = 8;
 
-template <int D>
+template <int D, int STAGE>
 struct BGeo {
-  // keys (dq) or query rows (dkdv) per stage: 64, or 32 at D = 256 so that a
-  // stage tile stays 16 KB and each ring of three 48 KB
-  static constexpr int kStage = D == 256 ? 32 : 64;
+  // keys (dq) or query rows (dkdv) per stage
+  static constexpr int kStage = STAGE;
   static constexpr int kKB = kStage / 32;              // 32-row blocks of a stage
   static constexpr int kCH = kStage / 16;              // 16-row chunks of a stage
   static constexpr int kSPT = kTile / kStage;          // stages per 128-key tile
@@ -74,16 +73,16 @@ __device__ inline int swz(int r) {
 
 template <int D>
 __device__ inline unsigned row_off(int r, int chunk) {
-  return static_cast<unsigned>(r * BGeo<D>::kRowBytes + ((chunk ^ swz<D>(r)) * 16));
+  return static_cast<unsigned>(r * (D * 2) + ((chunk ^ swz<D>(r)) * 16));
 }
 
 // Copy one stage of rows of D bf16 starting at byte `gbase` of the slice behind `desc`
 // (rows `grb` bytes apart) into a stage buffer: this wave fills 1 KB runs
 // wq * kDma + j; lane i writes slot i, i.e. row s / kCpr at chunk position
 // s % kCpr.
-template <int D>
+template <int D, int STAGE>
 __device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned grb, unsigned lds_base, int wq, int lane) {
-  using G = BGeo<D>;
+  using G = BGeo<D, STAGE>;
 #pragma unroll
   for (int j = 0; j < G::kDma; ++j) {
     const int s = (wq * G::kDma + j) * 64 + lane;
@@ -100,8 +99,8 @@ __device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned grb, unsig
 // reads. toff[db][j] is this lane's offset for ch = 0.
 template <int D>
 __device__ inline bf16x8 trans_frag(const unsigned char* buf, unsigned toff0, unsigned toff1, int ch) {
-  const unsigned char* a0 = buf + toff0 + 16 * ch * BGeo<D>::kRowBytes;
-  const unsigned char* a1 = buf + toff1 + 16 * ch * BGeo<D>::kRowBytes;
+  const unsigned char* a0 = buf + toff0 + 16 * ch * (D * 2);
+  const unsigned char* a1 = buf + toff1 + 16 * ch * (D * 2);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
   const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -142,11 +141,21 @@ __device__ inline float mod_score(float s, const VariantArgs& va, float slope2, 
 }
 
 // ---------------------------------------------------------------------------
+// Stage sizes. dQ: 32 keys per stage at every D, which keeps a workgroup
+// under 64 KB of LDS and a wave under 256 registers at D <= 128, so two
+// workgroups share a CU (two waves per SIMD: one's matrix products overlap
+// the other's vector work). dK/dV: 64 query rows (32 at D = 256, where a
+// 64-row tile would not leave room for the three-stage rings), one wave per
+// SIMD: its accumulators and K^T, V^T fragments need more than 256 registers.
+template <int D> constexpr int kDqStage = 32;
+template <int D> constexpr int kDkvStage = D == 256 ? 32 : 64;
+template <int D> constexpr int kDqWaves = D == 256 ? 1 : 2;   // waves per SIMD
+
 // dQ (and delta)
 template <int D, int MOD, bool DOCS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>, kDqWaves<D>)))
 void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
-  using G = BGeo<D>;
+  using G = BGeo<D, kDqStage<D>>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
   constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH, SPT = G::kSPT;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
@@ -250,8 +259,8 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const unsigned kl = lds_addr(kbuf), vl = lds_addr(vbuf);
   auto copy_stage = [&](int t, int ring) {
     const unsigned kv0 = static_cast<unsigned>(stage_kv0(t, __builtin_amdgcn_readfirstlane(ent(t))));
-    copy_tile<D>(kdesc, kv0 * krb, krb, kl + ring * G::kBufBytes, wave, lane);
-    copy_tile<D>(vdesc, kv0 * vrb, vrb, vl + ring * G::kBufBytes, wave, lane);
+    copy_tile<D, kStage>(kdesc, kv0 * krb, krb, kl + ring * G::kBufBytes, wave, lane);
+    copy_tile<D, kStage>(vdesc, kv0 * vrb, vrb, vl + ring * G::kBufBytes, wave, lane);
   };
 
   if (T > 0) copy_stage(0, 0);
@@ -359,13 +368,13 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 template <int D, int MOD, bool DOCS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_kernel(BwdLaunch p) {
-  using G = BGeo<D>;
+  using G = BGeo<D, kDkvStage<D>>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
   constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH;
   __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing * G::kBufBytes];
-  __shared__ __attribute__((aligned(16))) float lbuf[kRing * BGeo<D>::kStage];
-  __shared__ __attribute__((aligned(16))) float dbuf[kRing * BGeo<D>::kStage];
+  __shared__ __attribute__((aligned(16))) float lbuf[kRing * kDkvStage<D>];
+  __shared__ __attribute__((aligned(16))) float dbuf[kRing * kDkvStage<D>];
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
 
@@ -447,8 +456,8 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
                                static_cast<unsigned>(p.Sq - 1) * qrb + RB);
     const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + b * p.o_sb + hh * p.o_sh,
                                static_cast<unsigned>(p.Sq - 1) * orb + RB);
-    copy_tile<D>(qd, static_cast<unsigned>(r0) * qrb, qrb, ql + ring * G::kBufBytes, wave, lane);
-    copy_tile<D>(od, static_cast<unsigned>(r0) * orb, orb, ol + ring * G::kBufBytes, wave, lane);
+    copy_tile<D, kStage>(qd, static_cast<unsigned>(r0) * qrb, qrb, ql + ring * G::kBufBytes, wave, lane);
+    copy_tile<D, kStage>(od, static_cast<unsigned>(r0) * orb, orb, ol + ring * G::kBufBytes, wave, lane);
     if (wave == 0 && lane < kStage / 4) {
       // kStage floats of LSE and of delta, 16 bytes per lane
       const u32x4 lsd = make_desc(p.lse + q_head, static_cast<unsigned>(p.Sq) * 4u);
