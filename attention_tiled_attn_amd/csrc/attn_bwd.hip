@@ -15,17 +15,18 @@
 //  * attn_bwd_dq_kernel: one workgroup (4 waves x 32 rows) per 128 query rows
 //    of one (batch, head); it first forms delta for its rows (written to the
 //    caller's scratch for the second kernel), then walks the key tiles of the
-//    block mask: S^T = K Q^T and dP^T = V dO^T (A operands K and V rows), then
-//    dQ^T += K^T dS^T (A operand K^T through transposing LDS reads).
+//    block mask in 32-key stages: S^T = K Q^T and dP^T = V dO^T (A operands K
+//    and V rows), then dQ^T += K^T dS^T (A operand K^T through transposing
+//    LDS reads). Two of these workgroups share a CU at D <= 128.
 //  * attn_bwd_dkdv_kernel: one workgroup (4 waves x 32 keys) per 128 keys of
 //    one (batch, key/value head); it walks the query heads of the group and
-//    the 64-row query stages that can see its keys: S = Q K^T and dP = dO V^T
-//    (B operands K^T and V^T kept in registers), then dV^T += dO^T P and
-//    dK^T += Q^T dS (A operands through transposing LDS reads of dO and Q).
+//    the query stages (64 rows, 32 at D = 256) that can see its keys:
+//    S = Q K^T and dP = dO V^T (B operands K^T and V^T kept in registers),
+//    then dV^T += dO^T P and dK^T += Q^T dS (A operands through transposing
+//    LDS reads of dO and Q).
 // Tiles go from HBM/L2 straight into LDS (buffer-to-LDS copies, a ring of
-// three 64-row stages), rows unpadded with 16-byte chunks permuted so that
-// both the b128 row reads and the transposing reads are free of bank
-// conflicts.
+// three stages), rows unpadded with 16-byte chunks permuted so that both the
+// b128 row reads and the transposing reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -416,7 +417,7 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   const rsrc_t rdoc = make_rsrc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
   const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
 
-  // the 64-row query stages that can see keys [k_lo, k_hi] of this tile
+  // the query stages that can see keys [k_lo, k_hi] of this tile
   // (query row r sits at position r + q_offset; keys below the prefix are
   // exempt from the causal part)
   const bool causal = p.mask_kind & kMaskCausal;

@@ -83,6 +83,8 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 // PACK (decode mode): a workgroup owns the rep = H / Hkv query heads of one
 // key/value head, packed as rows r = head_in_group * Sq + q_row (at most 256),
 // and one of p.splits contiguous parts of the key-tile list of query tile 0.
+// Without PACK, p.splits > 1 cuts every query tile's list the same way. Split
+// results go to the workspace and attn_decode_merge_kernel combines them.
 template <int D, int MOD, bool DOCS, bool PACK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
@@ -105,8 +107,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // ---- workgroup -> (b, h, 256-row tile): XCD-contiguous, heavy tiles first;
-  // decode mode: (b, key/value head, split)
+  // ---- workgroup -> (b, h, 256-row tile[, split]): XCD-contiguous, heavy
+  // tiles first; decode mode: (b, key/value head, split)
   const int rep = p.H / p.Hkv;
   const int np = PACK ? 1 : (p.Sq + kBM - 1) / kBM;
   const int total = (PACK ? p.B * p.Hkv : p.B * p.H * np) * p.splits;
