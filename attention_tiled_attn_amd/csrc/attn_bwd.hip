@@ -372,10 +372,13 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   using G = BGeo<D, kDkvStage<D>>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
   constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH;
-  __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kRing * G::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing * G::kBufBytes];
-  __shared__ __attribute__((aligned(16))) float lbuf[kRing * kDkvStage<D>];
-  __shared__ __attribute__((aligned(16))) float dbuf[kRing * kDkvStage<D>];
+  // a ring of four stages: stage u is read for S, dP and P, dS in iteration
+  // u, and again for dV, dK in iteration u + 1, while stage u + 2 arrives
+  constexpr int kRing4 = 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kRing4 * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf[kRing4 * G::kBufBytes];
+  __shared__ __attribute__((aligned(16))) float lbuf[kRing4 * kDkvStage<D>];
+  __shared__ __attribute__((aligned(16))) float dbuf[kRing4 * kDkvStage<D>];
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
 
@@ -488,8 +491,29 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) dkt[i] = dvt[i] = f32x16{};
 
-  int ring = 0;
+  // dV^T += dO^T P and dK^T += Q^T dS of one stage (slot `sl`). They run one
+  // iteration late, beside the next stage's vector work, which they do not
+  // depend on: with one wave per SIMD this is where matrix and vector work
+  // overlap.
+  bf16x8 pf_prev[CH], dsf_prev[CH];
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) pf_prev[ch] = dsf_prev[ch] = bf16x8{};
+  auto dkdv_products = [&](int sl) {
+    const unsigned char* qp_ = qbuf + sl * G::kBufBytes;
+    const unsigned char* op_ = obuf + sl * G::kBufBytes;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(op_, toff_at(db, 0), toff_at(db, 1), ch),
+                                                          pf_prev[ch], dvt[db], 0, 0, 0);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qp_, toff_at(db, 0), toff_at(db, 1), ch),
+                                                          dsf_prev[ch], dkt[db], 0, 0, 0);
+      }
+  };
+
   for (int u = 0; u < T; ++u) {
+    const int ring = u % kRing4;
     const int hh = kvh * rep + u / ns;
     const int r0 = (s0 + u % ns) * kStage;
     const unsigned char* qb_ = qbuf + ring * G::kBufBytes;
@@ -527,7 +551,42 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
       }
 
     // P and dS in the query order of the B operand (element 16 qb + i is row
-    // r0 + 32 qb + 8 (i / 4) + 4 g + i % 4)
+    // r0 + 32 qb + 8 (i / 4) + 4 g + i % 4). The modified scores are formed
+    // for every element first and masked in place on partial stages, so the
+    // exponentials below sit in one block with the previous stage's
+    // products, which the compiler can interleave with them.
+    float tt[KB * 16];
+    float dmv[MOD == kModSoftcap ? KB * 16 : 1];
+#pragma unroll
+    for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qpos = r0 + 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3) + off;
+        float dmod;
+        tt[qb * 16 + i] = mod_score<MOD>(s[qb][i], p.va, slope2, tab, k_row - qpos, dmod);
+        if constexpr (MOD == kModSoftcap) dmv[qb * 16 + i] = dmod;
+      }
+    if (!full) {
+      const float ninf = -INFINITY;
+#pragma unroll
+      for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int ql0 = 32 * qb + 8 * i4 + 4 * g;
+          u32x4 lab = {0u, 0u, 0u, 0u};
+          if constexpr (DOCS) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0 + off) * 4u, 0, 0);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int qrow = r0 + ql0 + x;
+            const int qpos = qrow + off;
+            bool ok = k_ok && qrow < p.Sq;
+            ok &= !causal | (qpos >= k_row) | (k_row < p.va.prefix);
+            ok &= !window | (qpos - k_row < p.va.window);
+            if constexpr (DOCS) ok &= static_cast<int>(lab[x]) == doc_k;
+            mask_in_place(tt[qb * 16 + 4 * i4 + x], __builtin_amdgcn_ballot_w64(ok), ninf);
+          }
+        }
+    }
     bf16x8 pf[CH], dsf[CH];
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
@@ -539,29 +598,15 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
         const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + ql0);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + ql0);
-        u32x4 lab = {0u, 0u, 0u, 0u};
-        if constexpr (DOCS) {
-          if (!full) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0 + off) * 4u, 0, 0);
-        }
         float pv[4], dv4[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = i0 + 4 * hv + x;
-          const int qrow = r0 + ql0 + x;
-          float dmod;
-          const int qpos = qrow + off;
-          float tt = mod_score<MOD>(s[qb][i], p.va, slope2, tab, k_row - qpos, dmod);
-          if (!full) {
-            bool ok = k_ok && qrow < p.Sq;
-            ok &= !causal | (qpos >= k_row) | (k_row < p.va.prefix);
-            ok &= !window | (qpos - k_row < p.va.window);
-            if constexpr (DOCS) ok &= static_cast<int>(lab[x]) == doc_k;
-            tt = ok ? tt : -INFINITY;
-          }
           const float lse2 = (l4[x] == -INFINITY) ? INFINITY : l4[x] * kLog2e;
-          const float pr = __builtin_amdgcn_exp2f(tt - lse2);
+          const float pr = __builtin_amdgcn_exp2f(tt[qb * 16 + i] - lse2);
           pv[x] = pr;
-          dv4[x] = pr * (dp[qb][i] - d4[x]) * dmod;
+          dv4[x] = pr * (dp[qb][i] - d4[x]);
+          if constexpr (MOD == kModSoftcap) dv4[x] *= dmv[qb * 16 + i];
         }
         wp[2 * hv] = pack_bf16(pv[0], pv[1]);
         wp[2 * hv + 1] = pack_bf16(pv[2], pv[3]);
@@ -574,24 +619,27 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
       dsf[ch] = __builtin_bit_cast(bf16x8, wdv);
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS
+    // the previous stage's dV, dK products (at u = 0 the zero fragments on
+    // stage 0's rows, which add exactly nothing)
+    dkdv_products(u == 0 ? 0 : (u - 1) % kRing4);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int ch = 0; ch < CH; ++ch) {
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(ob_, toff_at(db, 0), toff_at(db, 1), ch),
-                                                          pf[ch], dvt[db], 0, 0, 0);
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qb_, toff_at(db, 0), toff_at(db, 1), ch),
-                                                          dsf[ch], dkt[db], 0, 0, 0);
-      }
+    for (int ch = 0; ch < CH; ++ch) {
+      // P and dS are needed only by the next iteration: without this use the
+      // compiler sinks them past the copies below, out of the products' block
+      asm volatile("" ::"v"(pf[ch]), "v"(dsf[ch]));
+      pf_prev[ch] = pf[ch];
+      dsf_prev[ch] = dsf[ch];
+    }
 
-    const int ring2 = ring == 0 ? kRing - 1 : ring - 1;
+    // stage u + 2 into the slot stage u - 2 used (its last reader, the
+    // previous iteration's products, finished before the last barrier);
+    // retire stage u + 1
     const bool more = u + 2 < T;
-    if (more) copy_stage(u + 2, ring2);
+    if (more) copy_stage(u + 2, (u + 2) % kRing4);
     retire(more);
     __syncthreads();
-    ring = ring == kRing - 1 ? 0 : ring + 1;
   }
+  if (T > 0) dkdv_products((T - 1) % kRing4);
 
   if (k_ok) {
     __bf16* const dkrow = static_cast<__bf16*>(p.dk) + b * p.k_sb + kvh * p.k_sh + static_cast<size_t>(k_row) * p.k_sr;
