@@ -159,8 +159,11 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   using G = BGeo<D, kDqStage<D>>;
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
   constexpr int kStage = G::kStage, KB = G::kKB, CH = G::kCH, SPT = G::kSPT;
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing * G::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing * G::kBufBytes];
+  // a ring of four stages: stage t is read for S^T, dP^T in iteration t and
+  // for the dQ products in iteration t + 1, while stage t + 2 arrives
+  constexpr int kRing4 = 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing4 * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing4 * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
@@ -273,8 +276,23 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
   for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
 
-  int ring = 0;
+  // dQ^T += K^T dS^T of one stage (slot `sl`), one iteration late, beside the
+  // next stage's exponentials (as in the dK/dV kernel)
+  bf16x8 dsf_prev[CH];
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) dsf_prev[ch] = bf16x8{};
+  auto dq_products = [&](int sl) {
+    const unsigned char* kp_ = kbuf + sl * G::kBufBytes;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(kp_, toff_at(db, 0), toff_at(db, 1), ch),
+                                                         dsf_prev[ch], dq[db], 0, 0, 0);
+  };
+
   for (int t = 0; t < T; ++t) {
+    const int ring = t % kRing4;
     const int e = __builtin_amdgcn_readfirstlane(ent(t));
     const bool full = ((e >> full_bit) & 1) != 0;
     const int kv0 = stage_kv0(t, e);
@@ -296,7 +314,37 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
       }
 
     // dS^T = P^T (dP^T - delta) ds'/ds, packed to bf16 in the key order of
-    // the B operand (element 16 kb + r is key kv0 + 32 kb + 8 (r / 4) + 4 g + r % 4)
+    // the B operand (element 16 kb + r is key kv0 + 32 kb + 8 (r / 4) + 4 g + r % 4).
+    // The modified scores are formed first and masked in place on partial
+    // stages, so the exponentials share a block with the deferred products.
+    float tt[KB * 16];
+    float dmv[MOD == kModSoftcap ? KB * 16 : 1];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float dmod;
+        tt[kb * 16 + r] = mod_score<MOD>(s[kb][r], p.va, slope2, tab, kidx - q_pos, dmod);
+        if constexpr (MOD == kModSoftcap) dmv[kb * 16 + r] = dmod;
+      }
+    if (!full) {
+      const float ninf = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          bool ok = kidx < p.Skv;
+          ok &= !(p.mask_kind & kMaskCausal) | (q_pos >= kidx) | (kidx < p.va.prefix);
+          ok &= !(p.mask_kind & kMaskWindow) | (q_pos - kidx < p.va.window);
+          if constexpr (DOCS) {
+            const int lab = __builtin_amdgcn_raw_buffer_load_b32(rdoc, static_cast<unsigned>(kidx) * 4u, 0, 0);
+            ok &= lab == doc_q;
+          }
+          mask_in_place(tt[kb * 16 + r], __builtin_amdgcn_ballot_w64(ok), ninf);
+        }
+    }
     bf16x8 dsf[CH];
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
@@ -308,21 +356,9 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int r = r0 + 2 * jj + x;
-          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          float dmod;
-          float tt = mod_score<MOD>(s[kb][r], p.va, slope2, tab, kidx - q_pos, dmod);
-          if (!full) {
-            bool ok = kidx < p.Skv;
-            ok &= !(p.mask_kind & kMaskCausal) | (q_pos >= kidx) | (kidx < p.va.prefix);
-            ok &= !(p.mask_kind & kMaskWindow) | (q_pos - kidx < p.va.window);
-            if constexpr (DOCS) {
-              const int lab = __builtin_amdgcn_raw_buffer_load_b32(rdoc, static_cast<unsigned>(kidx) * 4u, 0, 0);
-              ok &= lab == doc_q;
-            }
-            tt = ok ? tt : -INFINITY;
-          }
-          const float pr = __builtin_amdgcn_exp2f(tt - lse2);
-          v2[x] = pr * (dp[kb][r] - delta) * dmod;
+          const float pr = __builtin_amdgcn_exp2f(tt[kb * 16 + r] - lse2);
+          v2[x] = pr * (dp[kb][r] - delta);
+          if constexpr (MOD == kModSoftcap) v2[x] *= dmv[kb * 16 + r];
         }
         w[jj] = pack_bf16(v2[0], v2[1]);
       }
@@ -330,25 +366,25 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
       dsf[ch] = __builtin_bit_cast(bf16x8, wv);
     }
 
-    // dQ^T += K^T dS^T
+    // the previous stage's dQ products (at t = 0 zero fragments on stage 0's
+    // rows, which add exactly nothing)
+    dq_products(t == 0 ? 0 : (t - 1) % kRing4);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int ch = 0; ch < CH; ++ch)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(kb_, toff_at(db, 0), toff_at(db, 1), ch),
-                                                         dsf[ch], dq[db], 0, 0, 0);
+    for (int ch = 0; ch < CH; ++ch) {
+      asm volatile("" ::"v"(dsf[ch]));   // keeps dS in the products' block
+      dsf_prev[ch] = dsf[ch];
+    }
 
-    // stage t + 2 into the slot stage t - 1 used; retire stage t + 1
-    const int ring2 = ring == 0 ? kRing - 1 : ring - 1;
+    // stage t + 2 into the slot stage t - 2 used; retire stage t + 1
     if (t + 2 < T) {
-      copy_stage(t + 2, ring2);
+      copy_stage(t + 2, (t + 2) % kRing4);
       wait_vm<2 * G::kDma>();
     } else {
       wait_vm<0>();
     }
     __syncthreads();
-    ring = ring == kRing - 1 ? 0 : ring + 1;
   }
+  if (T > 0) dq_products((T - 1) % kRing4);
 
   if (q_ok) {
     __bf16* const drow = static_cast<__bf16*>(p.dq) + b * p.q_sb + h * p.q_sh + static_cast<size_t>(q_row) * p.q_sr;
