@@ -447,9 +447,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       // The causal part (with its prefix), the window and the key range each
       // admit an interval of key positions for this row, so together they
       // admit keys kk0 + c for c in [lo, hi], where element (kb, i, e) of this
-      // lane is key kk0 + c with c = 32 kb + 8 i + e. Bounds are formed in 64
-      // bits and clamped to the stage, then every element takes two compares
-      // against a constant (and the document test against staged labels).
+      // lane is key kk0 + c with c = 32 kb + 8 i + e (0 <= c <= kBN - 5).
+      // Bounds are formed in 64 bits and clamped to the stage.
       const bool causal = p.mask_kind & kMaskCausal;
       const bool window = p.mask_kind & kMaskWindow;
       const int kk0 = kv0 + 4 * g;
@@ -459,22 +458,53 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       const long long lo = window ? d - p.va.window + 1 : 0LL;
       int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBN)));
       int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
-      asm("" : "+v"(hi_c), "+v"(lo_c));   // compare the clamped 32-bit bounds
-      const int* lab = labbuf + (DOCS ? ring * kBN + 4 * g : 0);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4 l4 = {0u, 0u, 0u, 0u};
-          if constexpr (DOCS) l4 = *reinterpret_cast<const u32x4*>(lab + kb * 32 + 8 * i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = kb * 32 + 8 * i + e;
-            uint64_t ok = __builtin_amdgcn_ballot_w64(c >= lo_c) & __builtin_amdgcn_ballot_w64(c <= hi_c);
-            if constexpr (DOCS) ok &= __builtin_amdgcn_ballot_w64(static_cast<int>(l4[e]) == doc_q);
-            mask_in_place(t[kb * 16 + 4 * i + e], ok, ninf);
-          }
+      // Documents: when the stage's keys all carry one label, a row's label
+      // test has one answer for all of them and is folded into the interval
+      // (a row of another document admits none); otherwise every element
+      // compares its key's staged label with the row's.
+      bool need_doc = false;
+      if constexpr (DOCS) {
+        const int lk = labbuf[ring * kBN + (lane & (kBN - 1))];
+        const int l0 = __builtin_amdgcn_readfirstlane(lk);
+        if (__all(lk == l0)) {
+          if (doc_q != l0) hi_c = -1;
+        } else {
+          need_doc = true;
         }
+      }
+      asm("" : "+v"(hi_c), "+v"(lo_c));   // compare the clamped 32-bit bounds
+      // Each test runs only when some lane of the wave needs it (a stage on
+      // the diagonal needs the upper bound alone, one on the window's far
+      // edge the lower bound alone), as one compare and one select per element.
+      const bool need_lo = !__all(lo_c <= 0);
+      const bool need_hi = !__all(hi_c >= kBN - 1);
+      if (need_doc) {
+        const int* lab = labbuf + ring * kBN + 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 l4 = *reinterpret_cast<const u32x4*>(lab + kb * 32 + 8 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              mask_in_place(t[kb * 16 + 4 * i + e],
+                            __builtin_amdgcn_ballot_w64(static_cast<int>(l4[e]) == doc_q), ninf);
+          }
+      }
+      if (need_lo) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j) {
+          const int c = (j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3);
+          mask_in_place(t[j], __builtin_amdgcn_ballot_w64(c >= lo_c), ninf);
+        }
+      }
+      if (need_hi) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j) {
+          const int c = (j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3);
+          mask_in_place(t[j], __builtin_amdgcn_ballot_w64(c <= hi_c), ninf);
+        }
+      }
     }
     // P = exp2(t) rounded to bf16 into pf; returns this lane's fp32 sum of
     // the unrounded values
