@@ -329,21 +329,55 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
         if constexpr (MOD == kModSoftcap) dmv[kb * 16 + r] = dmod;
       }
     if (!full) {
+      // Element 16 kb + r is key kk0 + c with c = 32 kb + 8 (r / 4) + r % 4.
+      // The key range, the causal part (with its prefix) and the window
+      // admit c in [lo_c, hi_c]; a stage whose keys share one document label
+      // folds the label test into that interval. Each test runs only when
+      // some lane of the wave needs it (one compare and one select per element).
       const float ninf = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          bool ok = kidx < p.Skv;
-          ok &= !(p.mask_kind & kMaskCausal) | (q_pos >= kidx) | (kidx < p.va.prefix);
-          ok &= !(p.mask_kind & kMaskWindow) | (q_pos - kidx < p.va.window);
-          if constexpr (DOCS) {
-            const int lab = __builtin_amdgcn_raw_buffer_load_b32(rdoc, static_cast<unsigned>(kidx) * 4u, 0, 0);
-            ok &= lab == doc_q;
-          }
-          mask_in_place(tt[kb * 16 + r], __builtin_amdgcn_ballot_w64(ok), ninf);
+      const int kk0 = kv0 + 4 * g;
+      const long long d = static_cast<long long>(q_pos) - kk0;
+      long long hi = static_cast<long long>(p.Skv) - 1 - kk0;
+      if (p.mask_kind & kMaskCausal) hi = min(hi, max(d, static_cast<long long>(p.va.prefix) - 1 - kk0));
+      const long long lo = (p.mask_kind & kMaskWindow) ? d - p.va.window + 1 : 0LL;
+      int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kStage)));
+      const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kStage)));
+      bool need_doc = false;
+      if constexpr (DOCS) {
+        const int lk = __builtin_amdgcn_raw_buffer_load_b32(
+            rdoc, static_cast<unsigned>(kv0 + (lane & (kStage - 1))) * 4u, 0, 0);
+        const int l0 = __builtin_amdgcn_readfirstlane(lk);
+        if (__all(lk == l0)) {
+          if (doc_q != l0) hi_c = -1;
+        } else {
+          need_doc = true;
         }
+      }
+      if (need_doc) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 l4 = __builtin_amdgcn_raw_buffer_load_b128(
+                rdoc, static_cast<unsigned>(kk0 + 32 * kb + 8 * i) * 4u, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              mask_in_place(tt[kb * 16 + 4 * i + e],
+                            __builtin_amdgcn_ballot_w64(static_cast<int>(l4[e]) == doc_q), ninf);
+          }
+      }
+      if (!__all(lo_c <= 0)) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j)
+          mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) >= lo_c),
+                        ninf);
+      }
+      if (!__all(hi_c >= kStage - 1)) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j)
+          mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) <= hi_c),
+                        ninf);
+      }
     }
     bf16x8 dsf[CH];
 #pragma unroll
@@ -603,25 +637,57 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
         if constexpr (MOD == kModSoftcap) dmv[qb * 16 + i] = dmod;
       }
     if (!full) {
+      // Element 16 qb + i is query row rr0 + c with c = 32 qb + 8 (i / 4) +
+      // i % 4, at position rr0 + c + off. The query range, the causal part
+      // (keys below the prefix are seen by every row) and the window admit c
+      // in [lo_c, hi_c] (none for a key past Skv); a stage whose rows share
+      // one document label folds the label test into that interval. Each test
+      // runs only when some lane of the wave needs it.
       const float ninf = -INFINITY;
-#pragma unroll
-      for (int qb = 0; qb < KB; ++qb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql0 = 32 * qb + 8 * i4 + 4 * g;
-          u32x4 lab = {0u, 0u, 0u, 0u};
-          if constexpr (DOCS) lab = __builtin_amdgcn_raw_buffer_load_b128(rdoc, static_cast<unsigned>(r0 + ql0 + off) * 4u, 0, 0);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int qrow = r0 + ql0 + x;
-            const int qpos = qrow + off;
-            bool ok = k_ok && qrow < p.Sq;
-            ok &= !causal | (qpos >= k_row) | (k_row < p.va.prefix);
-            ok &= !window | (qpos - k_row < p.va.window);
-            if constexpr (DOCS) ok &= static_cast<int>(lab[x]) == doc_k;
-            mask_in_place(tt[qb * 16 + 4 * i4 + x], __builtin_amdgcn_ballot_w64(ok), ninf);
-          }
+      const int rr0 = r0 + 4 * g;
+      const long long kq = static_cast<long long>(k_row) - off - rr0;   // the row at the key's position
+      long long hi = static_cast<long long>(p.Sq) - 1 - rr0;
+      if (window) hi = min(hi, kq + p.va.window - 1);
+      if (!k_ok) hi = -1;
+      const long long lo = (causal && k_row >= p.va.prefix) ? kq : 0LL;
+      int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kStage)));
+      const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kStage)));
+      bool need_doc = false;
+      if constexpr (DOCS) {
+        const int lq = __builtin_amdgcn_raw_buffer_load_b32(
+            rdoc, static_cast<unsigned>(r0 + off + (lane & (kStage - 1))) * 4u, 0, 0);
+        const int l0 = __builtin_amdgcn_readfirstlane(lq);
+        if (__all(lq == l0)) {
+          if (doc_k != l0) hi_c = -1;
+        } else {
+          need_doc = true;
         }
+      }
+      if (need_doc) {
+#pragma unroll
+        for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const u32x4 lab = __builtin_amdgcn_raw_buffer_load_b128(
+                rdoc, static_cast<unsigned>(rr0 + 32 * qb + 8 * i4 + off) * 4u, 0, 0);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              mask_in_place(tt[qb * 16 + 4 * i4 + x],
+                            __builtin_amdgcn_ballot_w64(static_cast<int>(lab[x]) == doc_k), ninf);
+          }
+      }
+      if (!__all(lo_c <= 0)) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j)
+          mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) >= lo_c),
+                        ninf);
+      }
+      if (!__all(hi_c >= kStage - 1)) {
+#pragma unroll
+        for (int j = 0; j < KB * 16; ++j)
+          mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) <= hi_c),
+                        ninf);
+      }
     }
     bf16x8 pf[CH], dsf[CH];
 #pragma unroll
