@@ -114,6 +114,21 @@ def test_backward_head_dim_256_ragged():
     check(small(B=1, H=2, S=290, D=256, documents=True, mod="alibi", doc_range=(30, 150)), "S=290 D=256 docs alibi")
 
 
+@pytest.mark.parametrize("var", [dict(), dict(causal=True, window=150)],
+                         ids=lambda v: ",".join(f"{a}={b}" for a, b in v.items()) or "plain")
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_backward_recurring_document_labels(var, D):
+    """Run j of the contiguous documents takes label j % 3: equal labels in
+    several separate runs, so label equality alone decides the mask."""
+    import dataclasses
+    inp = small(S=500, D=D, documents=True, doc_range=(20, 140), **var)
+    inp = dataclasses.replace(inp, doc_ids=(inp.doc_ids % 3).astype(np.int32))
+    check(inp, f"recurring labels D={D} {var}")
+    (a, _), (b, _) = run_bwd(inp, "auto"), run_bwd(inp, None)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), var
+
+
 def test_backward_is_reproducible():
     """No atomics: two runs give identical bits."""
     inp = small(B=2, H=4, Hkv=2, S=300, D=128, causal=True)

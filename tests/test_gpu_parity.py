@@ -112,6 +112,29 @@ def test_document_items_longest_first(case):
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
+def recurring_labels(inp, period=3):
+    """The same inputs with document labels that come back: run j of the
+    contiguous documents takes label j % period, so equal labels lie in
+    several separate runs (label equality alone decides the mask)."""
+    import dataclasses
+    return dataclasses.replace(inp, doc_ids=(inp.doc_ids % period).astype(np.int32))
+
+
+@pytest.mark.parametrize("var", [dict(), dict(causal=True), dict(causal=True, window=150),
+                                 dict(causal=True, mod="alibi")],
+                         ids=lambda v: ",".join(f"{k}={x}" for k, x in v.items()) or "plain")
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_recurring_document_labels(var, D):
+    inp = recurring_labels(small(S=700, D=D, documents=True, doc_range=(20, 140), **var))
+    labels = inp.doc_ids[0]
+    starts = np.flatnonzero(np.diff(labels) != 0) + 1
+    assert len(set(labels.tolist())) < len(starts) + 1   # some label spans several runs
+    check_full(inp, "auto", f"recurring labels D={D} {var}")
+    O1, L1 = run_gpu(inp, "auto")
+    O2, L2 = run_gpu(inp, None)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
 def test_repeat_runs_are_bitwise_equal():
     inp = small(S=700, D=128, causal=True, mod="alibi", H=4, Hkv=2)
     O1, L1 = run_gpu(inp)
