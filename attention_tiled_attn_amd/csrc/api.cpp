@@ -84,6 +84,9 @@ int check_mask_args(int mask_kind, const flexattn_params* prm, int B, int Sq, in
     const long long need = std::max(static_cast<long long>(Sq) + prm->q_offset, static_cast<long long>(Skv));
     if (prm->doc_stride < need) return FLEXATTN_ERR_ARG;
     if (static_cast<long long>(B) * prm->doc_stride > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
+    // the kernels read a batch row's labels through a buffer descriptor with
+    // 32-bit byte offsets (position * 4)
+    if (prm->doc_stride > INT_MAX / 4) return FLEXATTN_ERR_OVERFLOW;
   }
   return FLEXATTN_OK;
 }

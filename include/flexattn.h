@@ -120,7 +120,8 @@ typedef struct flexattn_params {
   const int* doc_ids;        /* device int32 [B][doc_stride] document label per position,
                                 when the mask has FLEXATTN_MASK_DOCUMENT               */
   int doc_stride;            /* elements per batch row of doc_ids,
-                                >= max(Sq + q_offset, Skv)                            */
+                                >= max(Sq + q_offset, Skv), <= INT_MAX / 4 and
+                                B * doc_stride <= INT_MAX (else ERR_OVERFLOW)          */
   int q_offset;              /* >= 0: position of query row 0 (see "Positions")       */
   int prefix;                /* >= 0 when the mask has FLEXATTN_MASK_PREFIX           */
   const float* rel_bias;     /* device float32 [H][2 * rel_max + 1], 16-byte aligned,

@@ -136,6 +136,7 @@ def P(**kw):
     (dict(mask_kind=4, params=P()), _lib.ERR_NULLPTR),                   # documents, no labels
     (dict(mask_kind=4, params=P(doc_ids=A, doc_stride=100)), _lib.ERR_ARG),  # stride < S
     (dict(mask_kind=4, params=P(doc_ids=A + 2, doc_stride=128)), _lib.ERR_ALIGN),
+    (dict(mask_kind=4, params=P(doc_ids=A, doc_stride=2**29)), _lib.ERR_OVERFLOW),   # byte offsets past 2^31
     (dict(mod_kind=1, params=P()), _lib.ERR_NULLPTR),                    # ALiBi, no slopes
     (dict(mod_kind=1, params=P(alibi_slopes=A + 1)), _lib.ERR_ALIGN),
     (dict(mod_kind=2, params=P(softcap=0.0)), _lib.ERR_ARG),
