@@ -704,8 +704,12 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = i0 + 4 * hv + x;
-          const float lse2 = (l4[x] == -INFINITY) ? INFINITY : l4[x] * kLog2e;
-          const float pr = __builtin_amdgcn_exp2f(tt[qb * 16 + i] - lse2);
+          // exp2(t - log2(e) LSE) as one FMA. A row with no admitted key
+          // has LSE = -inf and every score masked to -inf; its LSE is
+          // clamped (one med3) to -1e30 so that the FMA gives -inf (P = 0),
+          // not NaN.
+          const float lc = __builtin_amdgcn_fmed3f(l4[x], -1e30f, 3e38f);
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(lc, -kLog2e, tt[qb * 16 + i]));
           pv[x] = pr;
           dv4[x] = pr * (dp[qb][i] - d4[x]);
           if constexpr (MOD == kModSoftcap) dv4[x] *= dmv[qb * 16 + i];
