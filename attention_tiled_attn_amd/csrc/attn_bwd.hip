@@ -325,7 +325,10 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
       for (int r = 0; r < 16; ++r) {
         const int kidx = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         float dmod;
-        tt[kb * 16 + r] = mod_score<MOD>(s[kb][r], p.va, slope2, tab, kidx - q_pos, dmod);
+        // without a score mod the row's LSE joins the scale in one FMA (for a
+        // row with no admitted key lse2 = +inf, so P = exp2(-inf) = 0)
+        if constexpr (MOD == kModNone) tt[kb * 16 + r] = __builtin_fmaf(s[kb][r], p.va.c1, -lse2);
+        else tt[kb * 16 + r] = mod_score<MOD>(s[kb][r], p.va, slope2, tab, kidx - q_pos, dmod);
         if constexpr (MOD == kModSoftcap) dmv[kb * 16 + r] = dmod;
       }
     if (!full) {
@@ -390,7 +393,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int r = r0 + 2 * jj + x;
-          const float pr = __builtin_amdgcn_exp2f(tt[kb * 16 + r] - lse2);
+          const float pr = __builtin_amdgcn_exp2f(MOD == kModNone ? tt[kb * 16 + r] : tt[kb * 16 + r] - lse2);
           v2[x] = pr * (dp[kb][r] - delta);
           if constexpr (MOD == kModSoftcap) v2[x] *= dmv[kb * 16 + r];
         }
