@@ -129,6 +129,21 @@ def test_backward_recurring_document_labels(var, D):
         assert torch.equal(x, y), var
 
 
+@pytest.mark.parametrize("mod", ["none", "alibi"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_backward_rows_with_no_admitted_key(mod, D):
+    """300 query rows against 100 keys under documents: the rows whose
+    document has no key are fully masked (LSE = -inf), so their P is 0 and
+    their dQ rows are exactly zero."""
+    inp = small(Sq=300, Skv=100, S=300, D=D, documents=True, doc_range=(20, 60), mod=mod)
+    key_labels = set(inp.doc_ids[0, :100].tolist())
+    empty = [i for i in range(300) if int(inp.doc_ids[0, i]) not in key_labels]
+    assert len(empty) > 100
+    check(inp, f"rows with no admitted key D={D} mod={mod}")
+    (dq, dk, dv), _ = run_bwd(inp)
+    assert torch.count_nonzero(dq[:, :, empty]).item() == 0
+
+
 def test_backward_is_reproducible():
     """No atomics: two runs give identical bits."""
     inp = small(B=2, H=4, Hkv=2, S=300, D=128, causal=True)
