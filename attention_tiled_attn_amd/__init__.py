@@ -26,7 +26,7 @@ __all__ = [
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
     "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError", "attention_backward",
     "flexattn_decode", "flexattn_decode_splits", "flexattn_decode_workspace_bytes", "decode",
-    "flexattn_split_count",
+    "flexattn_split_count", "check_variant", "non_overlapping",
 ]
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
@@ -78,6 +78,63 @@ def set_layout(p: Params, q, k, v, out) -> None:
         getattr(p, f"{name}_stride")[:] = [t.stride(0), t.stride(1), t.stride(2)]
 
 
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(t: torch.Tensor, device) -> bool:
+    device = torch.device(device)
+    if t.device.type != device.type:
+        return False
+    return device.index is None or t.device.index is None or t.device.index == device.index
+
+
+def check_variant(var: Variant, B: int, H: int | None, Sq: int, Skv: int, device) -> None:
+    """Check the variant's device tensors against the call's sizes. The C ABI
+    receives them as bare pointers and cannot see their extents, so a short
+    tensor would be read past its end on the device; this is the one place
+    that can reject it."""
+    need_pos = max(Sq + int(var.q_offset), Skv)
+    if var.doc_ids is not None:
+        d = var.doc_ids
+        _need(d.dtype == torch.int32 and d.is_contiguous() and d.dim() == 2,
+              "doc_ids must be a contiguous int32 [B, positions] tensor")
+        _need(_same_device(d, device), "doc_ids must be on the device of q")
+        _need(d.shape[0] >= B, f"doc_ids has {d.shape[0]} rows, the call has B = {B}")
+        _need(d.shape[1] >= need_pos,
+              f"doc_ids rows hold {d.shape[1]} labels, the call needs {need_pos} (max(Sq + q_offset, Skv))")
+    if H is None:
+        return
+    if var.alibi_slopes is not None:
+        a = var.alibi_slopes
+        _need(a.dtype == torch.float32 and a.is_contiguous() and a.dim() == 1,
+              "alibi_slopes must be a contiguous float32 [H] tensor")
+        _need(_same_device(a, device), "alibi_slopes must be on the device of q")
+        _need(a.numel() >= H, f"alibi_slopes has {a.numel()} entries, the call has H = {H}")
+    if var.rel_bias is not None:
+        r = var.rel_bias
+        _need(r.dtype == torch.float32 and r.is_contiguous() and r.dim() == 2,
+              "rel_bias must be a contiguous float32 [H, 2R + 1] tensor")
+        _need(_same_device(r, device), "rel_bias must be on the device of q")
+        _need(r.shape[0] >= H, f"rel_bias has {r.shape[0]} rows, the call has H = {H}")
+        _need(r.shape[1] % 2 == 1, f"rel_bias rows must hold an odd count 2R + 1, not {r.shape[1]}")
+
+
+def non_overlapping(t: torch.Tensor) -> bool:
+    """True when no two elements of t share an address (ordered by stride,
+    every dimension longer than 1 steps over the span of those below it: the
+    rule flexattn_bwd applies to the layouts its gradients take)."""
+    span = 1
+    for stride, size in sorted(zip(t.stride(), t.shape)):
+        if size <= 1:
+            continue
+        if stride < span:
+            return False
+        span = stride * size
+    return True
+
+
 def make_params(var: Variant, dtype: torch.dtype) -> Params:
     p = Params()
     if dtype not in _DTYPES:
@@ -125,6 +182,7 @@ def build_block_mask(var: Variant, B: int, Sq: int, Skv: int, device=None,
     if nbytes == 0:
         raise ValueError("invalid sizes or mask kind for a block mask")
     device = device or (var.doc_ids.device if var.doc_ids is not None else torch.device("cuda"))
+    check_variant(var, B, None, Sq, Skv, device)
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
     out = BlockMask()
     flexattn_build_block_mask(mk, make_params(var, torch.bfloat16), B, Sq, Skv, buf, nbytes, out,
@@ -150,6 +208,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | 
             raise TypeError("q, k, v must be 4-D device tensors of one dtype")
     if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("shape mismatch between q, k and v")
+    check_variant(var, B, H, Sq, Skv, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -181,6 +240,9 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, var: Variant | Non
     for t in (q, k, v):
         if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4:
             raise TypeError("q, k, v must be 4-D bf16 device tensors")
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    check_variant(var, B, H, Sq, Skv, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     splits = flexattn_split_count(B, H, Hkv, Sq, Skv) if splits is None else int(splits)
     if out is None:
@@ -222,7 +284,14 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
             raise TypeError("q, k, v, out, dout must be bf16 device tensors")
     if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
         raise ValueError("shape mismatch")
+    check_variant(var, B, H, Sq, Skv, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    # Each gradient takes its input's strides. An input whose elements share
+    # addresses (e.g. K expanded over the batch) is copied first, so that its
+    # gradient gets a layout of its own: the gradient with respect to the
+    # view, one slice per batch row or head (a caller that expanded the
+    # tensor sums them, as autograd does for expand).
+    q, k, v = (t if non_overlapping(t) else t.contiguous() for t in (q, k, v))
 
     def like(t):
         return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
@@ -238,6 +307,8 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     if isinstance(block_mask, str):
         block_mask = build_block_mask(var, B, Sq, Skv, q.device, stream)
     p = make_params(var, q.dtype)
+    if not non_overlapping(out):
+        raise ValueError("out must not overlap itself (it is the forward's output)")
     set_layout(p, q, k, v, out)
     flexattn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, B, H, Hkv, Sq, Skv, D, scale,
                  var.mask_kind, var.mod_kind, p, block_mask.struct if block_mask is not None else None, stream)

@@ -50,6 +50,24 @@ int check_layout(const Strides& s, int rows, int D, long long esz) {
   return FLEXATTN_OK;
 }
 
+// True when distinct elements [n][heads][rows][D] of a layout never share an
+// address. Sufficient test: ordered by stride, every dimension of extent > 1
+// steps over the whole span of the dimensions below it. The backward writes
+// its gradients with the strides of q, k and v, so a broadcast (stride 0) or
+// otherwise overlapping input would make several workgroups write one element.
+bool non_overlapping(const Strides& s, int n, int heads, int rows, int D) {
+  struct Dim { long long stride, extent; };
+  Dim d[4] = {{1, D}, {s.r, rows}, {s.h, heads}, {s.b, n}};
+  std::sort(d, d + 4, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+  long long span = 1;   // elements covered by the dimensions taken so far
+  for (const Dim& x : d) {
+    if (x.extent <= 1) continue;
+    if (x.stride < span) return false;
+    span = x.stride * x.extent;
+  }
+  return true;
+}
+
 constexpr int kMaskBits = FLEXATTN_MASK_CAUSAL | FLEXATTN_MASK_WINDOW | FLEXATTN_MASK_DOCUMENT |
                           FLEXATTN_MASK_PREFIX;
 
@@ -258,8 +276,6 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   // D = 256 runs on the bf16 ping-pong kernel only
   if (D == 256 && (prm->dtype != FLEXATTN_BF16 || ceil_div(Skv, FLEXATTN_TILE) > fa::kPairMaxKeyTiles))
     return FLEXATTN_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
-  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
 
   fa::FwdLaunch p{};
   p.q = q;
@@ -286,6 +302,9 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
     if (!ls) ls = check_layout(vs, Skv, D, esz);
     if (!ls) ls = check_layout(os, Sq, D, esz);
     if (ls) return ls;
+    if (!non_overlapping(os, B, H, Sq, D)) return FLEXATTN_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
+    if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
     p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
     p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);
     p.v_sb = vs.b; p.v_sh = vs.h; p.v_sr = static_cast<int>(vs.r);
@@ -349,8 +368,6 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
     return FLEXATTN_ERR_UNSUPPORTED;
   if (splits < 1 || splits > 64) return FLEXATTN_ERR_ARG;
   if (static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_QTILE) * splits > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
-  if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
   if (splits > 1) {
     if (!workspace) return FLEXATTN_ERR_NULLPTR;
     if (!aligned(workspace, 16)) return FLEXATTN_ERR_ALIGN;
@@ -381,10 +398,13 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
     if (!ls) ls = check_layout(vs, Skv, D, 2);
     if (!ls) ls = check_layout(os, Sq, D, 2);
     if (ls) return ls;
+    if (!non_overlapping(os, B, H, Sq, D)) return FLEXATTN_ERR_ARG;
     // packed: the rows of a group's rep query heads are addressed from its
     // first head with 32-bit byte offsets
     if (packed && ((rep - 1) * qs.h + static_cast<long long>(Sq + FLEXATTN_QTILE) * qs.r) * 2 > INT_MAX)
       return FLEXATTN_ERR_OVERFLOW;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FLEXATTN_ERR_ALIGN;
+    if (lse && !aligned(lse, 4)) return FLEXATTN_ERR_ALIGN;
     p.q_sb = qs.b; p.q_sh = qs.h; p.q_sr = static_cast<int>(qs.r);
     p.k_sb = ks.b; p.k_sh = ks.h; p.k_sr = static_cast<int>(ks.r);
     p.v_sb = vs.b; p.v_sh = vs.h; p.v_sr = static_cast<int>(vs.r);
@@ -426,6 +446,12 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
     if (!ls) ls = check_layout(vs, Skv, D, 2);
     if (!ls) ls = check_layout(os, Sq, D, 2);
     if (ls) return ls;
+    // dq, dk and dv take the strides of q, k and v: their elements must be
+    // distinct addresses (and out's, which dout shares, for symmetry with
+    // the forward that wrote out)
+    if (!non_overlapping(qs, B, H, Sq, D) || !non_overlapping(ks, B, Hkv, Skv, D) ||
+        !non_overlapping(vs, B, Hkv, Skv, D) || !non_overlapping(os, B, H, Sq, D))
+      return FLEXATTN_ERR_ARG;
   }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))

@@ -5,8 +5,8 @@
 // explainer, "Enter Tri Dao and FlashAttention"); run the softmax online, one key
 // tile at a time, rescaling the running output when the running maximum grows
 // (same page, "FlashAttention-4: Built for Blackwell", forward-pass fixes); split
-// the work over query tiles (same section, and FlashAttention-2's "better
-// parallelism and work partitioning" in "Enter Tri Dao and FlashAttention").
+// the work over query tiles, FlashAttention-2's improvement in how work is
+// divided among parallel units (same page, "Enter Tri Dao and FlashAttention").
 //
 // Mapping to CDNA4:
 //  * A workgroup owns one 128-row query tile of one (batch, head): 4 waves of 64

@@ -53,13 +53,14 @@ enum flexattn_status {
   FLEXATTN_OK = 0,
   FLEXATTN_ERR_NULLPTR = -1,     /* a required pointer is NULL                         */
   FLEXATTN_ERR_SHAPE = -2,       /* B, H, Hkv, Sq, Skv < 1, or H % Hkv != 0            */
-  FLEXATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, mask or mod kind      */
+  FLEXATTN_ERR_UNSUPPORTED = -3, /* D not 64/128/256, unknown dtype, mask or mod kind  */
   FLEXATTN_ERR_ALIGN = -4,       /* Q/K/V/O not 16-byte or LSE/params not 4-byte aligned */
   FLEXATTN_ERR_BLOCKMASK = -5,   /* block mask does not match the call                 */
   FLEXATTN_ERR_OVERFLOW = -6,    /* sizes exceed the 32-bit index range (also: one
                                     (batch, head) slice must stay below 2^31 bytes)    */
   FLEXATTN_ERR_HIP = -7,         /* a HIP call failed; see flexattn_last_error()       */
-  FLEXATTN_ERR_ARG = -8          /* bad scalar argument (scale, window, softcap, size)  */
+  FLEXATTN_ERR_ARG = -8          /* bad scalar argument (scale, window, softcap, size,
+                                    stride; overlapping gradient layouts)              */
 };
 
 /* Element type of Q, K, V and O. LSE is always float32. FP32 inputs are
@@ -132,10 +133,15 @@ typedef struct flexattn_params {
    * contiguous [B][H][S][D] layout; e.g. a [B][S][H][D] buffer viewed as
    * [B][H][S][D] has strides {S*H*D, D, H*D}. Strides are >= 0, a row stride
    * is >= D, and each stride times the element size is a multiple of 16
-   * bytes (else FLEXATTN_ERR_ALIGN). Rows of out must not overlap. LSE is
-   * always contiguous [B][H][Sq]. flexattn_bwd applies the same strides to
-   * the gradients: dq takes q_stride, dk k_stride, dv v_stride and dout
-   * o_stride; rows of dq, dk and dv must not overlap.                        */
+   * bytes (else FLEXATTN_ERR_ALIGN). LSE is always contiguous [B][H][Sq].
+   * flexattn_bwd applies the same strides to the gradients: dq takes
+   * q_stride, dk k_stride, dv v_stride and dout o_stride.
+   * Every layout that is written must not overlap: out in every call, and in
+   * flexattn_bwd also q, k and v (whose strides the gradients take). "Not
+   * overlapping" is tested as: ordered by stride, each dimension of extent
+   * > 1 steps over the span of those below it (so no stride 0 over a
+   * dimension longer than 1); else FLEXATTN_ERR_ARG. The forward only reads
+   * q, k and v, so it accepts overlapping (e.g. broadcast) inputs.          */
   long long q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } flexattn_params;
 

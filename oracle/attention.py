@@ -5,14 +5,15 @@ CPU-baseline leg may import this module. The GPU library never calls it and
 shares no code with it.
 
 What it computes. The fused, tiled method reorganises where the work happens
-but makes "no approximations" and changes no result (Neuron FA4 explainer,
-"Enter Tri Dao and FlashAttention"; "zero loss in accuracy" in its TL;DR). So
-the oracle is the unfused definition of attention written out, comparing every
-query with every key (same page, "What Is Attention, and Why Is It
-Expensive?"), with the score modification and the mask that FlexAttention lets a
-user attach to a (query index, key index) pair applied literally (NextVector
-FlexAttention article, body: a function of q_idx and k_idx modifies the score;
-PyTorch FlexAttention FA4-backend post: "score/mask modifications"):
+but approximates nothing, so its result is the plain one and accuracy is not
+traded for speed (Neuron FA4 explainer, "Enter Tri Dao and FlashAttention",
+and its TL;DR). So the oracle is the unfused definition of attention written
+out, comparing every query with every key (same page, "What Is Attention, and
+Why Is It Expensive?"), with the score modification and the mask that
+FlexAttention lets a user attach to a (query index, key index) pair applied
+literally (NextVector FlexAttention article, body: a function of q_idx and
+k_idx modifies the score; PyTorch FlexAttention FA4-backend post: user
+functions that modify scores or mask pairs out):
 
     s[q, j]  = scale * <Q[b, h, q, :], K[b, kvh(h), j, :]>
     s'[q, j] = score_mod(s[q, j], b, h, q, j)

@@ -343,3 +343,31 @@ def dcall(**over):
 ])
 def test_decode_validation(over, code):
     assert dcall(**over) == code
+
+
+# ------------------------------------------------------------------ overlapping layouts
+# GOOD / BGOOD are B=1, H=2 (Hkv=2), S=128, D=64: contiguous head stride 128*64.
+@pytest.mark.parametrize("which,stride,B,code", [
+    ("k", (0, 128 * 64, 64), 2, _lib.ERR_ARG),          # K expanded over the batch: dK rows collide
+    ("v", (0, 128 * 64, 64), 2, _lib.ERR_ARG),
+    ("q", (0, 128 * 64, 64), 2, _lib.ERR_ARG),
+    ("k", (2 * 128 * 64, 0, 64), 1, _lib.ERR_ARG),      # heads share one slice
+    ("q", (2 * 128 * 64, 64, 64), 1, _lib.ERR_ARG),     # head stride inside a row span
+    ("o", (2 * 128 * 64, 0, 64), 1, _lib.ERR_ARG),      # out (and dout) overlapping
+    ("k", (0, 128 * 64, 64), 1, _lib.ERR_ALIGN),        # stride 0 over B = 1 is no overlap
+    ("k", (64 * 128, 64, 64 * 2), 1, _lib.ERR_ALIGN),   # [B, S, H, D] view: distinct elements
+])
+def test_bwd_rejects_overlapping_layouts(which, stride, B, code):
+    # the calls that pass the overlap rule stop at the misaligned dq after it
+    assert bcall(B=B, params=P(**{which + "_stride": stride}), dq=A + 2) == code
+
+
+@pytest.mark.parametrize("which,stride,code", [
+    ("o", (2 * 128 * 64, 0, 64), _lib.ERR_ARG),     # two heads written to one slice
+    ("o", (2 * 128 * 64, 128 * 64, 0), _lib.ERR_ARG),   # row stride below D
+    ("q", (2 * 128 * 64, 0, 64), _lib.ERR_ALIGN),   # inputs may overlap: read only
+    ("k", (0, 0, 64), _lib.ERR_ALIGN),
+])
+def test_fwd_overlap_rule_applies_to_out_only(which, stride, code):
+    assert call(params=P(**{which + "_stride": stride}), lse=A + 2) == code
+    assert dcall(params=P(**{which + "_stride": stride}), lse=A + 2) == code

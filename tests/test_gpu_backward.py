@@ -234,3 +234,36 @@ def test_backward_full_size_one_group(name, b, kvh):
         assert rmax <= REL_MAX and rmean <= REL_MEAN, (name, nm, rmax, rmean)
     for t in (dq, dk, dv):
         assert not torch.isnan(t).any().item()
+
+
+# ------------------------------------------------------------------ broadcast (overlapping) inputs
+def test_backward_expanded_kv():
+    """K and V expanded over the batch (stride 0): the C ABI refuses the
+    layout for the gradients (they would collide), and the binding copies
+    such inputs first, giving the per-batch gradients of the view, bit for
+    bit those of the contiguous call."""
+    inp = small(B=3, H=4, Hkv=2, S=150, D=64, causal=True)
+    wl = inp.wl
+    q = inp.q.cuda()
+    k1, v1 = inp.k[:1].cuda(), inp.v[:1].cuda()
+    kb, vb = k1.expand(3, -1, -1, -1), v1.expand(3, -1, -1, -1)
+    assert kb.stride(0) == 0 and not fa.non_overlapping(kb)
+    var = fa.Variant(causal=True)
+    out, lse = fa.attention(q, kb, vb, var, scale=wl.scale)
+    dout = draw_dout(wl.B, wl.H, wl.Sq, wl.D, 5).to(torch.bfloat16).cuda()
+    # the raw entry point with the expanded strides: rejected before any launch
+    p = fa.make_params(var, torch.bfloat16)
+    fa.set_layout(p, q, kb, vb, out)
+    dk = torch.empty(1, 2, 150, 64, dtype=torch.bfloat16, device="cuda").expand(3, -1, -1, -1)
+    dq, dv = torch.empty_like(q), torch.empty_like(dk)
+    delta = torch.empty(3, 4, 150, dtype=torch.float32, device="cuda")
+    st = fa.flexattn_bwd(q, kb, vb, out, lse, dout, dq, dk, dv, delta, 3, 4, 2, 150, 150, 64, wl.scale,
+                         var.mask_kind, var.mod_kind, p, None, check=False)
+    assert st == fa._lib.ERR_ARG
+    # the binding: gradients of the view, equal to the contiguous call's
+    got = fa.attention_backward(q, kb, vb, out, lse, dout, var, scale=wl.scale)
+    ref = fa.attention_backward(q, kb.contiguous(), vb.contiguous(), out, lse, dout, var, scale=wl.scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert fa.non_overlapping(a), name
+        assert torch.equal(a, b), name

@@ -9,8 +9,8 @@ The pages name the variants (sliding window, document packing, ALiBi,
 soft-capping: Neuron FA4 explainer, "PyTorch Gets the Upgrade Too"; NextVector
 FlexAttention article, "What Happened?") but give no shapes and no data set; the
 shapes, seeds and distributions below are synthetic stand-ins of the workloads
-the method is benchmarked on ("compute-bound workloads": PyTorch FlexAttention
-FA4-backend post).
+the method is benchmarked on (workloads limited by arithmetic rather than
+memory traffic: PyTorch FlexAttention FA4-backend post).
 """
 from __future__ import annotations
 
