@@ -15,11 +15,13 @@
 // classified exactly from the rectangle's corners. Under a prefix-LM mask the
 // keys below the prefix drop the causal part: a tile is split at the prefix
 // and each side classified exactly, the tile being full when both sides are
-// and empty when both are. The document
-// part is classified from the label ranges of the query rows and of the keys;
-// where they cannot tell "empty" from "partial" the tile is kept as partial.
-// Keys at or past Skv never count as admitted, so a tile that reaches past Skv
-// is at most partial.
+// and empty when both are. The document part is classified from the label
+// ranges of the query rows and of the keys where those decide it (disjoint
+// ranges: empty; one shared label: the positional class); the pairs they
+// leave open are decided exactly by a test over the key tile's label runs.
+// So every class equals the one a pair-by-pair test would give. Keys at or
+// past Skv never count as admitted, so a tile that reaches past Skv is at
+// most partial.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -55,6 +57,48 @@ __device__ inline void label_range(const int* doc, int lo, int hi, int lane, int
   mx = wave_max(b);
 }
 
+// Exact "empty or partial" test of one (128-row half, key tile) pair under a
+// document mask, by the whole wave. Every mask part but the documents admits,
+// for a query at position q, one interval of key positions: from
+// q - window + 1 (window) or 0, up to max(q, prefix - 1) (causal, with the
+// prefix-LM relaxation: k <= q or k < prefix) or Skv - 1. The lane's rows
+// carry their labels lab_r[] and intervals [lo_r[], hi_r[]] (an empty
+// interval for a row past Sq). The tile's keys fall into runs of equal
+// label; a pair is admitted iff some row's label equals a run's label and its
+// interval meets that run. Lanes hold keys ka + lane and ka + 64 + lane, run
+// starts are found with a ballot, and the runs are walked in order on the
+// scalar unit, so the cost is a few instructions per run, not per pair.
+__device__ bool half_tile_has_pair(const int* doc, int ka, int kb, int lane, const int (&lab_r)[2],
+                                   const int (&lo_r)[2], const int (&hi_r)[2]) {
+  const int n = kb - ka + 1;   // keys in the tile (1..128)
+  const bool in0 = lane < n, in1 = lane + 64 < n;
+  const int l0 = in0 ? doc[ka + lane] : 0;
+  const int l1 = in1 ? doc[ka + 64 + lane] : 0;
+  // label of the key before each of the lane's two keys
+  const int prev0 = __shfl(l0, lane == 0 ? 0 : lane - 1);
+  const int prev1 = lane == 0 ? __shfl(l0, 63) : __shfl(l1, lane - 1);
+  uint64_t s0 = __ballot(in0 && (lane == 0 || l0 != prev0));
+  uint64_t s1 = __ballot(in1 && l1 != prev1);
+  bool hit = false;
+  while (s0 | s1) {
+    int st;
+    if (s0) {
+      st = __builtin_ctzll(s0);
+      s0 &= s0 - 1;
+    } else {
+      st = 64 + __builtin_ctzll(s1);
+      s1 &= s1 - 1;
+    }
+    const int nx = s0 ? __builtin_ctzll(s0) : s1 ? 64 + __builtin_ctzll(s1) : n;
+    const int label = st < 64 ? __builtin_amdgcn_readlane(l0, st) : __builtin_amdgcn_readlane(l1, st - 64);
+    const int rs = ka + st, re = ka + nx - 1;   // the run's key positions
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      hit = hit || (lab_r[i] == label && max(lo_r[i], rs) <= min(hi_r[i], re));
+  }
+  return __ballot(hit) != 0;
+}
+
 // One wave per (batch row, 256-row query tile); each lane classifies one key
 // tile (64 per pass) for both 128-row halves, and the non-empty tiles are
 // compacted in order with a ballot.
@@ -63,8 +107,9 @@ __device__ inline void label_range(const int* doc, int lo, int hi, int lane, int
 // Documents: with the label ranges of the half's rows [dq_min, dq_max] and of
 // the tile's keys [dk_min, dk_max], disjoint ranges mean empty and one shared
 // label means cls_d. A full tile needs every pair to share its label, which
-// the ranges decide exactly, so "full" is never given wrongly; the one
-// question they leave open is "empty or partial", answered "partial".
+// the ranges decide exactly. Ranges that overlap without one shared label
+// leave "empty or partial" open (never "full": some pair then has two
+// labels); half_tile_has_pair decides those pairs.
 __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
   const int qp = blockIdx.x;
   const int bb = blockIdx.y;
@@ -92,6 +137,26 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
   const long long lo_p = -(1LL << 40);
   const long long hi_d = window ? static_cast<long long>(p.window) - 1 : (1LL << 40);
   const int prefix = causal ? p.prefix : 0;
+
+  // for the exact document test: rows r_lo + lane and r_lo + 64 + lane of
+  // each half, with their labels and admitted key intervals
+  int lab_r[2][2] = {{0, 0}, {0, 0}}, lo_r[2][2], hi_r[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = qp * 2 * kTile + hf * kTile + 64 * i + lane;
+      lo_r[hf][i] = 1;   // empty interval unless the row exists
+      hi_r[hf][i] = 0;
+      if (docs && row < p.Sq) {
+        const int q = row + p.q_offset;
+        lab_r[hf][i] = doc[q];
+        const long long lo = window ? static_cast<long long>(q) - p.window + 1 : 0;
+        const long long hi = causal ? max(q, prefix - 1) : p.Skv - 1;
+        lo_r[hf][i] = static_cast<int>(max(lo, 0LL));
+        hi_r[hf][i] = static_cast<int>(min(hi, static_cast<long long>(p.Skv) - 1));
+      }
+    }
   // class of rows [qa, qb] x keys [ka, kb] under d in [lo, hi]
   auto rect = [&](int qa, int qb, int ka, int kb, long long lo) -> int {
     const long long dmin = static_cast<long long>(qa) - kb;
@@ -155,14 +220,23 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
       }
     }
 
-    // Ranges that overlap without one shared label leave "empty or partial"
-    // open; such a tile is kept as partial. The per-element mask then decides
-    // every pair of it, so results are unchanged (a visited tile with no
-    // admitted pair adds exactly nothing); only its compute may be spent
-    // in vain. Testing its pairs here cost more than computing it.
+    // Pairs the label ranges leave open: decided one by one, by the whole
+    // wave, walking the open (tile, half) pairs of this pass in order.
+    if (docs) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      if (cls[hf] == kUnknown) cls[hf] = kPartial;
+      for (int hf = 0; hf < 2; ++hf) {
+        uint64_t open = __ballot(cls[hf] == kUnknown);
+        uint64_t found = 0;
+        while (open) {
+          const int j = __builtin_ctzll(open);
+          open &= open - 1;
+          const int ka = (kt0 + j) * kTile;
+          const int kb = min(p.Skv, ka + kTile) - 1;
+          if (half_tile_has_pair(doc, ka, kb, lane, lab_r[hf], lo_r[hf], hi_r[hf])) found |= 1ull << j;
+        }
+        if (cls[hf] == kUnknown) cls[hf] = ((found >> lane) & 1) ? kPartial : kEmpty;
+      }
+    }
 
     int bits = 0;
 #pragma unroll

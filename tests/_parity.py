@@ -35,48 +35,14 @@ def pair_lists(ref: np.ndarray) -> list[list[int]]:
     return out
 
 
-def check_pair_lists(counts: np.ndarray, lists: np.ndarray, ref: np.ndarray, Sq: int, Skv: int,
-                     doc_row: np.ndarray | None = None, q_offset: int = 0) -> int:
-    """Check the block-mask lists of one batch row against per-(128-row tile,
-    128-key tile) classes `ref` (0 empty, 1 partial, 2 full). Without documents
-    the lists must equal pair_lists(ref). With documents, full and partial
-    halves must match exactly, and a half the oracle finds empty may be listed
-    as partial only when the label range of its rows overlaps that of the
-    tile's keys without both being one single label. Returns the number of
-    such extra partial halves."""
-    if doc_row is None:
-        for qp, want in enumerate(pair_lists(ref)):
-            assert lists[qp, :counts[qp]].tolist() == want, qp
-        return 0
-    extra = 0
-    nq128, nk = ref.shape
-    for qp in range((nq128 + 1) // 2):
-        got = {}
-        entries = lists[qp, :counts[qp]].tolist()
-        assert entries == sorted(entries), qp
-        for e in entries:
-            got[e >> 4] = e & 0xF
-        for j in range(nk):
-            bits = got.get(j, 0)
-            for hf in range(2):
-                qt = 2 * qp + hf
-                g = (bits >> (2 * hf)) & 3          # 0 empty, 1 partial, 3 full
-                o = int(ref[qt, j]) if qt < nq128 else 0
-                if o == 2:
-                    assert g == 3, (qp, j, hf)
-                elif o == 1:
-                    assert g == 1, (qp, j, hf)
-                else:
-                    assert g in (0, 1), (qp, j, hf)
-                    if g == 1:
-                        ql = doc_row[qt * 128 + q_offset:min(Sq, qt * 128 + 128) + q_offset]
-                        kl = doc_row[j * 128:min(Skv, j * 128 + 128)]
-                        overlap = ql.min() <= kl.max() and kl.min() <= ql.max()
-                        single = ql.min() == ql.max() == kl.min() == kl.max()
-                        assert overlap and not single, (qp, j, hf)
-                        extra += 1
-            assert (bits != 0) == (j in got), (qp, j)
-    return extra
+def check_pair_lists(counts: np.ndarray, lists: np.ndarray, ref: np.ndarray) -> None:
+    """Assert that the block-mask lists of one batch row equal the lists that
+    per-(128-row tile, 128-key tile) classes `ref` (0 empty, 1 partial, 2
+    full; from the oracle's pair-by-pair test) give: every key tile, its
+    order and both halves' classes, bit for bit (index work is exact)."""
+    for qp, want in enumerate(pair_lists(ref)):
+        got = lists[qp, :counts[qp]].tolist()
+        assert got == want, (qp, [e for e in got if e not in want][:8], [e for e in want if e not in got][:8])
 
 
 def device_variant(inp: Inputs, device="cuda") -> fa.Variant:
@@ -120,6 +86,14 @@ def run_oracle(inp: Inputs, rows=None, heads=None):
     return oracle.attention(q, k, v, inp.wl.scale, rows=rows, heads=heads, **oracle_kwargs(inp))
 
 
+def run_oracle_full(inp: Inputs, heads=None, stats=None):
+    """The oracle over whole tensors (every batch row, head and query row
+    unless `heads` is given), in a pool of host processes."""
+    from oracle.pool import attention_parallel
+    q, k, v = (bf16_values(t) for t in (inp.q, inp.k, inp.v))
+    return attention_parallel(q, k, v, inp.wl.scale, heads=heads, stats=stats, **oracle_kwargs(inp))
+
+
 def compare(O, L, Oref, Lref, what=""):
     """Assert the GPU result (numpy float64) matches the oracle."""
     assert not np.isnan(O).any(), f"{what}: NaN in O"
@@ -142,14 +116,18 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0) -> np.ndarray:
-    """Query rows for sampled checks at full size: both ends, tile edges, the
-    middle, document boundaries, and seeded random rows."""
+def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0, n_ends: int = 0) -> np.ndarray:
+    """Query rows for sampled checks at full size: both ends (the first and
+    last `n_ends` rows), tile edges, the middle, document boundaries, and
+    seeded random rows."""
     S = wl.Sq
     r = {0, 1, 2, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 1}
+    r.update(range(min(n_ends, S)))
+    r.update(range(max(0, S - n_ends), S))
+    r.update(x for t in range(256, S, 256) for x in (t - 1, t))
     if inp.doc_ids is not None:
         starts = np.flatnonzero(np.diff(inp.doc_ids[0]) != 0) + 1
-        for s in starts[:6]:
+        for s in starts:
             r.update({int(s) - 1, int(s), int(s) + 1})
     r.update(np.random.default_rng(seed).integers(0, S, n_random).tolist())
     return np.array(sorted(x for x in r if 0 <= x < S))
@@ -189,5 +167,5 @@ class _SqSkv:
         return getattr(self._wl, name)
 
 
-__all__ = ["run_gpu", "run_oracle", "compare", "to_np", "sample_rows", "small", "make_inputs",
+__all__ = ["run_gpu", "run_oracle", "run_oracle_full", "compare", "to_np", "sample_rows", "small", "make_inputs",
            "device_variant", "oracle_kwargs"]

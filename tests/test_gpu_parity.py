@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Small shapes are compared element by element over the whole output; the full
-workload sizes are compared on sampled query rows the oracle computes one by
-one. Tolerances: O max-abs 2e-2 and mean-abs 2e-3, LSE 1e-3; rows with no
+Small shapes and the full-size workloads are compared element by element over
+the whole output (the full sizes against the oracle run in a pool of host
+processes); the four long-context workloads, whose oracle would take tens of
+minutes each, on a stratified sample of query rows. Tolerances: O max-abs 2e-2 and mean-abs 2e-3, LSE 1e-3; rows with no
 admitted key must be O = 0 and LSE = -inf on both sides.
 """
 import sys
@@ -14,7 +15,7 @@ import torch
 import attention_tiled_attn_amd as fa
 import oracle
 from tests._parity import (check_pair_lists, compare, device_variant, make_inputs, run_gpu, run_oracle,
-                           sample_rows, small, to_np)
+                           run_oracle_full, sample_rows, small, to_np)
 from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +36,17 @@ def check_full(inp, block_mask="auto", what=""):
 
 # ------------------------------------------------------------------ the tiny workload, whole
 def test_tiny_causal_fp32():
-    check_full(make_inputs(WORKLOADS["tiny_causal"]), what="tiny_causal")
+    inp = make_inputs(WORKLOADS["tiny_causal"])
+    check_full(inp, what="tiny_causal")
+    # Reported, not gated: the kernel rounds the fp32 inputs to bf16 on load
+    # (both products run on bf16 matrix cores), so the distance to the oracle
+    # on the unrounded fp32 values holds that input rounding too.
+    O, L = run_gpu(inp)
+    q, k, v = (t.double().numpy() for t in (inp.q, inp.k, inp.v))
+    Oref, Lref = oracle.attention(q, k, v, inp.wl.scale, causal=True)
+    e = np.abs(to_np(O) - Oref)
+    print(f"[parity] tiny_causal fp32 vs oracle on unrounded fp32 inputs: O max-abs {e.max():.3e} "
+          f"mean-abs {e.mean():.3e}, LSE max-abs {np.abs(to_np(L) - Lref).max():.3e} (not gated)")
 
 
 # ------------------------------------------------------------------ shapes x variants
@@ -236,7 +247,7 @@ def test_block_mask_offset_and_prefix(case):
         doc_row = None if inp.doc_ids is None else inp.doc_ids[b]
         ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
                                   doc_row=doc_row, q_offset=wl.q_offset, prefix=wl.prefix)
-        check_pair_lists(counts[b], lists[b], ref, wl.Sq, wl.Skv, doc_row, wl.q_offset)
+        check_pair_lists(counts[b], lists[b], ref)
 
 
 # ------------------------------------------------------------------ block-mask builder
@@ -256,7 +267,7 @@ def test_block_mask_matches_tile_classes(case):
         doc_row = None if inp.doc_ids is None else inp.doc_ids[b]
         ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
                                   doc_row=doc_row)
-        check_pair_lists(counts[b], lists[b], ref, wl.Sq, wl.Skv, doc_row)
+        check_pair_lists(counts[b], lists[b], ref)
 
 
 def test_block_mask_document_workload_full_size():
@@ -266,32 +277,83 @@ def test_block_mask_document_workload_full_size():
     torch.cuda.synchronize()
     counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
     ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=True, window=wl.window, doc_row=inp.doc_ids[0])
-    n_full = n_part = 0
-    extra = check_pair_lists(counts[0], lists[0], ref, wl.Sq, wl.Skv, inp.doc_ids[0])
-    n_full = int((ref == 2).sum())
-    n_part = int((ref == 1).sum())
-    say(f"[blockmask] doc_swa: {n_full} full + {n_part} partial half-tiles of {ref.size}; "
-        f"{extra} empty half-tiles listed as partial")
+    check_pair_lists(counts[0], lists[0], ref)
+    say(f"[blockmask] doc_swa: {int((ref == 2).sum())} full + {int((ref == 1).sum())} partial "
+        f"half-tiles of {ref.size}, lists equal to the oracle's classes")
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled rows
-@pytest.mark.parametrize("name", ["dense", "causal_gqa", "causal_gqa_shard8", "doc_swa", "alibi_d64",
-                                  "alibi_d128", "softcap_d64", "softcap_d128", "prefix_lm",
-                                  "chunked_prefill", "relbias", "causal_gqa_d256"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("case", [
+    dict(S=1300), dict(S=1300, causal=True), dict(S=1300, causal=True, window=256),
+    dict(S=900, window=200), dict(Sq=500, Skv=1100, q_offset=600, causal=True),
+    dict(S=1000, causal=True, prefix=300), dict(S=1000, causal=True, prefix=300, window=200),
+    dict(Sq=333, Skv=777, q_offset=100, window=150, B=2),
+], ids=lambda c: ",".join(f"{k}={x}" for k, x in c.items()))
+@pytest.mark.parametrize("period,runs", [(3, (50, 400)), (2, (5, 40)), (4, (1, 3))],
+                         ids=["long runs", "short runs", "runs of 1-3"])
+def test_block_mask_recurring_labels_exact(case, period, runs):
+    """Labels that come back in separate runs (run j takes label j % period):
+    the label ranges of a half and a key tile overlap without deciding
+    whether a pair is admitted, and the builder's exact test must give the
+    oracle's classes."""
+    inp = recurring_labels(small(documents=True, doc_range=runs, **case), period)
+    wl = inp.wl
+    bm = fa.build_block_mask(device_variant(inp), wl.B, wl.Sq, wl.Skv)
+    torch.cuda.synchronize()
+    counts, lists = bm.counts().cpu().numpy(), bm.lists().cpu().numpy()
+    for b in range(counts.shape[0]):
+        ref = oracle.tile_classes(wl.Sq, wl.Skv, 128, causal=wl.causal, window=wl.window or None,
+                                  doc_row=inp.doc_ids[b], q_offset=wl.q_offset, prefix=wl.prefix)
+        check_pair_lists(counts[b], lists[b], ref)
+
+
+# ------------------------------------------------------------------ full-size workloads
+# Every element of O and LSE, against the oracle run over the whole tensors in
+# a pool of host processes (tens of seconds on the host), in the launch
+# configuration the benchmark times (the library's own block mask).
+WHOLE = ["dense", "causal_gqa", "doc_swa", "causal_gqa_shard8", "prefix_lm", "chunked_prefill",
+         "relbias", "causal_gqa_d256"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", WHOLE)
+def test_full_size_whole(name):
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
-    say(f"[parity] full-size {name}")
+    say(f"[parity] full-size {name}, whole tensors: gpu")
     O, L = run_gpu(inp)
-    rows = sample_rows(wl, inp)
-    heads = sorted({0, wl.H // 2, wl.H - 1})
-    Oref, Lref = run_oracle(inp, rows=rows, heads=heads)
-    idx = torch.as_tensor(rows, device=O.device)
-    Og, Lg = to_np(O[:, heads][:, :, idx]), to_np(L[:, heads][:, :, idx])
-    stats = compare(Og, Lg, Oref[:, heads], Lref[:, heads], name)
-    say(f"[parity] {name}: {stats}")
     # every element written (outputs were NaN-filled)
     assert not torch.isnan(O).any().item() and not torch.isnan(L).any().item()
+    Og, Lg = to_np(O), to_np(L)
+    del O, L
+    st = {}
+    Oref, Lref = run_oracle_full(inp, stats=st)
+    stats = compare(Og, Lg, Oref, Lref, name)
+    say(f"[parity] {name}: {stats}; oracle {st['seconds']:.1f} s on {st['workers']} processes")
+
+
+# The four long-context workloads hold 34e9 scores each (17-35 TFLOP of fp64
+# products); the oracle would take tens of minutes per workload. They are
+# compared on a stratified row sample instead: the first and last 512 rows,
+# every 256-row tile edge, 1024 seeded random rows, on 4 heads spread over H.
+STRATIFIED = ["alibi_d64", "alibi_d128", "softcap_d64", "softcap_d128"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", STRATIFIED)
+def test_full_size_stratified(name):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    say(f"[parity] full-size {name}, stratified rows: gpu")
+    O, L = run_gpu(inp)
+    assert not torch.isnan(O).any().item() and not torch.isnan(L).any().item()
+    rows = sample_rows(wl, inp, n_random=1024, n_ends=512)
+    heads = sorted({0, wl.H // 3, (2 * wl.H) // 3, wl.H - 1})
+    idx = torch.as_tensor(rows, device=O.device)
+    Og, Lg = to_np(O[:, heads][:, :, idx]), to_np(L[:, heads][:, :, idx])
+    del O, L
+    Oref, Lref = run_oracle(inp, rows=rows, heads=heads)
+    stats = compare(Og, Lg, Oref[:, heads], Lref[:, heads], name)
+    say(f"[parity] {name}: {len(rows)} rows x {len(heads)} heads: {stats}")
 
 
 # ------------------------------------------------------------------ strided layouts

@@ -81,8 +81,8 @@ def test_pair_lists_from_tile_classes():
 
 
 def test_check_pair_lists_contract():
-    """The document-mask checker accepts a listed-but-empty half only where the
-    label ranges are inconclusive, and rejects a wrong full/partial class."""
+    """The block-mask checker accepts exactly the oracle's lists and rejects
+    a wrong class, a listed empty half, a missing tile and a wrong order."""
     import numpy as np
     import pytest
     from oracle import tile_classes
@@ -97,11 +97,26 @@ def test_check_pair_lists_contract():
     arr = np.zeros((len(lists), nk), dtype=np.int64)
     for i, x in enumerate(lists):
         arr[i, :len(x)] = x
-    assert check_pair_lists(counts, arr, ref, S, S, doc) == 0
-    # half 1 of query tile 0 (rows 128-255) against key tile 0 (labels 0 and 7):
-    # row labels {1, 7} overlap {0, 7}, so a partial in place of the oracle's class is allowed
-    # only if the oracle says empty; a corrupted full flag is always rejected
+    check_pair_lists(counts, arr, ref)
     bad = arr.copy()
-    bad[0, 0] |= 0x3 << 2
+    bad[0, 0] |= 0x3 << 2                                         # a corrupted full flag
     with pytest.raises(AssertionError):
-        check_pair_lists(counts, bad, ref, S, S, doc)
+        check_pair_lists(counts, bad, ref)
+    # half 1 of query tile 0 (rows 128-255, labels {1, 7}) against key tile 0
+    # (labels {0, 7}): rows 128-139 (label 7) see keys 100-127 (label 7), so
+    # the oracle finds it partial; against key tile 1 it is partial too. A
+    # half the oracle finds empty must not be listed.
+    assert ref[3, 0] == 0                                         # rows 384-511 vs keys 0-127: empty
+    bad = arr.copy()
+    entries = [int(e) for e in bad[1, :counts[1]]]
+    assert all(e >> 4 != 0 for e in entries)
+    bad[1, :counts[1] + 1] = [(0 << 4) | 0x4] + entries           # list key tile 0 for half 1 of tile 1
+    with pytest.raises(AssertionError):
+        check_pair_lists(counts + np.array([0, 1]), bad, ref)
+    bad = arr.copy()                                              # one tile dropped
+    with pytest.raises(AssertionError):
+        check_pair_lists(counts - np.array([0, 1]), bad, ref)
+    bad = arr.copy()                                              # two entries swapped
+    bad[1, [0, 1]] = bad[1, [1, 0]]
+    with pytest.raises(AssertionError):
+        check_pair_lists(counts, bad, ref)
