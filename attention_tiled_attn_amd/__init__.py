@@ -17,7 +17,8 @@ from ._lib import (  # noqa: F401
     BF16, FP32, MASK_CAUSAL, MASK_DOCUMENT, MASK_NONE, MASK_PREFIX, MASK_WINDOW, MOD_ALIBI, MOD_NONE,
     MOD_RELBIAS, MOD_SOFTCAP, QTILE, REL_MAX, TILE, BlockMask, FlexAttnError, Params, flexattn_block_mask_bytes,
     flexattn_build_block_mask, flexattn_bwd, flexattn_decode, flexattn_decode_splits,
-    flexattn_decode_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_split_count,
+    flexattn_decode_static, flexattn_decode_workspace_bytes, flexattn_fwd, flexattn_last_error,
+    flexattn_split_count,
     flexattn_strerror, flexattn_version, lib,
 )
 
@@ -26,7 +27,7 @@ __all__ = [
     "flexattn_last_error", "flexattn_version", "attention", "build_block_mask", "make_params",
     "mask_kind_of", "Variant", "BuiltBlockMask", "FlexAttnError", "attention_backward",
     "flexattn_decode", "flexattn_decode_splits", "flexattn_decode_workspace_bytes", "decode",
-    "flexattn_split_count", "check_variant", "non_overlapping",
+    "flexattn_split_count", "check_variant", "non_overlapping", "flexattn_decode_static",
 ]
 
 _DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}

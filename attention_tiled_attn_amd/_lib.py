@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflexattn
 OK = 0
 ERR_NULLPTR, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN = -1, -2, -3, -4
 ERR_BLOCKMASK, ERR_OVERFLOW, ERR_HIP, ERR_ARG = -5, -6, -7, -8
+ERR_SCRATCH = -9
+STATIC_SCRATCH_BYTES = 64 << 20
 BF16, FP32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOCUMENT, MASK_PREFIX = 0, 1, 2, 4, 8
 MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_RELBIAS = 0, 1, 2, 3
@@ -29,7 +31,7 @@ QTILE = 256
 EXPORTS = ("flexattn_version", "flexattn_strerror", "flexattn_last_error",
            "flexattn_block_mask_bytes", "flexattn_build_block_mask", "flexattn_fwd", "flexattn_bwd",
            "flexattn_decode_workspace_bytes", "flexattn_decode_splits", "flexattn_split_count",
-           "flexattn_decode")
+           "flexattn_decode", "flexattn_decode_static")
 
 
 class FlexAttnError(RuntimeError):
@@ -95,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.flexattn_decode.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_float, c_int, c_int, ctypes.POINTER(Params),
                                       ctypes.POINTER(BlockMask), c_int, vp, sz, vp]
+        L.flexattn_decode_static.restype = c_int
+        L.flexattn_decode_static.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                             c_float, c_int, c_int, ctypes.POINTER(Params),
+                                             ctypes.POINTER(BlockMask), c_int, vp]
         L.flexattn_bwd.restype = c_int
         L.flexattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int,
                                    c_int, c_int, c_int, c_float, c_int, c_int,
@@ -194,6 +200,20 @@ def flexattn_decode(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: i
                                _ptr(workspace), workspace_bytes, _stream(stream, q))
     if check:
         _check(st, "flexattn_decode")
+    return st
+
+
+def flexattn_decode_static(q, k, v, out, lse, B: int, H: int, Hkv: int, Sq: int, Skv: int, D: int,
+                           scale: float, mask_kind: int, mod_kind: int, params: Params | None = None,
+                           block_mask: BlockMask | None = None, splits: int = 1, stream=None, *,
+                           check: bool = True) -> int:
+    st = lib().flexattn_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq,
+                                      Skv, D, scale, mask_kind, mod_kind,
+                                      ctypes.byref(params) if params else None,
+                                      ctypes.byref(block_mask) if block_mask else None, splits,
+                                      _stream(stream, q))
+    if check:
+        _check(st, "flexattn_decode_static")
     return st
 
 

@@ -12,6 +12,8 @@
 #include "../../include/flexattn.h"
 #include "launch.h"
 
+static_assert(fa::kStaticScratchBytes == FLEXATTN_STATIC_SCRATCH_BYTES, "static scratch size");
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -126,6 +128,7 @@ const char* flexattn_strerror(int status) {
     case FLEXATTN_ERR_OVERFLOW: return "sizes exceed the 32-bit index range";
     case FLEXATTN_ERR_HIP: return "HIP runtime error";
     case FLEXATTN_ERR_ARG: return "invalid scalar argument";
+    case FLEXATTN_ERR_SCRATCH: return "the call needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -350,10 +353,16 @@ int flexattn_split_count(int B, int H, int Hkv, int Sq, int Skv) {
   return static_cast<int>(std::max<long long>(1, std::min<long long>(s, 64)));
 }
 
-int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
-                    const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// flexattn_decode (workspace from the caller) and flexattn_decode_static
+// (use_static: the library's static scratch; workspace ignored).
+int decode_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
+                int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind, const flexattn_params* params,
+                const flexattn_block_mask* block_mask, int splits, void* workspace, size_t workspace_bytes,
+                bool use_static, void* stream) {
   const flexattn_params* prm = params ? params : &kDefaultParams;
   if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
   int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
@@ -368,7 +377,16 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
     return FLEXATTN_ERR_UNSUPPORTED;
   if (splits < 1 || splits > 64) return FLEXATTN_ERR_ARG;
   if (static_cast<long long>(B) * H * ceil_div(Sq, FLEXATTN_QTILE) * splits > INT_MAX) return FLEXATTN_ERR_OVERFLOW;
-  if (splits > 1) {
+  if (use_static) {
+    const size_t need = flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits);
+    if (need > fa::kStaticScratchBytes) {
+      std::snprintf(g_last_error, sizeof(g_last_error),
+                    "flexattn_decode_static: %zu bytes of split results exceed the %zu-byte static scratch "
+                    "(use fewer splits or flexattn_decode with a workspace)",
+                    need, static_cast<size_t>(fa::kStaticScratchBytes));
+      return FLEXATTN_ERR_SCRATCH;
+    }
+  } else if (splits > 1) {
     if (!workspace) return FLEXATTN_ERR_NULLPTR;
     if (!aligned(workspace, 16)) return FLEXATTN_ERR_ALIGN;
     if (workspace_bytes < flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits)) return FLEXATTN_ERR_ARG;
@@ -416,6 +434,26 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
   p.nk = ceil_div(Skv, FLEXATTN_TILE);
   p.bm_num_b = block_mask ? block_mask->num_b : 1;
   p.splits = splits;
+  if (splits > 1 && use_static) {
+    // the scratch of the device the work runs on: the stream's, which must
+    // be the current device (where the address is looked up)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (stream) {
+      int sdev = 0;
+      e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+      if (sdev != dev) {
+        std::snprintf(g_last_error, sizeof(g_last_error),
+                      "flexattn_decode_static: the stream belongs to device %d, the current device is %d",
+                      sdev, dev);
+        return FLEXATTN_ERR_ARG;
+      }
+    }
+    e = fa::static_scratch(dev, &workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  }
   if (splits > 1) {
     const size_t rows = static_cast<size_t>(B) * H * Sq;
     p.ws_o = static_cast<float*>(workspace);
@@ -424,6 +462,26 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
   hipError_t e = fa::launch_attn_decode(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return FLEXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flexattn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                    const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params, block_mask,
+                     splits, workspace, workspace_bytes, false, stream);
+}
+
+int flexattn_decode_static(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                           const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
+                           void* stream) {
+  return decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params, block_mask,
+                     splits, nullptr, 0, true, stream);
 }
 
 int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,

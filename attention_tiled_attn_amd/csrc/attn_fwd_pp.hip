@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_util.h"
 #include "launch.h"
 #include "variants.h"
@@ -776,7 +778,32 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(FwdLaunch p) {
     p.lse[(static_cast<size_t>(b) * p.H + h) * p.Sq + q_row] = mx > -INFINITY ? mx + __logf(tot) : -INFINITY;
 }
 
+// Split results of flexattn_decode_static, whose callers cannot allocate
+// device memory: a file-scope array, one copy per device, held until the
+// process ends. Host code never names it as an address (in host code the name
+// stands for a host-side shadow, not device memory); it uses the address that
+// hipGetSymbolAddress returns for the current device.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+hipError_t static_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    // once per device, with that device current (the caller's check)
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<false>(p, stream); }
 

@@ -47,6 +47,12 @@ struct FwdLaunch {
 
 hipError_t launch_attn_fwd(const FwdLaunch& p, hipStream_t stream);
 hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream);
+
+// Static scratch of flexattn_decode_static (bytes; the header's
+// FLEXATTN_STATIC_SCRATCH_BYTES), and its device address on `device`, which
+// must be the current device. Looked up once per device, then cached.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(int device, void** ptr);
 // bf16 inputs with nk <= kPairMaxKeyTiles (256-row ping-pong kernel)
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream);
 

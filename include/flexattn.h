@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_VERSION 3
+#define FLEXATTN_VERSION 4
 
 /* Block-mask tiles: FLEXATTN_QTILE query rows (two halves of FLEXATTN_TILE
  * rows) by FLEXATTN_TILE keys. */
@@ -59,8 +59,10 @@ enum flexattn_status {
   FLEXATTN_ERR_OVERFLOW = -6,    /* sizes exceed the 32-bit index range (also: one
                                     (batch, head) slice must stay below 2^31 bytes)    */
   FLEXATTN_ERR_HIP = -7,         /* a HIP call failed; see flexattn_last_error()       */
-  FLEXATTN_ERR_ARG = -8          /* bad scalar argument (scale, window, softcap, size,
+  FLEXATTN_ERR_ARG = -8,         /* bad scalar argument (scale, window, softcap, size,
                                     stride; overlapping gradient layouts)              */
+  FLEXATTN_ERR_SCRATCH = -9      /* flexattn_decode_static: the call's split results
+                                    exceed FLEXATTN_STATIC_SCRATCH_BYTES              */
 };
 
 /* Element type of Q, K, V and O. LSE is always float32. FP32 inputs are
@@ -260,6 +262,31 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
                     int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
                     const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* flexattn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as flexattn_decode (bitwise: the same kernels),
+ * without the workspace: the split results go to a scratch array that the
+ * library holds in device memory, FLEXATTN_STATIC_SCRATCH_BYTES per device,
+ * from the first call on a device until the process ends. The call allocates
+ * nothing.
+ *   splits : 1..64; the split results take
+ *            flexattn_decode_workspace_bytes(B, H, Hkv, Sq, D, splits) bytes
+ *            of the scratch, and a call needing more than
+ *            FLEXATTN_STATIC_SCRATCH_BYTES fails with FLEXATTN_ERR_SCRATCH
+ *            (flexattn_last_error() gives the sizes) before any HIP call
+ *   stream : must belong to the current device (else FLEXATTN_ERR_ARG); the
+ *            first call on a device looks up that device's scratch address
+ * Every call on one device shares that device's scratch, and the contents
+ * last written stay until the next call overwrites them (nothing in it needs
+ * to start at zero: every split writes all of its rows before the merge reads
+ * them). Calls that overlap in time on one device (other streams, other host
+ * threads) race on the scratch and give undefined results: order them. */
+#define FLEXATTN_STATIC_SCRATCH_BYTES (64u << 20)
+int flexattn_decode_static(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                           int H, int Hkv, int Sq, int Skv, int D, float scale, int mask_kind,
+                           int mod_kind, const flexattn_params* params,
+                           const flexattn_block_mask* block_mask, int splits, void* stream);
 
 /* Attention backward: the gradients of L = sum(O * dout) with respect to q, k
  * and v, for O = flexattn_fwd(q, k, v, ...) with the same variant. The pages

@@ -43,8 +43,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.flexattn_version() == 3
-    for code in range(-8, 1):
+    assert fa.flexattn_version() == 4
+    for code in range(-9, 1):
         assert fa.flexattn_strerror(code) and fa.flexattn_strerror(code) != "unknown status"
     assert fa.flexattn_strerror(-99) == "unknown status"
     assert fa.flexattn_last_error() == ""
@@ -371,3 +371,32 @@ def test_bwd_rejects_overlapping_layouts(which, stride, B, code):
 def test_fwd_overlap_rule_applies_to_out_only(which, stride, code):
     assert call(params=P(**{which + "_stride": stride}), lse=A + 2) == code
     assert dcall(params=P(**{which + "_stride": stride}), lse=A + 2) == code
+
+
+# ------------------------------------------------------------------ allocation-free decode
+def scall(**over):
+    a = dict(GOOD, H=8, Hkv=2, Sq=1, Skv=512)
+    params = over.pop("params", None)
+    splits = over.pop("splits", 2)
+    a.update(over)
+    return fa.flexattn_decode_static(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Hkv"],
+                                     a["Sq"], a["Skv"], a["D"], a["scale"], a["mask_kind"], a["mod_kind"],
+                                     params, None, splits, stream=None, check=False)
+
+
+def test_decode_static_validation():
+    # the same checks as flexattn_decode, no workspace arguments
+    assert scall(q=None) == _lib.ERR_NULLPTR
+    assert scall(splits=0) == _lib.ERR_ARG
+    assert scall(splits=65) == _lib.ERR_ARG
+    assert scall(params=P(dtype=_lib.FP32)) == _lib.ERR_UNSUPPORTED
+    assert scall(out=A + 2) == _lib.ERR_ALIGN
+    # split results beyond the static scratch: rejected before any HIP call,
+    # with the sizes in the message
+    B, H, Sq, D = 8, 32, 200, 128        # 8 * 32 * 200 rows * 129 floats = 26.4 MB per split
+    need = fa.flexattn_decode_workspace_bytes(B, H, 8, Sq, D, 3)
+    assert need > _lib.STATIC_SCRATCH_BYTES >= fa.flexattn_decode_workspace_bytes(B, H, 8, Sq, D, 2)
+    assert scall(B=B, H=H, Hkv=8, Sq=Sq, D=D, splits=3) == _lib.ERR_SCRATCH
+    assert str(need) in fa.flexattn_last_error() and str(_lib.STATIC_SCRATCH_BYTES) in fa.flexattn_last_error()
+    # two splits fit: validation passes, and the misaligned output stops the call
+    assert scall(B=B, H=H, Hkv=8, Sq=Sq, D=D, splits=2, out=A + 2) == _lib.ERR_ALIGN
