@@ -44,6 +44,13 @@
 #include "launch.h"
 #include "variants.h"
 
+// Every fused multiply-add of this file is written out (__builtin_fmaf), so
+// the compiler may not fuse others: a copy of the loop it specialises (the
+// first stage, where the exponent base is a known zero) would otherwise round
+// some scores differently from the loop body, and whether a stage takes the
+// specialised copy depends on how many empty stages precede it.
+#pragma clang fp contract(off)
+
 namespace fa {
 namespace {
 
@@ -204,8 +211,15 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
   int n_entries = p.nk;
   int e_spec = 0;
-  // the whole list, from its head: the first copies start before it is staged
-  const bool early = !PACK && p.splits == 1;
+  // Key order. ALiBi's bias grows with the key position, so under a causal
+  // mask ascending keys would raise the running max past the rescale
+  // threshold (and rescale O) on most stages of most heads; visiting the key
+  // tiles in descending order meets the largest biases first, after which the
+  // farther keys only score lower. Other variants take ascending order.
+  constexpr bool kDesc = MOD == kModAlibi;
+  // the whole list, from its head: the first copies start before it is
+  // staged (ascending order only: the descending order starts at its tail)
+  const bool early = !PACK && p.splits == 1 && !kDesc;
   if (!early || n_head < 0) {
     if (kv_count) n_entries = kv_count[bm_b * p.nq + qp];
     if (early && list) {
@@ -273,7 +287,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const bool lab_wave = DOCS && __builtin_amdgcn_readfirstlane(wave) == 0;
   const u32x4 ldesc = make_desc(doc_row, DOCS ? static_cast<unsigned>(p.va.doc_stride) * 4u : 0u);
   const unsigned lab_lds = lds_addr(labbuf);
-  // group 0 copies K(t), group 1 V(t), into ring slot `ring`
+  // group 0 copies K(t), group 1 V(t), into ring slot `ring` (t: the
+  // stage's index in ascending key order)
   auto issue_copy = [&](int t, int e, int ring) {
     const int kv0 = stage_kv0(t, e);
     const unsigned gbase = static_cast<unsigned>(kv0) * grb;
@@ -342,13 +357,21 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     const int kept = (p.Skv - last * kTile + kBN - 1) / kBN;
     n_stages -= kSPT - min(kept, kSPT);
   }
-  auto ent = [&](int t) -> int { return ents[min(t, max(n_stages - 1, 0)) / kSPT]; };
+  // step u of the loop visits stage ord(u) of the ascending key order;
+  // steps past the end clamp to the last stage (their copies are never issued)
+  auto ord = [&](int u) -> int { return kDesc ? max(n_stages - 1 - u, 0) : min(u, max(n_stages - 1, 0)); };
+  auto ent = [&](int u) -> int { return ents[ord(u) / kSPT]; };
 
   // ---- running state
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  // The running max starts as -inf, hidden from the compiler: a copy of the
+  // first loop step that knew it would compute the first stage's scores from
+  // a constant exponent base, with other instructions (and roundings) than
+  // the loop body, and which stage comes first depends on the block mask.
   float m_run = -INFINITY;
+  asm("" : "+v"(m_run));
   float l_run = 0.f;
   using SM = ScoreMod<MOD>;
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
@@ -539,9 +562,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // the max is computed only when the check fails or no base exists yet.
     // This pays off with soft-capping, whose tanh already keeps the vector
     // ALU busy; without it the denser exponential stream slows the other
-    // wave's matrix products more than the skipped max saves, and with ALiBi
-    // the bias grows with the key position so the max rises nearly every
-    // stage. Those take the max first.
+    // wave's matrix products more than the skipped max saves. The other
+    // variants take the max first.
     // After a failed check the base moves to the row max whenever it grew at
     // all, so that the following stages pass the check again.
     // Only rows that exist take part in these wave-wide decisions: a padding
@@ -578,10 +600,20 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     l_run += ls;
   };
 
+  // Barrier between slots. Without the LDS wait of __syncthreads: the copies
+  // into LDS are ordered by the explicit vmcnt waits before it, and every
+  // LDS read of a slot is consumed by that slot's own instructions. The empty
+  // asm statements keep the compiler from moving memory accesses across it.
+  auto slot_barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   // ---- prologue: stages 0 and 1 (group 0 copies K, group 1 copies V)
   const int T = n_stages;
-  if (!early && T > 0) issue_copy(0, ent(0), 0);
-  if (!early && T > 1) issue_copy(1, ent(1), 1);
+  if (!early && T > 0) issue_copy(ord(0), ent(0), 0);
+  if (!early && T > 1) issue_copy(ord(1), ent(1), 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (grp == 1) __syncthreads();   // group 1 runs one slot behind
@@ -605,20 +637,20 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     if (do_pv) pv(ring_old);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    slot_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // vector slot
     const int e_n2 = ent(u + 2);
-    if (do_s) softmax(s, stage_kv0(u, __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0, ring);
+    if (do_s) softmax(s, stage_kv0(ord(u), __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0, ring);
     if (u + 2 < T) {
-      issue_copy(u + 2, __builtin_amdgcn_readfirstlane(e_n2), ring_old);
+      issue_copy(ord(u + 2), __builtin_amdgcn_readfirstlane(e_n2), ring_old);
       wait_prev_stage();   // this group's copies of stage u + 1 are complete
     } else {
       wait_vm<0>();
     }
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    slot_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     e_prev = e_cur;

@@ -116,23 +116,6 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def sample_rows(wl: Workload, inp: Inputs, n_random: int = 40, seed: int = 0, n_ends: int = 0) -> np.ndarray:
-    """Query rows for sampled checks at full size: both ends (the first and
-    last `n_ends` rows), tile edges, the middle, document boundaries, and
-    seeded random rows."""
-    S = wl.Sq
-    r = {0, 1, 2, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 1}
-    r.update(range(min(n_ends, S)))
-    r.update(range(max(0, S - n_ends), S))
-    r.update(x for t in range(256, S, 256) for x in (t - 1, t))
-    if inp.doc_ids is not None:
-        starts = np.flatnonzero(np.diff(inp.doc_ids[0]) != 0) + 1
-        for s in starts:
-            r.update({int(s) - 1, int(s), int(s) + 1})
-    r.update(np.random.default_rng(seed).integers(0, S, n_random).tolist())
-    return np.array(sorted(x for x in r if 0 <= x < S))
-
-
 def small(name="t", *, B=1, H=2, Hkv=None, S=200, Sq=None, Skv=None, D=64, dtype="bf16",
           causal=False, window=0, documents=False, mod="none", softcap=30.0, seed=7,
           doc_range=(16, 96), q_offset=0, prefix=None, rel_max=0) -> Inputs:
@@ -167,5 +150,5 @@ class _SqSkv:
         return getattr(self._wl, name)
 
 
-__all__ = ["run_gpu", "run_oracle", "run_oracle_full", "compare", "to_np", "sample_rows", "small", "make_inputs",
+__all__ = ["run_gpu", "run_oracle", "run_oracle_full", "compare", "to_np", "small", "make_inputs",
            "device_variant", "oracle_kwargs"]
