@@ -41,8 +41,18 @@
 #include <mutex>
 
 #include "device_util.h"
+#include "exp2_poly.h"
 #include "launch.h"
 #include "variants.h"
+
+// Share of the softmax exponentials evaluated by the polynomial of
+// exp2_poly.h instead of the hardware unit: the first N 16-key chunks of
+// each stage (a build option, 0 by default: measured slower, since the vector
+// slot is bound by the issue rate of one wave, where a polynomial costs about
+// eight instructions against one).
+#ifndef FLEXATTN_EXP2_POLY_CHUNKS
+#define FLEXATTN_EXP2_POLY_CHUNKS 0
+#endif
 
 // Every fused multiply-add of this file is written out (__builtin_fmaf), so
 // the compiler may not fuse others: a copy of the loop it specialises (the
@@ -541,8 +551,10 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         unsigned w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j]);
-          const float p1 = __builtin_amdgcn_exp2f(t[kb * 16 + r0 + 2 * j + 1]);
+          const bool poly = ch < FLEXATTN_EXP2_POLY_CHUNKS;
+          const float x0 = t[kb * 16 + r0 + 2 * j], x1 = t[kb * 16 + r0 + 2 * j + 1];
+          const float p0 = poly ? exp2_poly(x0) : __builtin_amdgcn_exp2f(x0);
+          const float p1 = poly ? exp2_poly(x1) : __builtin_amdgcn_exp2f(x1);
           w[j] = pack_bf16(p0, p1);
           acc += p0 + p1;
         }

@@ -22,6 +22,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include "exp2_poly.h"
+
+// Soft-capping's exponential on the multiply-add units (exp2_poly.h) instead
+// of the hardware unit: a build option, 0 by default (measured slower).
+#ifndef FLEXATTN_EXP2_POLY_TANH
+#define FLEXATTN_EXP2_POLY_TANH 0
+#endif
+
 namespace fa {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -112,7 +120,7 @@ struct ScoreMod<kModSoftcap> {
     return {a.sc_out - base};
   }
   __device__ static float shifted(float s, const VariantArgs& a, const Lane&, const Stage& st, int /*c*/) {
-    const float e = __builtin_amdgcn_exp2f(s * a.sc_in);
+    const float e = FLEXATTN_EXP2_POLY_TANH ? exp2_poly4(s * a.sc_in) : __builtin_amdgcn_exp2f(s * a.sc_in);
     return __builtin_fmaf(__builtin_amdgcn_rcpf(e + 1.0f), -2.0f * a.sc_out, st.cb);
   }
 };

@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -96,98 +98,92 @@ def traffic_from_profile(workload: str):
         return None
 
 
-def cpu_baseline(inp, budget_s: float = 15.0):
-    """The oracle, as it is, on whole query rows of the same workload, (batch,
-    head) by (batch, head), until the budget is spent; rate in the unit of the
-    GPU metric (admitted-pair FLOPs per second)."""
-    import numpy as np
-    import oracle
-    from workload import bf16_values
+def _host() -> dict:
+    """Cores this process may use and the CPU model (from /proc/cpuinfo)."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    wl = inp.wl
-    kw = dict(causal=wl.causal, window=wl.window or None,
-              alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
-              softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
-              prefix=wl.prefix,
-              rel_bias=None if inp.rel_bias is None else inp.rel_bias.astype(np.float64))
-    t0 = time.perf_counter()
-    done_pairs = rows_done = heads_done = 0
-    chunk = 512
-    for b in range(wl.B):
-        q, k, v = (bf16_values(t) for t in (inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1]))
-        doc = None if inp.doc_ids is None else inp.doc_ids[b:b + 1]
-        for h in range(wl.H):
-            whole = True
-            for r0 in range(0, wl.Sq, chunk):
-                rows = np.arange(r0, min(wl.Sq, r0 + chunk))
-                oracle.attention(q, k, v, wl.scale, rows=rows, heads=[h], doc_ids=doc, **kw)
-                rows_done += rows.size
-                done_pairs += _pairs_in_rows(wl, rows, None if doc is None else doc[0])
-                if time.perf_counter() - t0 >= budget_s:
-                    whole = r0 + chunk >= wl.Sq
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
                     break
-            heads_done += int(whole)
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    tflops = 4.0 * wl.D * done_pairs / dt / 1e12
-    return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows ({heads_done} whole (batch, head) slices of "
-                      f"{wl.B * wl.H}), {done_pairs} admitted pairs, fp64 numpy oracle, "
-                      f"{dt:.1f} s"}
-
-
-def cpu_baseline_bwd(inp, dout, budget_s: float = 15.0):
-    """The oracle's gradients, as they are, on whole (batch, query head)
-    slices of the same workload until the budget is spent; rate in the unit of
-    the GPU metric (2.5 x the forward FLOPs of the admitted pairs done)."""
-    import numpy as np
-    import oracle
-    from workload import bf16_values
+    except OSError:
+        pass
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return {"affinity_cpus": n, "cpu_model": model}
+
+
+def _slice_sample(wl, doc_ids, pair_budget: float):
+    """Whole (batch row, query head) slices in order, as many as fit the
+    admitted-pair budget (at least one): (batches, heads, pairs)."""
+    per_b = [_pairs_in_rows(wl, np.arange(wl.Sq), None if doc_ids is None else doc_ids[b])
+             for b in range(wl.B)]
+    total = sum(per_b) * wl.H
+    if total <= pair_budget:
+        return list(range(wl.B)), list(range(wl.H)), total
+    n_heads = max(1, min(wl.H, int(pair_budget // max(per_b[0], 1))))
+    if n_heads < wl.H:
+        return [0], list(range(n_heads)), per_b[0] * n_heads
+    n_b = max(1, int(pair_budget // (per_b[0] * wl.H)))
+    return list(range(n_b)), list(range(wl.H)), sum(per_b[:n_b]) * wl.H
+
+
+def _oracle_kwargs(inp) -> dict:
     wl = inp.wl
-    rep = wl.H // wl.Hkv
-    t0 = time.perf_counter()
-    done_pairs = slices = 0
-    for b in range(wl.B):
-        for h in range(wl.H):
-            kh = h // rep
-            q = bf16_values(inp.q[b:b + 1, h:h + 1])
-            k = bf16_values(inp.k[b:b + 1, kh:kh + 1])
-            v = bf16_values(inp.v[b:b + 1, kh:kh + 1])
-            g = bf16_values(dout[b:b + 1, h:h + 1])
-            doc = None if inp.doc_ids is None else inp.doc_ids[b:b + 1]
-            kw = dict(causal=wl.causal, window=wl.window or None, doc_ids=doc,
-                      alibi_slopes=None if inp.slopes is None else inp.slopes[h:h + 1].astype(np.float64),
-                      softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
-                      prefix=wl.prefix,
-                      rel_bias=None if inp.rel_bias is None else inp.rel_bias[h:h + 1].astype(np.float64))
-            oracle.attention_backward(q, k, v, g, wl.scale, **kw)
-            slices += 1
-            done_pairs += _pairs_in_rows(wl, np.arange(wl.Sq), None if doc is None else doc[0])
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": 2.5 * 4.0 * wl.D * done_pairs / dt / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{slices} whole (batch, head) slices of {wl.B * wl.H}, {done_pairs} admitted "
-                      f"pairs, fp64 numpy oracle gradients, {dt:.1f} s"}
+    return dict(causal=wl.causal, window=wl.window or None, doc_ids=inp.doc_ids,
+                alibi_slopes=None if inp.slopes is None else inp.slopes.astype(np.float64),
+                softcap=wl.softcap if wl.mod == "softcap" else None, q_offset=wl.q_offset,
+                prefix=wl.prefix,
+                rel_bias=None if inp.rel_bias is None else inp.rel_bias.astype(np.float64))
+
+
+def cpu_baseline(inp, pair_budget: float = 4e9):
+    """The oracle, as it is, in a pool of host processes (one per usable core,
+    at most 16, one BLAS thread each), on whole (batch, head) slices of the
+    same workload: the whole workload when its admitted pairs fit the budget,
+    else its first slices. Rate in the unit of the GPU metric."""
+    from oracle.pool import attention_parallel
+    from workload import bf16_values
+    wl = inp.wl
+    batches, heads, pairs = _slice_sample(wl, inp.doc_ids, pair_budget)
+    q, k, v = (bf16_values(t) for t in (inp.q, inp.k, inp.v))
+    st = {}
+    attention_parallel(q, k, v, wl.scale, heads=heads, batches=batches, stats=st, **_oracle_kwargs(inp))
+    dt = st["seconds"]
+    whole = len(batches) * len(heads) == wl.B * wl.H
+    return {"value": 4.0 * wl.D * pairs / dt / 1e12, "unit": "TFLOPS", "cores": st["workers"],
+            "kind": "oracle", **_host(),
+            "sample": (f"{'the whole workload' if whole else 'a bounded sample'}: "
+                       f"{len(batches) * len(heads)} of {wl.B * wl.H} (batch, head) slices, "
+                       f"{pairs} admitted pairs; fp64 numpy oracle in {st['workers']} processes "
+                       f"(1 BLAS thread each, {st['tasks']} row blocks), {dt:.1f} s wall")}
+
+
+def cpu_baseline_bwd(inp, dout, pair_budget: float = 1e9):
+    """The oracle's gradients, as they are, per (batch, query head) slice in
+    a pool of host processes, on whole slices of the same workload up to the
+    pair budget; rate in the unit of the GPU metric (2.5 x the forward FLOPs
+    of the admitted pairs done)."""
+    from oracle.pool import attention_backward_slices
+    from workload import bf16_values
+    wl = inp.wl
+    batches, heads, pairs = _slice_sample(wl, inp.doc_ids, pair_budget)
+    q, k, v, g = (bf16_values(t) for t in (inp.q, inp.k, inp.v, dout))
+    st = {}
+    attention_backward_slices(q, k, v, g, wl.scale, [(b, h) for b in batches for h in heads], stats=st,
+                              **_oracle_kwargs(inp))
+    dt = st["seconds"]
+    return {"value": 2.5 * 4.0 * wl.D * pairs / dt / 1e12, "unit": "TFLOPS", "cores": st["workers"],
+            "kind": "oracle", **_host(),
+            "sample": (f"{len(batches) * len(heads)} of {wl.B * wl.H} whole (batch, head) slices, "
+                       f"{pairs} admitted pairs; fp64 numpy oracle gradients in {st['workers']} "
+                       f"processes (1 BLAS thread each), {dt:.1f} s wall")}
 
 
 def _pairs_in_rows(wl, rows, doc_row) -> int:
-    import numpy as np
     import oracle
     tot = 0
     keys = np.arange(wl.Skv)
@@ -318,18 +314,21 @@ def main(argv=None):
     if bwd:   # also reads dO and O, writes dQ, dK, dV and delta
         bytes_alg += (2 * q.numel() + q.numel() + k.numel() + v.numel()) * q.element_size() + lse.numel() * 4
     traffic = None if bwd else traffic_from_profile(wl.name)
+    # where `traffic` comes from: counters taken with rocprofv3 on this same
+    # kernel source (matched by kernel_sha), not measured in this run
+    traffic_src = f"profiles/attn_fwd_{wl.name}_traffic.md (rocprofv3 FETCH_SIZE + WRITE_SIZE)" if traffic else None
     if wl.decode:
         # HBM-bound: K and V are read once, Q read and O, LSE written once
         roof = {"bound": "hbm", "achieved": round(bytes_alg / (kern_avg_ms * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(bytes_alg / (kern_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": bytes_alg,
+                "traffic": traffic, "traffic_source": traffic_src, "algorithmic_bytes": bytes_alg,
                 "kernel": "attn_fwd_pp_kernel (decode mode) + attn_decode_merge_kernel",
                 "splits": splits}
     else:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_bytes": bytes_alg,
+                "traffic_source": traffic_src, "algorithmic_bytes": bytes_alg,
                 "kernel": ("attn_bwd_dq_kernel + attn_bwd_dkdv_kernel" if bwd else
                            "attn_fwd_pp_kernel (split keys) + attn_decode_merge_kernel" if wl.split else
                            "attn_fwd_pp_kernel" if wl.dtype == "bf16" else "attn_fwd_kernel")}

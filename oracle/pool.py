@@ -25,11 +25,12 @@ import time
 
 import numpy as np
 
-from .attention import attention, kv_head_of
+from .attention import attention, attention_backward, kv_head_of
 
-__all__ = ["attention_parallel", "default_workers"]
+__all__ = ["attention_parallel", "attention_backward_slices", "default_workers"]
 
 _ARRAYS: dict = {}
+_BARRIER = None
 
 
 def default_workers(limit: int = 16) -> int:
@@ -41,7 +42,9 @@ def default_workers(limit: int = 16) -> int:
     return max(1, min(n, limit))
 
 
-def _init(path: str) -> None:
+def _init(path: str, barrier) -> None:
+    global _BARRIER
+    _BARRIER = barrier
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(1)
@@ -50,6 +53,23 @@ def _init(path: str) -> None:
     for name in os.listdir(path):
         if name.endswith(".npy"):
             _ARRAYS[name[:-4]] = np.load(os.path.join(path, name), mmap_mode="r")
+
+
+def _sync() -> int:
+    _BARRIER.wait(timeout=600)
+    return os.getpid()
+
+
+def _start(ctx, workers: int, path: str):
+    """A pool whose workers have all started and loaded their inputs. The
+    executor starts a worker per task while none is idle, and each of these
+    tasks holds its worker at a barrier until all have arrived, so times taken
+    afterwards exclude starting the workers."""
+    ex = cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_init,
+                                initargs=(path, ctx.Barrier(workers)))
+    pids = {f.result() for f in [ex.submit(_sync) for _ in range(workers)]}
+    assert len(pids) == workers
+    return ex
 
 
 def _task(b: int, h: int, r0: int, r1: int, scale: float, kw: dict):
@@ -78,7 +98,8 @@ def attention_parallel(q, k, v, scale: float, *, workers: int | None = None, row
     query head) split into blocks of `rows_per_task` and evaluated in
     `workers` processes. Returns (O, LSE) as `attention` does; heads outside
     `heads` and batch rows outside `batches` are left as NaN. `stats`, if
-    given, receives the wall time and the worker count."""
+    given, receives the wall time of the evaluation (started workers, inputs
+    loaded) and the worker count."""
     q = np.asarray(q)
     B, H, Sq, D = q.shape
     workers = workers or default_workers()
@@ -99,10 +120,8 @@ def attention_parallel(q, k, v, scale: float, *, workers: int | None = None, row
         L = np.full((B, H, Sq), np.nan)
         tasks = [(b, h, r0, min(Sq, r0 + rows_per_task)) for b in batches for h in heads
                  for r0 in range(0, Sq, rows_per_task)]
-        t0 = time.perf_counter()
-        ctx = mp.get_context("spawn")
-        with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_init,
-                                    initargs=(tmp,)) as ex:
+        with _start(mp.get_context("spawn"), workers, tmp) as ex:
+            t0 = time.perf_counter()
             futs = [ex.submit(_task, b, h, r0, r1, float(scale), kw) for b, h, r0, r1 in tasks]
             for f in cf.as_completed(futs):
                 b, h, r0, r1, o, lse = f.result()
@@ -111,5 +130,50 @@ def attention_parallel(q, k, v, scale: float, *, workers: int | None = None, row
         if stats is not None:
             stats.update(seconds=time.perf_counter() - t0, workers=workers, tasks=len(tasks))
         return O, L
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def _bwd_task(b: int, h: int, scale: float, kw: dict):
+    """Gradients of one (batch row, query head) slice: the oracle's backward
+    on that head's query rows against its key/value head (its share of the
+    group's dK and dV)."""
+    q, k, v, g = _ARRAYS["q"], _ARRAYS["k"], _ARRAYS["v"], _ARRAYS["dout"]
+    kh = kv_head_of(h, q.shape[1], k.shape[1])
+    extra = dict(kw)
+    if "doc_ids" in _ARRAYS:
+        extra["doc_ids"] = _ARRAYS["doc_ids"][b:b + 1]
+    if "alibi_slopes" in _ARRAYS:
+        extra["alibi_slopes"] = _ARRAYS["alibi_slopes"][h:h + 1]
+    if "rel_bias" in _ARRAYS:
+        extra["rel_bias"] = _ARRAYS["rel_bias"][h:h + 1]
+    dq, dk, dv = attention_backward(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1],
+                                    g[b:b + 1, h:h + 1], scale, **extra)
+    return b, h, dq[0, 0], dk[0, 0], dv[0, 0]
+
+
+def attention_backward_slices(q, k, v, dout, scale: float, slices, *, workers: int | None = None,
+                              doc_ids=None, alibi_slopes=None, rel_bias=None, stats: dict | None = None,
+                              **kw):
+    """The oracle's gradients per (batch row, query head) slice in `slices`,
+    in `workers` processes: {(b, h): (dQ, dK share, dV share)}. The dK and dV
+    of a key/value head are the sums of its query heads' shares."""
+    workers = workers or default_workers()
+    tmp = tempfile.mkdtemp(prefix="oracle_pool_")
+    try:
+        for name, a in dict(q=q, k=k, v=v, dout=dout, doc_ids=doc_ids, alibi_slopes=alibi_slopes,
+                            rel_bias=rel_bias).items():
+            if a is not None:
+                np.save(os.path.join(tmp, name + ".npy"), np.asarray(a))
+        out = {}
+        with _start(mp.get_context("spawn"), workers, tmp) as ex:
+            t0 = time.perf_counter()
+            futs = [ex.submit(_bwd_task, b, h, float(scale), kw) for b, h in slices]
+            for f in cf.as_completed(futs):
+                b, h, dq, dk, dv = f.result()
+                out[(b, h)] = (dq, dk, dv)
+        if stats is not None:
+            stats.update(seconds=time.perf_counter() - t0, workers=workers, tasks=len(slices))
+        return out
     finally:
         shutil.rmtree(tmp, ignore_errors=True)

@@ -61,3 +61,23 @@ def test_pool_subsets_leave_the_rest_nan():
 def test_default_workers_bounded():
     assert 1 <= default_workers() <= 16
     assert default_workers(limit=1) == 1
+
+
+def test_backward_slices_sum_to_plain_oracle():
+    """Per-slice gradients summed over a group's query heads equal the plain
+    oracle's dK and dV; dQ slices equal its dQ."""
+    from oracle import attention_backward
+    from oracle.pool import attention_backward_slices
+    q, k, v = _inputs(B=2, H=4, Hkv=2, Sq=40, Skv=50)
+    g = np.random.default_rng(5).standard_normal(q.shape)
+    kw = dict(causal=True, alibi_slopes=np.array([0.5, 0.25, 0.1, 0.05]), q_offset=10)
+    dQ, dK, dV = attention_backward(q, k, v, g, 0.3, **kw)
+    res = attention_backward_slices(q, k, v, g, 0.3, [(b, h) for b in range(2) for h in range(4)],
+                                    workers=2, **kw)
+    for b in range(2):
+        for kh in range(2):
+            sk = sum(res[(b, h)][1] for h in (2 * kh, 2 * kh + 1))
+            sv = sum(res[(b, h)][2] for h in (2 * kh, 2 * kh + 1))
+            assert np.abs(sk - dK[b, kh]).max() <= 1e-12 and np.abs(sv - dV[b, kh]).max() <= 1e-12
+        for h in range(4):
+            assert np.abs(res[(b, h)][0] - dQ[b, h]).max() <= 1e-12
