@@ -1,9 +1,11 @@
 """Build libflexattn.so in-tree with hipcc for gfx950.
 
-    python -m attention_tiled_attn_amd.build [-v]
+    python -m attention_tiled_attn_amd.build [-v] [--define NAME=VALUE ...]
 
 Every call recompiles (sources are few). Objects go to _build/ beside this
-file; the shared library is written next to this file.
+file; the shared library is written next to this file. --define passes a
+preprocessor definition to every source (the kernels' build options, e.g.
+FLEXATTN_EXP2_POLY_CHUNKS=2 for the software-exp2 A/B).
 """
 from __future__ import annotations
 
@@ -37,8 +39,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, verbose: bool, defines=()) -> None:
+    cmd = [hipcc(), *COMMON, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,12 +50,12 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(r.stderr, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, defines=()) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        list(ex.map(lambda a: _compile(a[0], a[1], verbose), zip(SOURCES, objs)))
+        list(ex.map(lambda a: _compile(a[0], a[1], verbose, defines), zip(SOURCES, objs)))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
@@ -66,4 +68,6 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    defs = [args[i + 1] for i, a in enumerate(args) if a == "--define" and i + 1 < len(args)]
+    print(build(verbose="-v" in args, defines=defs))
