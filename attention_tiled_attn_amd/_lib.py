@@ -13,7 +13,10 @@ import os
 
 import torch  # noqa: F401  (must precede loading the library, see above)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflexattn.so")
+# FLEXATTN_LIB names another build of the same ABI (the sanitizer build of
+# the argument checks, loaded by tests/test_abi_sanitized.py)
+LIB_PATH = os.environ.get("FLEXATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libflexattn.so")
 
 # status codes and enums, as in include/flexattn.h
 OK = 0

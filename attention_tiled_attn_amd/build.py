@@ -1,11 +1,19 @@
 """Build libflexattn.so in-tree with hipcc for gfx950.
 
     python -m attention_tiled_attn_amd.build [-v] [--define NAME=VALUE ...]
+    python -m attention_tiled_attn_amd.build --sanitize
 
 Every call recompiles (sources are few). Objects go to _build/ beside this
 file; the shared library is written next to this file. --define passes a
 preprocessor definition to every source (the kernels' build options, e.g.
 FLEXATTN_EXP2_POLY_CHUNKS=2 for the software-exp2 A/B).
+
+--sanitize builds libflexattn_san.so instead: the C ABI's host code
+(api.cpp) compiled by the host C++ compiler with the address and
+undefined-behaviour sanitizers, linked with stand-ins for the kernels and
+HIP calls (csrc/host_stubs.cpp). It runs the argument checks only, on the
+CPU (tests/test_abi_sanitized.py loads it with the sanitizer runtime
+preloaded).
 """
 from __future__ import annotations
 
@@ -67,7 +75,32 @@ def build(verbose: bool = False, defines=()) -> str:
     return OUT
 
 
+SAN_OUT = os.path.join(HERE, "libflexattn_san.so")
+SAN_FLAGS = ["-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if not cxx:
+        raise RuntimeError("no host C++ compiler for the sanitizer build")
+    rocm_inc = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "include")
+    tmp = SAN_OUT + ".tmp"
+    cmd = [cxx, *SAN_FLAGS, f"-I{rocm_inc}", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "host_stubs.cpp"), "-shared", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     args = sys.argv[1:]
     defs = [args[i + 1] for i, a in enumerate(args) if a == "--define" and i + 1 < len(args)]
-    print(build(verbose="-v" in args, defines=defs))
+    if "--sanitize" in args:
+        print(build_sanitized(verbose="-v" in args))
+    else:
+        print(build(verbose="-v" in args, defines=defs))

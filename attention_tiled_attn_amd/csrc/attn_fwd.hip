@@ -36,17 +36,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "launch.h"
 #include "variants.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kBM = 128;        // query rows per workgroup
@@ -66,37 +63,6 @@ struct Geo {
   static constexpr int vCols = kBN * D / (4 * kThreads);  // V columns per thread (4 rows each)
   static_assert(kChunks >= 1 && vCols >= 2 && (D / vCols) == 16, "tile geometry");
 };
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
-__device__ inline unsigned pack_bf16(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-
-// Exchange with lane ^ 32: the pair returned holds this lane's value and the
-// partner's, in an order that depends on the half; symmetric reductions
-// (max, +) of the two give the 64-lane-pair result on both halves.
-__device__ inline float max_pair32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float sum_pair32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
-// return zero (the hardware range check). 0x00020000 in the last descriptor
-// word selects 32-bit data format, which untyped loads need on gfx9.
-__device__ inline rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
 
 // 8 consecutive elements at element offset `eo`, as 4 packed bf16 pairs
 // (fp32 sources rounded to nearest even).

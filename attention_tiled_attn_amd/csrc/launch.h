@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
-#include "variants.h"
+#include "variant_args.h"
 
 namespace fa {
 

@@ -36,6 +36,7 @@ KERNEL_SOURCES = ["attention_tiled_attn_amd/csrc/attn_fwd_pp.hip",
                   "attention_tiled_attn_amd/csrc/device_util.h",
                   "attention_tiled_attn_amd/csrc/exp2_poly.h",
                   "attention_tiled_attn_amd/csrc/variants.h",
+                  "attention_tiled_attn_amd/csrc/variant_args.h",
                   "attention_tiled_attn_amd/csrc/launch.h"]
 
 
