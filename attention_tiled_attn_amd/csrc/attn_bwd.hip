@@ -42,7 +42,6 @@ using namespace dev;
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kRows = 128;      // query rows (dq) or keys (dkdv) per workgroup
 constexpr int kTile = 128;      // key tile of the block mask
-constexpr int kRing = 3;
 constexpr int kXcds = 8;
 
 template <int D, int STAGE>
@@ -78,19 +77,20 @@ __device__ inline unsigned row_off(int r, int chunk) {
 }
 
 // Copy one stage of rows of D bf16 starting at byte `gbase` of the slice behind `desc`
-// (rows `grb` bytes apart) into a stage buffer: this wave fills 1 KB runs
-// wq * kDma + j; lane i writes slot i, i.e. row s / kCpr at chunk position
-// s % kCpr.
-template <int D, int STAGE>
+// (rows `grb` bytes apart) into a stage buffer, shared by WAVES waves: this
+// wave fills 1 KB runs wq * n + j (n = runs per wave); lane i writes slot i,
+// i.e. row s / kCpr at chunk position s % kCpr.
+template <int D, int STAGE, int WAVES = 4>
 __device__ inline void copy_tile(u32x4 desc, unsigned gbase, unsigned grb, unsigned lds_base, int wq, int lane) {
   using G = BGeo<D, STAGE>;
+  constexpr int n = G::kBufBytes / 1024 / WAVES;
+  static_assert(n >= 1 && n * 1024 * WAVES == G::kBufBytes, "copy shares");
 #pragma unroll
-  for (int j = 0; j < G::kDma; ++j) {
-    const int s = (wq * G::kDma + j) * 64 + lane;
+  for (int j = 0; j < n; ++j) {
+    const int s = (wq * n + j) * 64 + lane;
     const int r = s / G::kCpr, pos = s % G::kCpr;
     const unsigned goff = static_cast<unsigned>(r) * grb + static_cast<unsigned>((pos ^ swz<D>(r)) * 16);
-    copy_to_lds(desc, gbase + goff,
-                __builtin_amdgcn_readfirstlane(lds_base + (wq * G::kDma + j) * 1024));
+    copy_to_lds(desc, gbase + goff, __builtin_amdgcn_readfirstlane(lds_base + (wq * n + j) * 1024));
   }
 }
 
@@ -117,6 +117,24 @@ __device__ inline unsigned trans_off(int lane, int db, int j) {
   const int r = 8 * j + 4 * (G16 >> 1) + (sl >> 2);
   const int d0 = 32 * db + 16 * (G16 & 1) + 4 * (sl & 3);
   return row_off<D>(r, d0 >> 3) + (d0 & 7) * 2;
+}
+
+// Scheduling pattern for a run of N matrix-product groups whose LDS operand
+// reads are independent of earlier products: the reads of the first AHEAD
+// groups, then each group's products followed by the reads of the group
+// AHEAD later. A group is one product per chain (G = products per group:
+// reads per group = READS); used right after the code it orders.
+template <int N, int AHEAD, int READS, int G = (READS == 3 ? 2 : 1)>
+__device__ inline void reads_ahead() {
+  static_assert(N > AHEAD, "pipeline depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * READS, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
 }
 
 // Modified score in log2 units, and d s'/d s for the chain rule.
@@ -768,6 +786,393 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV at D <= 128 with two waves per SIMD. Eight waves: wave w < 4 and
+// wave w + 4 form a pair that owns keys 32 w .. 32 w + 31 of the 128-key
+// tile (on the usual round-robin placement both sit on SIMD w). Per 64-row
+// query stage u the first wave forms S = Q K^T, P, and dV^T += dO^T P, and
+// hands P (times ds'/ds under soft-capping) to its partner through LDS; the
+// partner forms dP = dO V^T for stage u and, for stage u - 1 (whose P the
+// barrier between the iterations published), dS = P (dP - delta) and
+// dK^T += Q^T dS. Each wave holds one of K^T, V^T and one accumulator, so
+// both stay within the 256 registers of two waves per SIMD, and one wave's
+// exponentials overlap the other's matrix products. Every gradient element
+// is still summed by one lane in stage order (no atomics).
+// LDS at D = 128: Q ring of three stages (stage u - 1 is read for dK while
+// u + 1 arrives), dO ring of two, P in float32 double-buffered, LSE, delta
+// and (documents) labels per stage: about 146 KB, one workgroup per CU.
+constexpr int kDkv2Threads = 512;
+
+template <int D, int MOD, bool DOCS>
+__global__ __launch_bounds__(kDkv2Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv2_kernel(BwdLaunch p) {
+  static_assert(D == 64 || D == 128, "two-wave dK/dV kernel: D = 64 or 128");
+  constexpr int kStage = 64;
+  using G = BGeo<D, kStage>;
+  constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
+  constexpr int KB = G::kKB, CH = G::kCH;
+  constexpr int kQRing = 3, kORing = 2, kSRing = 3;
+  constexpr int kWSlot = 4 * KB * 16 * 64;   // floats of P for the four pairs
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kQRing * G::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf[kORing * G::kBufBytes];
+  __shared__ __attribute__((aligned(16))) float wbuf[2 * kWSlot];
+  __shared__ __attribute__((aligned(16))) float lbuf[kSRing * kStage];
+  __shared__ __attribute__((aligned(16))) float dbuf[kSRing * kStage];
+  __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kSRing * kStage : 4];
+  __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
+  lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool first = wave < 4;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int nk = (p.Skv + kRows - 1) / kRows;
+  const int total = p.B * p.Hkv * nk;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int lin = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (lin >= total) return;
+  const int kt = lin % nk;
+  const int bkh = lin / nk;
+  const int kvh = bkh % p.Hkv, b = bkh / p.Hkv;
+  const int rep = p.H / p.Hkv;
+  const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u, orb = static_cast<unsigned>(p.o_sr) * 2u;
+  const unsigned krb = static_cast<unsigned>(p.k_sr) * 2u, vrb = static_cast<unsigned>(p.v_sr) * 2u;
+
+  const int k_row = kt * kRows + pair * 32 + l32;
+  const bool k_ok = k_row < p.Skv;
+
+  // B operand of this wave's first product: K^T (S = Q K^T) or V^T (dP = dO V^T);
+  // lane (key l32, half g) holds 8 consecutive d
+  bf16x8 bop[DC];
+  {
+    const void* base = first ? static_cast<const void*>(static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh)
+                             : static_cast<const void*>(static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh);
+    const unsigned rb = first ? krb : vrb;
+    const rsrc_t r = make_rsrc(base, static_cast<unsigned>(p.Skv - 1) * rb + RB);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const unsigned col = (c * 16 + g * 8) * 2;
+      const unsigned off = k_ok ? static_cast<unsigned>(k_row) * rb + col : 0x80000000u;
+      bop[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+  }
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
+
+  // the query stages that can see keys [k_lo, k_hi] of this tile (as in the
+  // one-wave kernel)
+  const bool causal = p.mask_kind & kMaskCausal;
+  const bool window = p.mask_kind & kMaskWindow;
+  const int off = p.va.q_offset;
+  const int k_lo = kt * kRows;
+  const int k_hi = min(p.Skv, k_lo + kRows) - 1;
+  const int q_first = (causal && k_lo >= p.va.prefix) ? min(max(k_lo - off, 0), p.Sq) : 0;
+  const int q_end = window ? static_cast<int>(min(static_cast<long long>(p.Sq),
+                                                  static_cast<long long>(k_hi) + p.va.window - off))
+                           : p.Sq;
+  const int s0 = q_first / kStage;
+  const int ns = q_end > q_first ? (q_end + kStage - 1) / kStage - s0 : 0;
+  const int T = rep * ns;
+
+  // fragment offsets from one base each: the chunk permutation touches only
+  // the low chunk bits and a row's chunk bits sit below its row offset, so
+  // chunk 2c + g's row offset is chunk g's XOR 32 c and block db's
+  // transposed offset block 0's XOR 64 db (at D = 64 and 128 alike)
+  const unsigned qoff0 = row_off<D>(l32, g);
+  const unsigned toff0[2] = {trans_off<D>(lane, 0, 0), trans_off<D>(lane, 0, 1)};
+  auto qoff = [&](int c) -> unsigned { return qoff0 ^ static_cast<unsigned>(c << 5); };
+  auto toff = [&](int db, int j) -> unsigned { return toff0[j] ^ static_cast<unsigned>(db << 6); };
+
+  const unsigned ql = lds_addr(qbuf), ol = lds_addr(obuf);
+  const unsigned ll = lds_addr(lbuf), dl = lds_addr(dbuf), labl = lds_addr(labbuf);
+  // stage u: query head rep kvh + u / ns, rows kStage (s0 + u % ns) ..; all
+  // eight waves share the tile copies, wave 0 copies LSE and delta and
+  // wave 1 the rows' document labels
+  auto copy_stage = [&](int u) {
+    const int hh = kvh * rep + u / ns;
+    const int r0 = (s0 + u % ns) * kStage;
+    const u32x4 qd = make_desc(static_cast<const __bf16*>(p.q) + b * p.q_sb + hh * p.q_sh,
+                               static_cast<unsigned>(p.Sq - 1) * qrb + RB);
+    const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + b * p.o_sb + hh * p.o_sh,
+                               static_cast<unsigned>(p.Sq - 1) * orb + RB);
+    copy_tile<D, kStage, 8>(qd, static_cast<unsigned>(r0) * qrb, qrb, ql + (u % kQRing) * G::kBufBytes, wave, lane);
+    copy_tile<D, kStage, 8>(od, static_cast<unsigned>(r0) * orb, orb, ol + (u % kORing) * G::kBufBytes, wave, lane);
+    const int sl = u % kSRing;
+    if (wave == 0 && lane < kStage / 4) {
+      const size_t q_head = (static_cast<size_t>(b) * p.H + hh) * p.Sq;
+      const u32x4 lsd = make_desc(p.lse + q_head, static_cast<unsigned>(p.Sq) * 4u);
+      const u32x4 dld = make_desc(p.delta + q_head, static_cast<unsigned>(p.Sq) * 4u);
+      copy_to_lds(lsd, static_cast<unsigned>(r0) * 4u + lane * 16u, __builtin_amdgcn_readfirstlane(ll + sl * kStage * 4));
+      copy_to_lds(dld, static_cast<unsigned>(r0) * 4u + lane * 16u, __builtin_amdgcn_readfirstlane(dl + sl * kStage * 4));
+    }
+    if constexpr (DOCS) {
+      if (wave == 1 && lane < kStage / 4) {
+        // positions past the label array read as zero; their rows are past
+        // Sq and masked by the query range
+        const u32x4 ld = make_desc(doc_row, static_cast<unsigned>(p.va.doc_stride) * 4u);
+        copy_to_lds(ld, static_cast<unsigned>(r0 + off) * 4u + lane * 16u,
+                    __builtin_amdgcn_readfirstlane(labl + sl * kStage * 4));
+      }
+    }
+  };
+  // a new query head under relative bias: its table replaces the last
+  // head's, whose last reader (the previous stage's P) finished before the
+  // previous barrier; every wave takes this barrier
+  auto head_table = [&](int u) {
+    if constexpr (MOD == kModRelBias) {
+      if (u % ns == 0) {
+        stage_rel_table(p.va, kvh * rep + u / ns, (lds_f32*)(rtab), tid, kDkv2Threads);
+        __syncthreads();
+      }
+    }
+  };
+
+  if (T > 0) copy_stage(0);
+  wait_vm<0>();
+  __syncthreads();
+
+  f32x16 acc[DB];   // dV^T (first wave) or dK^T (second)
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  if (first) {
+    for (int u = 0; u < T; ++u) {
+      head_table(u);
+      if (u + 1 < T) copy_stage(u + 1);
+      const int hh = __builtin_amdgcn_readfirstlane(kvh * rep + u / ns);
+      const int r0 = (s0 + u % ns) * kStage;
+      const unsigned char* qb_ = qbuf + (u % kQRing) * G::kBufBytes;
+      const unsigned char* ob_ = obuf + (u % kORing) * G::kBufBytes;
+      const float* lb = lbuf + (u % kSRing) * kStage;
+      const int q_last = r0 + kStage - 1;
+      bool full = !DOCS && q_last < p.Sq && k_hi == k_lo + kRows - 1;
+      if (causal) full = full && (r0 + off >= k_hi || k_hi < p.va.prefix);
+      if (window) full = full && (q_last + off - k_lo < p.va.window);
+      float slope2 = 0.f;
+      if constexpr (MOD == kModAlibi) {
+        // a scalar load (constant address space, uniform index): a vector
+        // load's wait would also wait for the copies just issued
+        const __attribute__((address_space(4))) float* sl =
+            (const __attribute__((address_space(4))) float*)(p.va.slopes);
+        slope2 = sl[hh] * kLog2e;
+      }
+
+      // S = Q K^T: KB 32-row query blocks, each operand read issued four
+      // products ahead of its product (the compiler's own order waits on
+      // almost every read)
+      f32x16 s[KB];
+#pragma unroll
+      for (int qb = 0; qb < KB; ++qb) s[qb] = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+#pragma unroll
+        for (int qb = 0; qb < KB; ++qb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qb_ + qoff(c) + qb * 32 * RB);
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[c], s[qb], 0, 0, 0);
+        }
+      reads_ahead<DC * KB, 4, 1>();
+
+      // modified scores, masked in place on partial stages (element 16 qb + i
+      // is row r0 + 32 qb + 8 (i / 4) + 4 g + i % 4)
+      float tt[KB * 16];
+      float dmv[MOD == kModSoftcap ? KB * 16 : 1];
+#pragma unroll
+      for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qpos = r0 + 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3) + off;
+          float dmod;
+          tt[qb * 16 + i] = mod_score<MOD>(s[qb][i], p.va, slope2, tab, k_row - qpos, dmod);
+          if constexpr (MOD == kModSoftcap) dmv[qb * 16 + i] = dmod;
+        }
+      if (!full) {
+        const float ninf = -INFINITY;
+        const int rr0 = r0 + 4 * g;
+        const long long kq = static_cast<long long>(k_row) - off - rr0;
+        long long hi = static_cast<long long>(p.Sq) - 1 - rr0;
+        if (window) hi = min(hi, kq + p.va.window - 1);
+        if (!k_ok) hi = -1;
+        const long long lo = (causal && k_row >= p.va.prefix) ? kq : 0LL;
+        int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kStage)));
+        const int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kStage)));
+        bool need_doc = false;
+        const int* lab = labbuf + (u % kSRing) * kStage;
+        if constexpr (DOCS) {
+          const int lq = lab[lane & (kStage - 1)];
+          const int l0 = __builtin_amdgcn_readfirstlane(lq);
+          if (__all(lq == l0)) {
+            if (doc_k != l0) hi_c = -1;
+          } else {
+            need_doc = true;
+          }
+        }
+        if (need_doc) {
+#pragma unroll
+          for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int4 l4 = *reinterpret_cast<const int4*>(lab + 32 * qb + 8 * i4 + 4 * g);
+              const int lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                mask_in_place(tt[qb * 16 + 4 * i4 + x], __builtin_amdgcn_ballot_w64(lv[x] == doc_k), ninf);
+            }
+        }
+        if (!__all(lo_c <= 0)) {
+#pragma unroll
+          for (int j = 0; j < KB * 16; ++j)
+            mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) >= lo_c),
+                          ninf);
+        }
+        if (!__all(hi_c >= kStage - 1)) {
+#pragma unroll
+          for (int j = 0; j < KB * 16; ++j)
+            mask_in_place(tt[j], __builtin_amdgcn_ballot_w64((j >> 4) * 32 + 8 * ((j >> 2) & 3) + (j & 3) <= hi_c),
+                          ninf);
+        }
+      }
+
+      // P = exp2(t - log2(e) LSE) (LSE clamped by one med3 so that a row
+      // with no admitted key gives P = 0, not NaN); P, times ds'/ds under
+      // soft-capping, goes to the partner as float32, P as bf16 into the
+      // B operand of dV^T += dO^T P
+      float* wout = wbuf + (u & 1) * kWSlot + pair * (KB * 16 * 64);
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        const int qb = ch >> 1, i0 = (ch & 1) * 8;
+        unsigned wp[4];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + ql0);
+          f32x4 pv;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int i = i0 + 4 * hv + x;
+            const float lc = __builtin_amdgcn_fmed3f(l4[x], -1e30f, 3e38f);
+            pv[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(lc, -kLog2e, tt[qb * 16 + i]));
+          }
+          f32x4 wv = pv;
+          if constexpr (MOD == kModSoftcap) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) wv[x] *= dmv[qb * 16 + i0 + 4 * hv + x];
+          }
+          *reinterpret_cast<f32x4*>(wout + ((2 * ch + hv) * 64 + lane) * 4) = wv;
+          wp[2 * hv] = pack_bf16(pv[0], pv[1]);
+          wp[2 * hv + 1] = pack_bf16(pv[2], pv[3]);
+        }
+        const u32x4 wpv = {wp[0], wp[1], wp[2], wp[3]};
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, wpv);
+        // dV^T += dO^T P for this chunk of 16 rows (each accumulator still
+        // sums the chunks in order)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(ob_, toff(db, 0), toff(db, 1), ch), pf,
+                                                            acc[db], 0, 0, 0);
+      }
+      wait_vm<0>();
+      __syncthreads();
+    }
+  } else {
+    // dS of stage v from its P (published by the barrier that ended
+    // iteration v) and dP, packed to bf16 in the key order of the B operand
+    auto ds_of = [&](int v, const f32x16 (&dp)[KB], bf16x8 (&dsf)[CH]) {
+      const float* win = wbuf + (v & 1) * kWSlot + pair * (KB * 16 * 64);
+      const float* dlb = dbuf + (v % kSRing) * kStage;
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        const int qb = ch >> 1, i0 = (ch & 1) * 8;
+        unsigned wd[4];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + ql0);
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(win + ((2 * ch + hv) * 64 + lane) * 4);
+          float dv4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) dv4[x] = wv[x] * (dp[qb][i0 + 4 * hv + x] - d4[x]);
+          wd[2 * hv] = pack_bf16(dv4[0], dv4[1]);
+          wd[2 * hv + 1] = pack_bf16(dv4[2], dv4[3]);
+        }
+        const u32x4 wdv = {wd[0], wd[1], wd[2], wd[3]};
+        dsf[ch] = __builtin_bit_cast(bf16x8, wdv);
+      }
+    };
+    // dK^T += Q^T dS of stage v, product i (chunk i / DB, block i % DB:
+    // each accumulator sums the chunks in order)
+    auto dk_product = [&](int v, int i, const bf16x8 (&dsf)[CH]) {
+      const unsigned char* qp_ = qbuf + (v % kQRing) * G::kBufBytes;
+      const int ch = i / DB, db = i % DB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(qp_, toff(db, 0), toff(db, 1), ch), dsf[ch],
+                                                        acc[db], 0, 0, 0);
+    };
+    // dP = dO V^T of stage u, product i (d chunk i / KB, row block i % KB)
+    auto dp_product = [&](int u, int i, f32x16 (&dp)[KB]) {
+      const unsigned char* ob_ = obuf + (u % kORing) * G::kBufBytes;
+      const int c = i / KB, qb = i % KB;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob_ + qoff(c) + qb * 32 * RB);
+      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[c], dp[qb], 0, 0, 0);
+    };
+    constexpr int NPROD = DC * KB;   // dP products per stage; as many dK products
+    static_assert(NPROD == CH * DB, "product counts");
+    // one iteration: dS and dK of stage u - 1, which consume dP of stage
+    // u - 1, then dP of stage u into the same registers. The dS work needs
+    // nothing from this iteration, so it runs while the first wave's S
+    // products occupy the matrix unit, and the dK and dP products then run
+    // beside the first wave's exponentials.
+    f32x16 dp[KB];
+    bf16x8 dsf[CH];
+    for (int u = 0; u < T; ++u) {
+      head_table(u);
+      if (u + 1 < T) copy_stage(u + 1);
+      if (u > 0) ds_of(u - 1, dp, dsf);
+#pragma unroll
+      for (int qb = 0; qb < KB; ++qb) dp[qb] = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      if (u > 0) {
+        // dK products of stage u - 1 and dP products of stage u alternate
+        // (two independent chains), operand reads three pairs ahead
+#pragma unroll
+        for (int i = 0; i < NPROD; ++i) {
+          dk_product(u - 1, i, dsf);
+          dp_product(u, i, dp);
+        }
+        reads_ahead<NPROD, 3, 3>();
+      } else {
+#pragma unroll
+        for (int i = 0; i < NPROD; ++i) dp_product(u, i, dp);
+        reads_ahead<NPROD, 4, 1>();
+      }
+      wait_vm<0>();
+      __syncthreads();
+    }
+    if (T > 0) {
+      ds_of(T - 1, dp, dsf);
+#pragma unroll
+      for (int i = 0; i < NPROD; ++i) dk_product(T - 1, i, dsf);
+    }
+  }
+
+  if (k_ok) {
+    const float sc = first ? 1.f : p.scale;
+    __bf16* const row = first
+        ? static_cast<__bf16*>(p.dv) + b * p.v_sb + kvh * p.v_sh + static_cast<size_t>(k_row) * p.v_sr
+        : static_cast<__bf16*>(p.dk) + b * p.k_sb + kvh * p.k_sh + static_cast<size_t>(k_row) * p.k_sr;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const u32x2 vv = {pack_bf16(acc[db][4 * i] * sc, acc[db][4 * i + 1] * sc),
+                          pack_bf16(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc)};
+        *reinterpret_cast<u32x2*>(row + d0) = vv;
+      }
+  }
+}
+
 template <int D, int MOD, bool DOCS>
 hipError_t launch_t(const BwdLaunch& p, hipStream_t stream) {
   {
@@ -780,8 +1185,13 @@ hipError_t launch_t(const BwdLaunch& p, hipStream_t stream) {
   }
   const long long total = static_cast<long long>(p.B) * p.Hkv * ((p.Skv + kRows - 1) / kRows);
   const long long per = (total + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
-                     dim3(kThreads), 0, stream, p);
+  if constexpr (D <= 128) {
+    hipLaunchKernelGGL((attn_bwd_dkdv2_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+                       dim3(kDkv2Threads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
+                       dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
