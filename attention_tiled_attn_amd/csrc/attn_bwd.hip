@@ -802,6 +802,7 @@ void attn_bwd_dkdv_kernel(BwdLaunch p) {
 // u + 1 arrives), dO ring of two, P in float32 double-buffered, LSE, delta
 // and (documents) labels per stage: about 146 KB, one workgroup per CU.
 constexpr int kDkv2Threads = 512;
+constexpr int kDkvMaxStages = 1024;   // stage list of the document path (Sq up to 64K rows)
 
 template <int D, int MOD, bool DOCS>
 __global__ __launch_bounds__(kDkv2Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -819,6 +820,12 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   __shared__ __attribute__((aligned(16))) float lbuf[kSRing * kStage];
   __shared__ __attribute__((aligned(16))) float dbuf[kSRing * kStage];
   __shared__ __attribute__((aligned(16))) int labbuf[DOCS ? kSRing * kStage : 4];
+  // documents with a block mask: the visited 64-row stages of this key tile
+  // in order, (stage << 1) | full, and the class of each candidate 128-row
+  // half (0 empty, 1 partial, 3 full)
+  __shared__ int slist[DOCS ? kDkvMaxStages : 1];
+  __shared__ unsigned char hcls[DOCS ? kDkvMaxStages / 2 + 1 : 1];
+  __shared__ int nvis_lds;
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // the current head's bias table
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
 
@@ -874,7 +881,69 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
                            : p.Sq;
   const int s0 = q_first / kStage;
   const int ns = q_end > q_first ? (q_end + kStage - 1) / kStage - s0 : 0;
-  const int T = rep * ns;
+
+  // Under a document mask the block mask (exact per 128-row half and 128-key
+  // tile) drops the stages of halves that see none of these keys and marks
+  // those that see all of them as full: the lists of the candidate query
+  // tiles are read in parallel (one entry per thread), the entries for this
+  // key tile give their halves' classes, and wave 0 compacts the visited
+  // stages in order. Without a block mask, or past kDkvMaxStages candidate
+  // stages, every candidate stage is visited with the mask.
+  int nvis = ns;
+  bool use_list = false;
+  if constexpr (DOCS) {
+    use_list = p.kv_count != nullptr && ns > 0 && ns <= kDkvMaxStages;
+    if (use_list) {
+      const int h0 = s0 >> 1, h1 = (s0 + ns - 1) >> 1;   // candidate halves, inclusive
+      for (int i = tid; i <= h1 - h0; i += kDkv2Threads) hcls[i] = 0;
+      __syncthreads();
+      const int bm_b = p.bm_num_b > 1 ? b : 0;
+      const int qp0 = h0 >> 1, nqp = (h1 >> 1) - qp0 + 1;
+      // thread t reads entry j of query tile qp0 + t / 32 + 16 m, j = t % 32 + 32 i
+      for (int m = 0; m * 16 < nqp; ++m) {
+        const int qp = qp0 + m * 16 + (tid >> 5);
+        if (qp - qp0 < nqp) {
+          const int cnt = p.kv_count[bm_b * p.nq + qp];
+          const int* lst = p.kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk;
+          for (int j = tid & 31; j < cnt; j += 32) {
+            const int e = lst[j];
+            if ((e >> 4) == kt) {
+#pragma unroll
+              for (int hf = 0; hf < 2; ++hf) {
+                const int h = 2 * qp + hf;
+                if (h >= h0 && h <= h1) hcls[h - h0] = static_cast<unsigned char>((e >> (2 * hf)) & 3);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < ns; j0 += 64) {
+          const int j = j0 + lane;
+          const int c = j < ns ? hcls[((s0 + j) >> 1) - h0] : 0;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(c != 0);
+          const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+          if (c != 0) slist[base + rank] = ((s0 + j) << 1) | (c == 3 ? 1 : 0);
+          base += __builtin_popcountll(m);
+        }
+        if (lane == 0) nvis_lds = base;
+      }
+      __syncthreads();
+      nvis = __builtin_amdgcn_readfirstlane(nvis_lds);
+    }
+  }
+  const int T = rep * nvis;
+  // stage u: query head kvh rep + u / nvis; (64-row stage << 1) | full
+  auto stage_of = [&](int u) -> int {
+    const int j = u % nvis;
+    if constexpr (DOCS) {
+      if (use_list) return __builtin_amdgcn_readfirstlane(slist[j]);
+    }
+    return (s0 + j) << 1;
+  };
 
   // fragment offsets from one base each: the chunk permutation touches only
   // the low chunk bits and a row's chunk bits sit below its row offset, so
@@ -887,12 +956,11 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
 
   const unsigned ql = lds_addr(qbuf), ol = lds_addr(obuf);
   const unsigned ll = lds_addr(lbuf), dl = lds_addr(dbuf), labl = lds_addr(labbuf);
-  // stage u: query head rep kvh + u / ns, rows kStage (s0 + u % ns) ..; all
-  // eight waves share the tile copies, wave 0 copies LSE and delta and
-  // wave 1 the rows' document labels
+  // all eight waves share the tile copies of stage u, wave 0 copies LSE and
+  // delta and wave 1 the rows' document labels
   auto copy_stage = [&](int u) {
-    const int hh = kvh * rep + u / ns;
-    const int r0 = (s0 + u % ns) * kStage;
+    const int hh = kvh * rep + u / nvis;
+    const int r0 = (stage_of(u) >> 1) * kStage;
     const u32x4 qd = make_desc(static_cast<const __bf16*>(p.q) + b * p.q_sb + hh * p.q_sh,
                                static_cast<unsigned>(p.Sq - 1) * qrb + RB);
     const u32x4 od = make_desc(static_cast<const __bf16*>(p.dout) + b * p.o_sb + hh * p.o_sh,
@@ -922,8 +990,8 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   // previous barrier; every wave takes this barrier
   auto head_table = [&](int u) {
     if constexpr (MOD == kModRelBias) {
-      if (u % ns == 0) {
-        stage_rel_table(p.va, kvh * rep + u / ns, (lds_f32*)(rtab), tid, kDkv2Threads);
+      if (u % nvis == 0) {
+        stage_rel_table(p.va, kvh * rep + u / nvis, (lds_f32*)(rtab), tid, kDkv2Threads);
         __syncthreads();
       }
     }
@@ -941,15 +1009,19 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
     for (int u = 0; u < T; ++u) {
       head_table(u);
       if (u + 1 < T) copy_stage(u + 1);
-      const int hh = __builtin_amdgcn_readfirstlane(kvh * rep + u / ns);
-      const int r0 = (s0 + u % ns) * kStage;
+      const int hh = __builtin_amdgcn_readfirstlane(kvh * rep + u / nvis);
+      const int st = stage_of(u);
+      const int r0 = (st >> 1) * kStage;
       const unsigned char* qb_ = qbuf + (u % kQRing) * G::kBufBytes;
       const unsigned char* ob_ = obuf + (u % kORing) * G::kBufBytes;
       const float* lb = lbuf + (u % kSRing) * kStage;
       const int q_last = r0 + kStage - 1;
+      // every pair of the stage in range and admitted? (for documents the
+      // block mask's class, which accounts for every part of the mask)
       bool full = !DOCS && q_last < p.Sq && k_hi == k_lo + kRows - 1;
       if (causal) full = full && (r0 + off >= k_hi || k_hi < p.va.prefix);
       if (window) full = full && (q_last + off - k_lo < p.va.window);
+      if (DOCS && use_list) full = (st & 1) != 0;
       float slope2 = 0.f;
       if constexpr (MOD == kModAlibi) {
         // a scalar load (constant address space, uniform index): a vector

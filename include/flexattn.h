@@ -305,8 +305,12 @@ int flexattn_decode_static(const void* q, const void* k, const void* v, void* ou
  *   delta      : device float32 [B][H][Sq], caller-owned scratch that the call
  *                overwrites with rowsum(dout * out); its contents afterwards
  *                are unspecified
- *   block_mask : as for flexattn_fwd (used for dq; dk/dv classify their own
- *                tiles), or NULL
+ *   block_mask : as for flexattn_fwd, or NULL. dq visits its key tiles;
+ *                dk/dv (D = 64, 128) under a document mask also read the
+ *                lists to skip query rows that see none of a key tile and
+ *                to treat fully admitted ones as full; other masks (and
+ *                NULL) give dk/dv the query range from the causal and
+ *                window parts. Results do not depend on whether it is given
  * Each gradient element is accumulated in a fixed order by one thread (no
  * atomics), so results are bitwise reproducible run to run. */
 int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
