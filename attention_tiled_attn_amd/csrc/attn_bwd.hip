@@ -124,17 +124,19 @@ __device__ inline unsigned trans_off(int lane, int db, int j) {
 // groups, then each group's products followed by the reads of the group
 // AHEAD later. A group is one product per chain (G = products per group:
 // reads per group = READS); used right after the code it orders.
+// (AHEAD is clamped below N.)
 template <int N, int AHEAD, int READS, int G = (READS == 3 ? 2 : 1)>
 __device__ inline void reads_ahead() {
-  static_assert(N > AHEAD, "pipeline depth");
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * READS, 0);
+  constexpr int A = AHEAD < N ? AHEAD : N - 1;
+  static_assert(A >= 1, "pipeline depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, A * READS, 0);
 #pragma unroll
-  for (int i = 0; i < N - AHEAD; ++i) {
+  for (int i = 0; i < N - A; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
   }
 #pragma unroll
-  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+  for (int i = 0; i < A; ++i) __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
 }
 
 // Modified score in log2 units, and d s'/d s for the chain rule.
@@ -263,10 +265,10 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   auto ent = [&](int t) -> int { return ents[min(t, max(T - 1, 0)) / SPT]; };
   auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t % SPT) * kStage; };
 
-  // fragment offsets; at D = 256 formed as needed (the chunk permutation
-  // XORs low bits only, so chunk c's row offset is chunk 0's XOR 32 c and
-  // block db's transposed offset block 0's XOR 64 db)
-  constexpr bool kXor = D == 256;
+  // fragment offsets formed as needed from one base each (the chunk
+  // permutation XORs low bits only, so chunk c's row offset is chunk 0's
+  // XOR 32 c and block db's transposed offset block 0's XOR 64 db)
+  constexpr bool kXor = true;
   unsigned koff[kXor ? 1 : DC];
 #pragma unroll
   for (int c = 0; c < (kXor ? 1 : DC); ++c) koff[c] = row_off<D>(l32, 2 * c + g);
@@ -317,19 +319,32 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
     const unsigned char* kb_ = kbuf + ring * G::kBufBytes;
     const unsigned char* vb_ = vbuf + ring * G::kBufBytes;
 
-    // S^T = K Q^T and dP^T = V dO^T
+    // S^T = K Q^T, then dP^T = V dO^T, each in a scheduling region of its
+    // own with its operand reads issued four products ahead (in one region
+    // the compiler runs one chain ahead and fetches each of its operands
+    // just before use)
     f32x16 s[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < DC; ++c)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff_at(c) + kb * 32 * RB);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    reads_ahead<DC * KB, 4, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(vb_ + koff_at(c) + kb * 32 * RB);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[c], dp[kb], 0, 0, 0);
       }
+    reads_ahead<DC * KB, 4, 1>();
+    __builtin_amdgcn_sched_barrier(0);
 
     // dS^T = P^T (dP^T - delta) ds'/ds, packed to bf16 in the key order of
     // the B operand (element 16 kb + r is key kv0 + 32 kb + 8 (r / 4) + 4 g + r % 4).
