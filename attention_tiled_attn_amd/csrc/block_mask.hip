@@ -3,9 +3,9 @@
 // 256-row query tile the ascending list of key tiles that are non-empty for
 // at least one of its two 128-row halves, with the class of each half.
 //
-// FlexAttention's score/mask modifications (PyTorch FlexAttention FA4-backend
-// post; NextVector FlexAttention article, body) let masked structure be known
-// ahead of the kernel. Skipping empty tiles and dropping the per-element test on
+// FlexAttention's user-supplied score and mask functions (PyTorch
+// FlexAttention FA4-backend post; NextVector FlexAttention article, body) let
+// masked structure be known ahead of the kernel. Skipping empty tiles and dropping the per-element test on
 // full ones is how a sparse variant (sliding window, document packing) runs at
 // dense-tile speed on the tiles it does compute.
 //
