@@ -322,7 +322,9 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
     // S^T = K Q^T, then dP^T = V dO^T, each in a scheduling region of its
     // own with its operand reads issued four products ahead (in one region
     // the compiler runs one chain ahead and fetches each of its operands
-    // just before use)
+    // just before use). dP^T starts from zero and delta is subtracted after
+    // the products: where P = 1 (a single admitted key) dP and delta are the
+    // same dot product and then cancel exactly, as the definition's dS = 0.
     f32x16 s[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = f32x16{};
@@ -828,6 +830,10 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   constexpr int DC = D / 16, DB = D / 32, RB = G::kRowBytes;
   constexpr int KB = G::kKB, CH = G::kCH;
   constexpr int kQRing = 3, kORing = 2, kSRing = 3;
+  // the row's LSE joins the S accumulator's start (the score mod is linear
+  // in s; relative bias, also linear, keeps the LSE in the exponent's FMA,
+  // since its table lookups leave no registers for the start values)
+  constexpr bool kLseInS = MOD == kModNone || MOD == kModAlibi;
   constexpr int kWSlot = 4 * KB * 16 * 64;   // floats of P for the four pairs
   __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kQRing * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char obuf[kORing * G::kBufBytes];
@@ -1048,10 +1054,26 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
 
       // S = Q K^T: KB 32-row query blocks, each operand read issued four
       // products ahead of its product (the compiler's own order waits on
-      // almost every read)
+      // almost every read). Without a score mod and under ALiBi (linear in
+      // s) the row's LSE goes into the accumulator's start,
+      // -LSE log2(e) / c1, so the modified score is already t - log2(e) LSE.
+      // A row with no admitted key (LSE = -inf) starts at +inf; it lies in
+      // partial stages only, whose mask sets every one of its scores to -inf.
       f32x16 s[KB];
+      if constexpr (kLseInS) {
+        const float f = -kLog2e / p.va.c1;
 #pragma unroll
-      for (int qb = 0; qb < KB; ++qb) s[qb] = f32x16{};
+        for (int qb = 0; qb < KB; ++qb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 32 * qb + 8 * i4 + 4 * g);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) s[qb][4 * i4 + x] = l4[x] * f;
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < KB; ++qb) s[qb] = f32x16{};
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < DC; ++c)
@@ -1122,10 +1144,10 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
         }
       }
 
-      // P = exp2(t - log2(e) LSE) (LSE clamped by one med3 so that a row
-      // with no admitted key gives P = 0, not NaN); P, times ds'/ds under
-      // soft-capping, goes to the partner as float32, P as bf16 into the
-      // B operand of dV^T += dO^T P
+      // P = exp2(t - log2(e) LSE) (where the LSE is not in S, it is clamped
+      // by one med3 so that a row with no admitted key gives P = 0, not NaN);
+      // P, times ds'/ds under soft-capping, goes to the partner as float32,
+      // P as bf16 into the B operand of dV^T += dO^T P
       float* wout = wbuf + (u & 1) * kWSlot + pair * (KB * 16 * 64);
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
@@ -1133,14 +1155,18 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
         unsigned wp[4];
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv) {
-          const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + ql0);
           f32x4 pv;
+          if constexpr (kLseInS) {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int i = i0 + 4 * hv + x;
-            const float lc = __builtin_amdgcn_fmed3f(l4[x], -1e30f, 3e38f);
-            pv[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(lc, -kLog2e, tt[qb * 16 + i]));
+            for (int x = 0; x < 4; ++x) pv[x] = __builtin_amdgcn_exp2f(tt[qb * 16 + i0 + 4 * hv + x]);
+          } else {
+            const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + ql0);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const float lc = __builtin_amdgcn_fmed3f(l4[x], -1e30f, 3e38f);
+              pv[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(lc, -kLog2e, tt[qb * 16 + i0 + 4 * hv + x]));
+            }
           }
           f32x4 wv = pv;
           if constexpr (MOD == kModSoftcap) {
@@ -1166,6 +1192,8 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   } else {
     // dS of stage v from its P (published by the barrier that ended
     // iteration v) and dP, packed to bf16 in the key order of the B operand
+    // (delta subtracted after the products, so that dP - delta cancels
+    // exactly where P = 1, as in the dQ kernel)
     auto ds_of = [&](int v, const f32x16 (&dp)[KB], bf16x8 (&dsf)[CH]) {
       const float* win = wbuf + (v & 1) * kWSlot + pair * (KB * 16 * 64);
       const float* dlb = dbuf + (v % kSRing) * kStage;
@@ -1175,10 +1203,9 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
         unsigned wd[4];
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv) {
-          const int ql0 = 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g;
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + ql0);
           const f32x4 wv = *reinterpret_cast<const f32x4*>(win + ((2 * ch + hv) * 64 + lane) * 4);
           float dv4[4];
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + 32 * qb + 8 * ((i0 >> 2) + hv) + 4 * g);
 #pragma unroll
           for (int x = 0; x < 4; ++x) dv4[x] = wv[x] * (dp[qb][i0 + 4 * hv + x] - d4[x]);
           wd[2 * hv] = pack_bf16(dv4[0], dv4[1]);
