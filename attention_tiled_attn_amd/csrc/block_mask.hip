@@ -68,12 +68,20 @@ __device__ inline void label_range(const int* doc, int lo, int hi, int lane, int
 // interval meets that run. Lanes hold keys ka + lane and ka + 64 + lane, run
 // starts are found with a ballot, and the runs are walked in order on the
 // scalar unit, so the cost is a few instructions per run, not per pair.
-__device__ bool half_tile_has_pair(const int* doc, int ka, int kb, int lane, const int (&lab_r)[2],
+// The labels come from tile_labels, issued for several tiles before the
+// first walk so that their loads are in flight together.
+struct TileLabels {
+  int l0, l1;   // labels of keys ka + lane and ka + 64 + lane (0 past the tile)
+};
+__device__ inline TileLabels tile_labels(const int* doc, int ka, int kb, int lane) {
+  const int n = kb - ka + 1;
+  return {lane < n ? doc[ka + lane] : 0, lane + 64 < n ? doc[ka + 64 + lane] : 0};
+}
+__device__ bool half_tile_has_pair(const TileLabels& t, int ka, int kb, int lane, const int (&lab_r)[2],
                                    const int (&lo_r)[2], const int (&hi_r)[2]) {
   const int n = kb - ka + 1;   // keys in the tile (1..128)
   const bool in0 = lane < n, in1 = lane + 64 < n;
-  const int l0 = in0 ? doc[ka + lane] : 0;
-  const int l1 = in1 ? doc[ka + 64 + lane] : 0;
+  const int l0 = t.l0, l1 = t.l1;
   // label of the key before each of the lane's two keys
   const int prev0 = __shfl(l0, lane == 0 ? 0 : lane - 1);
   const int prev1 = lane == 0 ? __shfl(l0, 63) : __shfl(l1, lane - 1);
@@ -110,7 +118,9 @@ __device__ bool half_tile_has_pair(const int* doc, int ka, int kb, int lane, con
 // the ranges decide exactly. Ranges that overlap without one shared label
 // leave "empty or partial" open (never "full": some pair then has two
 // labels); half_tile_has_pair decides those pairs.
-__global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
+// (Few workgroups run at once, so the kernel may take the registers that keep
+// all of a tile's label loads in flight.)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void block_mask_kernel(MaskLaunch p) {
   const int qp = blockIdx.x;
   const int bb = blockIdx.y;
   const int lane = threadIdx.x;
@@ -197,9 +207,9 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
       int dk_min = 0x7fffffff, dk_max = -0x7fffffff - 1;
       int k = k_lo;
       if (in_range && (reinterpret_cast<uintptr_t>(doc + k_lo) & 15) == 0) {
-        // a whole tile: 32 aligned 16-byte loads, several in flight
+        // a whole tile: 32 aligned 16-byte loads, all in flight
         const int4* v4 = reinterpret_cast<const int4*>(doc + k_lo);
-#pragma unroll 8
+#pragma unroll
         for (int i = 0; i < kTile / 4; ++i) {
           const int4 v = v4[i];
           dk_min = min(dk_min, min(min(v.x, v.y), min(v.z, v.w)));
@@ -220,19 +230,35 @@ __global__ __launch_bounds__(64) void block_mask_kernel(MaskLaunch p) {
       }
     }
 
-    // Pairs the label ranges leave open: decided one by one, by the whole
-    // wave, walking the open (tile, half) pairs of this pass in order.
+    // Pairs the label ranges leave open: decided by the whole wave, the open
+    // (tile, half) pairs of this pass in order, kBatch at a time (the labels
+    // of a batch's tiles are loaded together, then each tile is walked).
     if (docs) {
+      constexpr int kBatch = 8;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         uint64_t open = __ballot(cls[hf] == kUnknown);
         uint64_t found = 0;
         while (open) {
-          const int j = __builtin_ctzll(open);
-          open &= open - 1;
-          const int ka = (kt0 + j) * kTile;
-          const int kb = min(p.Skv, ka + kTile) - 1;
-          if (half_tile_has_pair(doc, ka, kb, lane, lab_r[hf], lo_r[hf], hi_r[hf])) found |= 1ull << j;
+          int js[kBatch];
+          TileLabels tl[kBatch];
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            js[q] = -1;
+            if (open) {
+              js[q] = __builtin_ctzll(open);
+              open &= open - 1;
+              const int ka = (kt0 + js[q]) * kTile;
+              tl[q] = tile_labels(doc, ka, min(p.Skv, ka + kTile) - 1, lane);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            if (js[q] < 0) break;
+            const int ka = (kt0 + js[q]) * kTile;
+            if (half_tile_has_pair(tl[q], ka, min(p.Skv, ka + kTile) - 1, lane, lab_r[hf], lo_r[hf], hi_r[hf]))
+              found |= 1ull << js[q];
+          }
         }
         if (cls[hf] == kUnknown) cls[hf] = ((found >> lane) & 1) ? kPartial : kEmpty;
       }

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dense] [--no-cpu-baseline] [--pass bwd]
+    python bench.py [--steps K] [--warmup W] [--settle-ms T] [--workload dense] [--no-cpu-baseline] [--pass bwd]
 
 One step is the whole hot path on one batch: build the block mask for the
 workload's mask, then run the attention forward (both kernels, enqueued on
@@ -9,6 +9,12 @@ torch's current stream). Inputs are seeded synthetic tensors resident in HBM
 before timing starts. The metric is effective TFLOPS counting only admitted
 (unmasked) pairs: 4 * D * pairs * B * H per forward (two products, 2 FLOP per
 multiply-add). Prints one JSON line.
+
+Before the W warm-up steps the step runs untimed for --settle-ms (300 by
+default): under sustained load the GPU raises its clock over the first ~50 ms
+(a cold dense run takes ~547 us a step over steps 5-25 and ~478 us from step
+50 on), so timing right after a few warm-up steps would measure that ramp,
+not the kernels' steady rate. The K timed steps follow the W warm-up steps.
 
 With --pass bwd the step is the block-mask build plus the backward call
 (flexattn_bwd: dQ, then dK/dV) on the forward's O and LSE, counted by the usual
@@ -202,6 +208,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed load before the warm-up steps, so the clock settles")
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
@@ -277,6 +285,13 @@ def main(argv=None):
             ev[1].record(stream)
         return bm
 
+    settle_steps = 0
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        settle_steps += 4
+        torch.cuda.synchronize()      # keep the host within a few steps of the GPU
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -345,6 +360,8 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
