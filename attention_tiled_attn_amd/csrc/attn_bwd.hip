@@ -185,6 +185,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing4 * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing4 * G::kBufBytes];
   __shared__ int ents[kPairMaxKeyTiles];
+  __shared__ int n_ent_lds;
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -245,23 +246,43 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
-  // key-tile list: half qt % 2 of 256-row tile qt / 2; a tile empty for this
-  // half is visited as partial (its masked scores give P = 0, adding nothing)
-  const int qp = qt >> 1, full_bit = 2 * (qt & 1) + 1;
+  // key-tile list: half qt % 2 of 256-row tile qt / 2. The list names the
+  // key tiles that either half sees; wave 0 keeps, in order, those this half
+  // sees (compacting in place: each 64-entry chunk is read before any of it
+  // is written, and no entry moves up). Without a block mask every key tile
+  // is visited as partial.
+  const int qp = qt >> 1, any_bit = 2 * (qt & 1), full_bit = any_bit + 1;
   const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
-  const int n_entries = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
-  for (int i = tid; i < n_entries; i += kThreads) ents[i] = list ? list[i] : (i << 4);
+  const int n_listed = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
+  for (int i = tid; i < n_listed; i += kThreads) ents[i] = list ? list[i] : (i << 4);
   if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
+  __syncthreads();
+  if (list) {
+    if (wave == 0) {
+      int base = 0;
+      for (int j0 = 0; j0 < n_listed; j0 += 64) {
+        const int e = j0 + lane < n_listed ? ents[j0 + lane] : 0;
+        const bool keep = j0 + lane < n_listed && ((e >> any_bit) & 1);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+        const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+        if (keep) ents[base + rank] = e;
+        base += __builtin_popcountll(m);
+      }
+      if (lane == 0) n_ent_lds = base;
+    }
+    __syncthreads();
+  }
+  const int n_entries = list ? __builtin_amdgcn_readfirstlane(n_ent_lds) : n_listed;
   int T = SPT * n_entries;
   if (n_entries > 0) {
     // stages of the last tile that start at or past Skv are dropped
-    const int last = list ? (list[n_entries - 1] >> 4) : (p.nk - 1);
+    const int last = ents[n_entries - 1] >> 4;
     const int kept = (p.Skv - last * kTile + kStage - 1) / kStage;
     T -= SPT - min(kept, SPT);
   }
-  __syncthreads();
   auto ent = [&](int t) -> int { return ents[min(t, max(T - 1, 0)) / SPT]; };
   auto stage_kv0 = [](int t, int e) -> int { return (e >> 4) * kTile + (t % SPT) * kStage; };
 
