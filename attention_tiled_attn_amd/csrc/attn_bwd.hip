@@ -10,22 +10,28 @@
 //     dS  = dS' * ds'/ds  (1, or 1 - tanh^2 for soft-capping)
 //     dQ  = scale * dS K,  dK += scale * dS^T Q
 //
-// Two kernels, no atomics (every gradient element is summed by one lane in a
-// fixed order, so results are reproducible bit for bit):
+// Two kernels per call, no atomics (every gradient element is summed by one
+// lane in a fixed order, so results are reproducible bit for bit):
 //  * attn_bwd_dq_kernel: one workgroup (4 waves x 32 rows) per 128 query rows
 //    of one (batch, head); it first forms delta for its rows (written to the
-//    caller's scratch for the second kernel), then walks the key tiles of the
-//    block mask in 32-key stages: S^T = K Q^T and dP^T = V dO^T (A operands K
-//    and V rows), then dQ^T += K^T dS^T (A operand K^T through transposing
-//    LDS reads). Two of these workgroups share a CU at D <= 128.
-//  * attn_bwd_dkdv_kernel: one workgroup (4 waves x 32 keys) per 128 keys of
-//    one (batch, key/value head); it walks the query heads of the group and
-//    the query stages (64 rows, 32 at D = 256) that can see its keys:
-//    S = Q K^T and dP = dO V^T (B operands K^T and V^T kept in registers),
-//    then dV^T += dO^T P and dK^T += Q^T dS (A operands through transposing
-//    LDS reads of dO and Q).
-// Tiles go from HBM/L2 straight into LDS (buffer-to-LDS copies, a ring of
-// three stages), rows unpadded with 16-byte chunks permuted so that both the
+//    caller's scratch for the second kernel), then walks the key tiles its
+//    half of the block mask admits, in 32-key stages: S^T = K Q^T and
+//    dP^T = V dO^T (A operands K and V rows), then dQ^T += K^T dS^T (A operand
+//    K^T through transposing LDS reads). Two of these workgroups share a CU
+//    at D <= 128.
+//  * attn_bwd_dkdv2_kernel (D = 64, 128): one workgroup of eight waves per
+//    128 keys of one (batch, key/value head), in pairs that own 32 keys: the
+//    first wave of a pair forms S = Q K^T, P and dV^T += dO^T P and hands P
+//    to its partner through LDS; the partner forms dP = dO V^T and, one stage
+//    later, dS and dK^T += Q^T dS. Each wave holds one operand set and one
+//    accumulator, so two waves share each SIMD.
+//  * attn_bwd_dkdv_kernel (D = 256): one workgroup (4 waves x 32 keys) per
+//    128 keys, each wave holding K^T, V^T and both accumulators: S = Q K^T
+//    and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS, one wave per SIMD.
+// Both dK/dV kernels walk the query heads of the group and the query stages
+// (64 rows, 32 at D = 256) that can see their keys.
+// Tiles go from HBM/L2 straight into LDS (buffer-to-LDS copies into rings of
+// stage buffers), rows unpadded with 16-byte chunks permuted so that both the
 // b128 row reads and the transposing reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
