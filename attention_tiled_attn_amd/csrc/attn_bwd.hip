@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 #include "variants.h"
@@ -190,7 +192,12 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   constexpr int kRing4 = 4;
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kRing4 * G::kBufBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kRing4 * G::kBufBytes];
-  __shared__ int ents[kPairMaxKeyTiles];
+  // list entries (kv_tile << 4) | class bits, kv_tile < kPairMaxKeyTiles;
+  // with the relative-bias table they are stored in 16 bits, so that two
+  // workgroups still fit one CU's LDS at D = 128
+  using Ent = std::conditional_t<MOD == kModRelBias, unsigned short, int>;
+  static_assert(kPairMaxKeyTiles << 4 <= 65536, "16-bit list entries");
+  __shared__ Ent ents[kPairMaxKeyTiles];
   __shared__ int n_ent_lds;
   __shared__ float rtab[MOD == kModRelBias ? kRelCap : 1];   // this head's bias table
 
@@ -261,7 +268,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
   const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
   const int n_listed = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
-  for (int i = tid; i < n_listed; i += kThreads) ents[i] = list ? list[i] : (i << 4);
+  for (int i = tid; i < n_listed; i += kThreads) ents[i] = static_cast<Ent>(list ? list[i] : (i << 4));
   if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
   __syncthreads();
@@ -274,7 +281,7 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
         const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
         const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
                                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
-        if (keep) ents[base + rank] = e;
+        if (keep) ents[base + rank] = static_cast<Ent>(e);
         base += __builtin_popcountll(m);
       }
       if (lane == 0) n_ent_lds = base;
