@@ -233,9 +233,19 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int q_row = qt * kRows + wave * 32 + l32;
   const bool q_ok = q_row < p.Sq;
 
-  // B operands (Q^T, dO^T) and this row's delta = dO . O
-  bf16x8 qf[DC], dof[DC];
-  float delta = 0.f;
+  // key-tile list: half qt % 2 of 256-row tile qt / 2. Its length and its
+  // first kThreads entries are fetched first (every list has room for nk
+  // entries), so that they arrive with the rows below instead of after them.
+  const int qp = qt >> 1, any_bit = 2 * (qt & 1), full_bit = any_bit + 1;
+  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
+  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
+  const int n_listed = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
+  const int e_first = (list && tid < p.nk) ? list[tid] : 0;
+
+  // B operands (Q^T, dO^T) and the O row for this row's delta = dO . O,
+  // formed once the list is in place and the first key stages are on their
+  // way (the rows arrive meanwhile)
+  bf16x8 qf[DC], dof[DC], of[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     const unsigned col = (c * 16 + g * 8) * 2;
@@ -243,12 +253,8 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
     const unsigned oo = q_ok ? static_cast<unsigned>(q_row) * orb + col : 0x80000000u;
     qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 0));
     dof[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, oo, 0, 0));
-    const bf16x8 of = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) delta = __builtin_fmaf(static_cast<float>(dof[c][e]), static_cast<float>(of[e]), delta);
+    of[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0));
   }
-  delta = sum_pair32(delta);
-  if (q_ok && g == 0) p.delta[q_head + q_row] = delta;
   const float lse_raw = q_ok ? p.lse[q_head + q_row] : -INFINITY;
   // exponent base in log2 units; a row that admitted nothing has P = 0
   const float lse2 = (lse_raw == -INFINITY) ? INFINITY : lse_raw * kLog2e;
@@ -259,16 +265,12 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
 
-  // key-tile list: half qt % 2 of 256-row tile qt / 2. The list names the
-  // key tiles that either half sees; wave 0 keeps, in order, those this half
-  // sees (compacting in place: each 64-entry chunk is read before any of it
-  // is written, and no entry moves up). Without a block mask every key tile
-  // is visited as partial.
-  const int qp = qt >> 1, any_bit = 2 * (qt & 1), full_bit = any_bit + 1;
-  const int bm_b = (kv_count && p.bm_num_b > 1) ? b : 0;
-  const int* list = kv_count ? kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk : nullptr;
-  const int n_listed = kv_count ? kv_count[bm_b * p.nq + qp] : p.nk;
-  for (int i = tid; i < n_listed; i += kThreads) ents[i] = static_cast<Ent>(list ? list[i] : (i << 4));
+  // The list names the key tiles that either half sees; wave 0 keeps, in
+  // order, those this half sees (compacting in place: each 64-entry chunk is
+  // read before any of it is written, and no entry moves up). Without a
+  // block mask every key tile is visited as partial.
+  if (tid < n_listed) ents[tid] = static_cast<Ent>(list ? e_first : (tid << 4));
+  for (int i = tid + kThreads; i < n_listed; i += kThreads) ents[i] = static_cast<Ent>(list ? list[i] : (i << 4));
   if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
   __syncthreads();
@@ -323,6 +325,13 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
 
   if (T > 0) copy_stage(0, 0);
   if (T > 1) copy_stage(1, 1);
+  float delta = 0.f;
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) delta = __builtin_fmaf(static_cast<float>(dof[c][e]), static_cast<float>(of[c][e]), delta);
+  delta = sum_pair32(delta);
+  if (q_ok && g == 0) p.delta[q_head + q_row] = delta;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -905,24 +914,6 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   const int k_row = kt * kRows + pair * 32 + l32;
   const bool k_ok = k_row < p.Skv;
 
-  // B operand of this wave's first product: K^T (S = Q K^T) or V^T (dP = dO V^T);
-  // lane (key l32, half g) holds 8 consecutive d
-  bf16x8 bop[DC];
-  {
-    const void* base = first ? static_cast<const void*>(static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh)
-                             : static_cast<const void*>(static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh);
-    const unsigned rb = first ? krb : vrb;
-    const rsrc_t r = make_rsrc(base, static_cast<unsigned>(p.Skv - 1) * rb + RB);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const unsigned col = (c * 16 + g * 8) * 2;
-      const unsigned off = k_ok ? static_cast<unsigned>(k_row) * rb + col : 0x80000000u;
-      bop[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-  }
-  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
-  const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
-
   // the query stages that can see keys [k_lo, k_hi] of this tile (as in the
   // one-wave kernel)
   const bool causal = p.mask_kind & kMaskCausal;
@@ -943,33 +934,63 @@ void attn_bwd_dkdv2_kernel(BwdLaunch p) {
   // tiles are read in parallel (one entry per thread), the entries for this
   // key tile give their halves' classes, and wave 0 compacts the visited
   // stages in order. Without a block mask, or past kDkvMaxStages candidate
-  // stages, every candidate stage is visited with the mask.
+  // stages, every candidate stage is visited with the mask. The first pass's
+  // list lengths and entries are fetched before the K and V rows below, so
+  // that the list is in place while those arrive.
+  const bool use_list = DOCS && p.kv_count != nullptr && ns > 0 && ns <= kDkvMaxStages;
+  const int h0 = s0 >> 1, h1 = (s0 + ns - 1) >> 1;   // candidate halves, inclusive
+  const int qp0 = h0 >> 1, nqp = (h1 >> 1) - qp0 + 1;
+  const int bm_b = p.bm_num_b > 1 ? b : 0;
+  // thread t reads entry j of query tile qp0 + t / 32 + 16 m, j = t % 32 + 32 i
+  const int j0 = tid & 31;
+  int cnt0 = 0, e00 = 0;
+  if (use_list && (tid >> 5) < nqp) {
+    const int qp = qp0 + (tid >> 5);
+    cnt0 = p.kv_count[bm_b * p.nq + qp];
+    e00 = j0 < p.nk ? p.kv_list[(static_cast<size_t>(bm_b) * p.nq + qp) * p.nk + j0] : 0;
+  }
+
+  // B operand of this wave's first product: K^T (S = Q K^T) or V^T (dP = dO V^T);
+  // lane (key l32, half g) holds 8 consecutive d
+  bf16x8 bop[DC];
+  {
+    const void* base = first ? static_cast<const void*>(static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh)
+                             : static_cast<const void*>(static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh);
+    const unsigned rb = first ? krb : vrb;
+    const rsrc_t r = make_rsrc(base, static_cast<unsigned>(p.Skv - 1) * rb + RB);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const unsigned col = (c * 16 + g * 8) * 2;
+      const unsigned off = k_ok ? static_cast<unsigned>(k_row) * rb + col : 0x80000000u;
+      bop[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+  }
+  const int* doc_row = DOCS ? p.va.doc + static_cast<size_t>(b) * p.va.doc_stride : p.va.doc;
+  const int doc_k = (DOCS && k_ok) ? doc_row[k_row] : 0;
+
+
   int nvis = ns;
-  bool use_list = false;
   if constexpr (DOCS) {
-    use_list = p.kv_count != nullptr && ns > 0 && ns <= kDkvMaxStages;
     if (use_list) {
-      const int h0 = s0 >> 1, h1 = (s0 + ns - 1) >> 1;   // candidate halves, inclusive
       for (int i = tid; i <= h1 - h0; i += kDkv2Threads) hcls[i] = 0;
       __syncthreads();
-      const int bm_b = p.bm_num_b > 1 ? b : 0;
-      const int qp0 = h0 >> 1, nqp = (h1 >> 1) - qp0 + 1;
-      // thread t reads entry j of query tile qp0 + t / 32 + 16 m, j = t % 32 + 32 i
+      auto note = [&](int qp, int e) {
+        if ((e >> 4) == kt) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int h = 2 * qp + hf;
+            if (h >= h0 && h <= h1) hcls[h - h0] = static_cast<unsigned char>((e >> (2 * hf)) & 3);
+          }
+        }
+      };
       for (int m = 0; m * 16 < nqp; ++m) {
         const int qp = qp0 + m * 16 + (tid >> 5);
         if (qp - qp0 < nqp) {
-          const int cnt = p.kv_count[bm_b * p.nq + qp];
           const int* lst = p.kv_list + (static_cast<size_t>(bm_b) * p.nq + qp) * p.nk;
-          for (int j = tid & 31; j < cnt; j += 32) {
-            const int e = lst[j];
-            if ((e >> 4) == kt) {
-#pragma unroll
-              for (int hf = 0; hf < 2; ++hf) {
-                const int h = 2 * qp + hf;
-                if (h >= h0 && h <= h1) hcls[h - h0] = static_cast<unsigned char>((e >> (2 * hf)) & 3);
-              }
-            }
-          }
+          const int cnt = m == 0 ? cnt0 : p.kv_count[bm_b * p.nq + qp];
+          const int e0 = m == 0 ? e00 : (j0 < p.nk ? lst[j0] : 0);
+          if (j0 < cnt) note(qp, e0);
+          for (int j = j0 + 32; j < cnt; j += 32) note(qp, lst[j]);
         }
       }
       __syncthreads();
