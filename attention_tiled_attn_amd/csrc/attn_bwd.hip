@@ -268,9 +268,13 @@ void attn_bwd_dq_kernel(BwdLaunch p, const int* __restrict__ kv_count, const int
   // The list names the key tiles that either half sees; wave 0 keeps, in
   // order, those this half sees (compacting in place: each 64-entry chunk is
   // read before any of it is written, and no entry moves up). Without a
-  // block mask every key tile is visited as partial.
-  if (tid < n_listed) ents[tid] = static_cast<Ent>(list ? e_first : (tid << 4));
-  for (int i = tid + kThreads; i < n_listed; i += kThreads) ents[i] = static_cast<Ent>(list ? list[i] : (i << 4));
+  // block mask every key tile is visited as partial, except when there is no
+  // mask at all: then a tile wholly inside Skv is full.
+  auto unlisted = [&](int j) -> int {
+    return (j << 4) | ((p.mask_kind == 0 && (j + 1) * kTile <= p.Skv) ? 0xF : 0);
+  };
+  if (tid < n_listed) ents[tid] = static_cast<Ent>(list ? e_first : unlisted(tid));
+  for (int i = tid + kThreads; i < n_listed; i += kThreads) ents[i] = static_cast<Ent>(list ? list[i] : unlisted(i));
   if constexpr (MOD == kModRelBias) stage_rel_table(p.va, h, (lds_f32*)(rtab), tid, kThreads);
   lds_cf32* const tab = (lds_cf32*)(rtab) + p.va.rel_max;
   __syncthreads();

@@ -105,8 +105,19 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 // and one of p.splits contiguous parts of the key-tile list of query tile 0.
 // Without PACK, p.splits > 1 cuts every query tile's list the same way. Split
 // results go to the workspace and attn_decode_merge_kernel combines them.
+// Waves per SIMD: 2 (one workgroup per CU), or 4 (two workgroups per CU) at
+// D = 64, where a wave fits 128 registers and a workgroup ~57 KB of LDS. There
+// the softmax outweighs the products, and the other workgroup's waves add
+// vector issue slots (A/B on one box: alibi_d64 +12%, softcap_d64 +18%, doc_swa
+// at D = 64 +29%, dense at D = 64 +6%). Not with the relative-bias table or in
+// decode mode, whose registers do not fit 128 without spilling (6% and 11%
+// slower measured).
+template <int D, int MOD, bool PACK>
+constexpr int kWavesPerSimd = (D == 64 && !PACK && MOD != kModRelBias) ? 4 : 2;
+
 template <int D, int MOD, bool DOCS, bool PACK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, MOD, PACK>, kWavesPerSimd<D, MOD, PACK>)))
 void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = PGeo<D>;
   constexpr int DC = D / 16;   // 16-wide d chunks (k-steps of S^T)
@@ -240,7 +251,12 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   } else {
     n_entries = n_head;
   }
-  if (!list) e_head = 0x5;
+  // Without a block mask a key tile is partial (every element tested), except
+  // when there is no mask at all: then a tile wholly inside Skv is full.
+  auto unlisted = [&](int j) -> int {
+    return (j << 4) | ((p.mask_kind == 0 && (j + 1) * kTile <= p.Skv) ? 0xF : 0x5);
+  };
+  if (!list) e_head = unlisted(0);
 
   // Q^T fragments (B operand of S^T): rows past Sq (and, in decode mode,
   // packed rows past the group) read as zero
@@ -339,7 +355,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // either half admits a pair, and skips the per-element mask only when
     // both halves are full (half 1 has no rows when Sq <= 128)
     for (int i = tid; i < n_entries; i += kThreads) {
-      const int e = list ? list[e_first + i] : (((e_first + i) << 4) | 0x5);
+      const int e = list ? list[e_first + i] : unlisted(e_first + i);
       const bool full = (e & 2) && ((e & 8) || p.Sq <= kPairHalf);
       ents[i] = (e & ~15) | ((e & 5) ? (full ? 0xF : 0x5) : 0);
     }
@@ -351,7 +367,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     }
     for (; i < n_entries; i += kThreads) ents[i] = list[e_first + i];
   } else {
-    for (int i = tid; i < n_entries; i += kThreads) ents[i] = ((e_first + i) << 4) | 0x5;
+    for (int i = tid; i < n_entries; i += kThreads) ents[i] = unlisted(e_first + i);
   }
   if constexpr (MOD == kModRelBias) {
     // decode mode: the tables of all rep heads of the group, one after another
@@ -383,6 +399,11 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // the loop body, and which stage comes first depends on the block mask.
   float m_run = -INFINITY;
   asm("" : "+v"(m_run));
+  // Kept beside it, so that a stage needs no test of m_run against -inf:
+  // the exponent base (m_run, or 0 while the row has none) and the rescale
+  // threshold (kRescaleLog2 above the base, or -inf while there is none).
+  float base_run = 0.f, thr_run = -INFINITY;
+  asm("" : "+v"(base_run), "+v"(thr_run));
   float l_run = 0.f;
   using SM = ScoreMod<MOD>;
   const int q_pos = q_row + p.va.q_offset;   // position in the key sequence
@@ -392,6 +413,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     return L;
   }();
   const int doc_q = (DOCS && q_ok) ? doc_row[q_pos] : 0;
+  // lanes of real rows: wave-wide softmax decisions are voted by these only
+  const uint64_t qmask = __builtin_amdgcn_ballot_w64(q_ok);
+  auto rows_any = [&](bool c) { return (__builtin_amdgcn_ballot_w64(c) & qmask) != 0; };
 
   constexpr int KB = G::kKB, CH = G::kCH;
   bf16x8 pf[CH];
@@ -447,7 +471,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // u = t - base0: the modified scores in log2 units, measured from this
     // lane's exponent base at the start of the stage (0 while it has none);
     // each score mod folds the base into a per-stage constant
-    const float base0 = (m_run == -INFINITY) ? 0.f : m_run;
+    const float base0 = base_run;
     const int dk0 = kv0 + 4 * g - q_pos;   // key kv0 + 4 g + c is at distance dk0 + c
     float t[KB * 16];
     // Relative bias: when every distance of the stage, over the wave's 32
@@ -502,7 +526,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       if constexpr (DOCS) {
         const int lk = labbuf[ring * kBN + (lane & (kBN - 1))];
         const int l0 = __builtin_amdgcn_readfirstlane(lk);
-        if (__all(lk == l0)) {
+        if (wave_all(lk == l0)) {
           if (doc_q != l0) hi_c = -1;
         } else {
           need_doc = true;
@@ -512,8 +536,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       // Each test runs only when some lane of the wave needs it (a stage on
       // the diagonal needs the upper bound alone, one on the window's far
       // edge the lower bound alone), as one compare and one select per element.
-      const bool need_lo = !__all(lo_c <= 0);
-      const bool need_hi = !__all(hi_c >= kBN - 1);
+      const bool need_lo = !wave_all(lo_c <= 0);
+      const bool need_hi = !wave_all(hi_c >= kBN - 1);
       if (need_doc) {
         const int* lab = labbuf + ring * kBN + 4 * g;
 #pragma unroll
@@ -545,7 +569,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // P = exp2(t) rounded to bf16 into pf; returns this lane's fp32 sum of
     // the unrounded values
     auto exps = [&]() -> float {
-      float acc = 0.f;
+      // four partial sums, so that the adds form four short chains instead
+      // of one long one (-0 + x = x, so the first add of each folds away)
+      float acc4[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
         const int kb = ch >> 1, r0 = (ch & 1) * 8;
@@ -557,12 +583,12 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
           const float p0 = poly ? exp2_poly(x0) : __builtin_amdgcn_exp2f(x0);
           const float p1 = poly ? exp2_poly(x1) : __builtin_amdgcn_exp2f(x1);
           w[j] = pack_bf16(p0, p1);
-          acc += p0 + p1;
+          acc4[j] += p0 + p1;
         }
         const u32x4 wv = {w[0], w[1], w[2], w[3]};
         pf[ch] = __builtin_bit_cast(bf16x8, wv);
       }
-      return acc;
+      return (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     };
     float ls = 0.f;
     // Exponent base. Any base gives the same O / l and base + log2 l in exact
@@ -584,29 +610,38 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     // admits in a partial one, and must not make the real rows of its wave
     // rescale in one case and not in the other.
     bool need_max = true;
-    float grow = kRescaleLog2;
+    bool checked = false;   // soft-capping: the stage failed the sum check
     if constexpr (MOD == kModSoftcap) {
-      if (!__any(q_ok && m_run == -INFINITY)) {
+      if (!rows_any(m_run == -INFINITY)) {
         ls = exps();
-        need_max = __any(q_ok && !(ls <= kSumLimit));
-        grow = 0.f;
+        need_max = rows_any(!(ls <= kSumLimit));
+        checked = true;
       }
     }
     if (need_max) {
-      float mx = -INFINITY;
+      // row max as four chains of three-input maxima, joined at the end
+      float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int i = 0; i < KB * 16; ++i) mx = fmaxf(mx, t[i]);
-      mx = max_pair32(mx);   // the row max, relative to base0
-      if (__any(q_ok && mx > (m_run == -INFINITY ? -INFINITY : grow))) {
+      for (int i = 0; i < KB * 16; i += 8)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx4[c] = fmaxf(fmaxf(mx4[c], t[i + c]), t[i + 4 + c]);
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = max_pair32_nn(mx);   // the row max, relative to base0
+      // after a failed check every real row has a base: move it on any growth
+      const float thr = checked ? 0.f : thr_run;
+      if (rows_any(mx > thr)) {
         const float m_new = fmaxf(m_run, mx + base0);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] *= alpha;
-        const float shift = (m_new == -INFINITY) ? 0.f : m_new - base0;
+        const float shift = none ? 0.f : m_new - base0;
 #pragma unroll
         for (int i = 0; i < KB * 16; ++i) t[i] -= shift;
         m_run = m_new;
+        base_run = none ? 0.f : m_new;
+        thr_run = none ? -INFINITY : kRescaleLog2;
       }
       ls = exps();
     }

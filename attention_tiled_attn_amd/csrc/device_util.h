@@ -27,6 +27,18 @@ __device__ inline float max_pair32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// The same row max without the canonicalising v_max of each input that
+// fmaxf needs in IEEE mode (the median of a, b and +inf is max(a, b) for any
+// a, b that are not NaN).
+__device__ inline float max_pair32_nn(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float inf = __builtin_inff();
+  asm("" : "+s"(inf));   // opaque, or the median is folded back into fmaxf
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), inf);
+}
+// wave-wide votes over the active lanes, as one compare and a scalar test
+__device__ inline bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+__device__ inline bool wave_all(bool c) { return __builtin_amdgcn_ballot_w64(!c) == 0; }
 __device__ inline float sum_pair32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -89,7 +89,7 @@ def test_relative_bias_fp32_path(D, R):
 def test_null_block_mask_is_bitwise_equal():
     # the last two have padding rows past Sq in waves with real rows, beside
     # full tiles: the padding rows must not sway the rescale of the real ones
-    for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict(),
+    for var in (dict(causal=True), dict(documents=True, causal=True, window=60), dict(), dict(mod="alibi"),
                 dict(S=1800, documents=True, causal=True, window=300, doc_range=(60, 700)),
                 dict(S=1000, documents=True, mod="softcap", softcap=5.0, doc_range=(60, 700))):
         var = {"S": 520, **var}
