@@ -174,11 +174,16 @@ __device__ inline float mod_score(float s, const VariantArgs& va, float slope2, 
 // under 64 KB of LDS and a wave under 256 registers at D <= 128, so two
 // workgroups share a CU (two waves per SIMD: one's matrix products overlap
 // the other's vector work). dK/dV: 64 query rows (32 at D = 256, where a
-// 64-row tile would not leave room for the three-stage rings), one wave per
-// SIMD: its accumulators and K^T, V^T fragments need more than 256 registers.
+// 64-row tile would not leave room for the three-stage rings); at D = 64 and
+// 128 two waves split each key block's work and share a SIMD, at D = 256 one
+// wave per SIMD holds the accumulators and K^T, V^T fragments (more than 256
+// registers).
 template <int D> constexpr int kDqStage = 32;
 template <int D> constexpr int kDkvStage = D == 256 ? 32 : 64;
-template <int D> constexpr int kDqWaves = D == 256 ? 1 : 2;   // waves per SIMD
+// waves per SIMD; at D = 64 three dQ workgroups share a CU (registers under
+// 168 and 41-45 KB of LDS each): alibi_d64 backward +2.7%, doc_swa at D = 64
+// +6% against two (A/B on one box)
+template <int D> constexpr int kDqWaves = D == 256 ? 1 : D == 64 ? 3 : 2;
 
 // dQ (and delta)
 template <int D, int MOD, bool DOCS>

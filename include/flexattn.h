@@ -213,8 +213,11 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
  *   mask_kind, mod_kind, params: the variant (see above)
  *   block_mask: from flexattn_build_block_mask for the same mask_kind, sizes
  *           and params, or NULL to visit every key tile with the per-element
- *           mask (correct for any mask, slower). Results are bitwise equal
- *           either way.
+ *           mask (correct for any mask, slower). With mask_kind 0 (no mask)
+ *           NULL costs nothing: every key tile inside Skv is then taken as
+ *           full, the last one partial when Skv is not a multiple of
+ *           FLEXATTN_TILE, as the built mask would classify them. Results are
+ *           bitwise equal either way.
  * Query head h reads key/value head h / (H / Hkv). */
 int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                  int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
