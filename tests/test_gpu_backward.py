@@ -240,15 +240,17 @@ def test_backward_strided_layouts(var, D):
 # ------------------------------------------------------------------ full size, as the bench runs it
 @pytest.mark.parametrize("name,b,kvh", [("dense", 3, 5), ("causal_gqa", 1, 6)])
 def test_backward_full_size_one_group(name, b, kvh):
-    """The bench's backward (whole workload, block mask, one launch of each
-    kernel), checked on one batch row and one key/value head: the oracle's
-    gradients of that slice (its query heads' dQ, the head's dK and dV) are
-    exact, since no other slice feeds them."""
+    """The bench's backward (whole workload, one launch of each kernel, with
+    the block mask of a masked variant and none for an unmasked one, as the
+    bench runs them), checked on one batch row and one key/value head: the
+    oracle's gradients of that slice (its query heads' dQ, the head's dK and
+    dV) are exact, since no other slice feeds them."""
     from workload import WORKLOADS, make_inputs
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
     say(f"[bwd] full-size {name}: gpu")
-    (dq, dk, dv), dout = run_bwd(inp, seed=wl.seed)
+    bm = "auto" if device_variant(inp).mask_kind else None
+    (dq, dk, dv), dout = run_bwd(inp, block_mask=bm, seed=wl.seed)
     rep = wl.H // wl.Hkv
     heads = list(range(kvh * rep, (kvh + 1) * rep))
     q = bf16_values(inp.q[b:b + 1, heads])
