@@ -30,6 +30,10 @@ OUT = os.path.join(HERE, "libflexattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_bwd.hip", "block_mask.hip", "api.cpp"]
+# microbenchmarks of the units the kernels use (measurement tooling, its own
+# library; attention_tiled_attn_amd.microbench runs them)
+MB_SOURCE = "microbench.hip"
+MB_OUT = os.path.join(HERE, "libflexattn_mb.so")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -58,20 +62,28 @@ def _compile(src: str, obj: str, verbose: bool, defines=()) -> None:
         print(r.stderr, file=sys.stderr)
 
 
-def build(verbose: bool = False, defines=()) -> str:
-    bdir = os.path.join(HERE, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        list(ex.map(lambda a: _compile(a[0], a[1], verbose, defines), zip(SOURCES, objs)))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, defines=()) -> str:
+    """Build libflexattn.so (returned) and the microbenchmark library
+    libflexattn_mb.so beside it."""
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    srcs = SOURCES + [MB_SOURCE]
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        list(ex.map(lambda a: _compile(a[0], a[1], verbose, defines), zip(srcs, objs)))
+    _link(objs[:-1], OUT, verbose)
+    _link(objs[-1:], MB_OUT, verbose)
     return OUT
 
 
