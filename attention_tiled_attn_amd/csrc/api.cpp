@@ -4,10 +4,13 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <string>
 
 #include "../../include/flexattn.h"
 #include "launch.h"
@@ -22,6 +25,42 @@ int hip_fail(hipError_t e, const char* where) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
                 static_cast<int>(e));
   return FLEXATTN_ERR_HIP;
+}
+
+// ---- dispatch log. FLEXATTN_LOG set to anything but "" or "0" makes every
+// entry point that can launch work print one line on stderr when it returns:
+// its arguments, each kernel it launched (template arguments, grid and
+// workgroup size) and its status. Read once per process; when off, a call
+// pays one test of a cached flag.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* s = std::getenv("FLEXATTN_LOG");
+    return s && *s && std::strcmp(s, "0") != 0;
+  }();
+  return on;
+}
+
+thread_local std::string g_launches;   // kernels noted by the current call
+
+void log_begin() {
+  if (log_enabled()) g_launches.clear();
+}
+
+const char* dtype_name(const flexattn_params* prm) {
+  if (!prm) return "bf16";
+  return prm->dtype == FLEXATTN_BF16 ? "bf16" : prm->dtype == FLEXATTN_FP32 ? "fp32" : "?";
+}
+
+__attribute__((format(printf, 3, 4))) void log_end(const char* entry, int status, const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char args[384];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(args, sizeof(args), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[flexattn] %s(%s) -> %s -> %d (%s)\n", entry, args,
+               g_launches.empty() ? "no launch" : g_launches.c_str(), status, flexattn_strerror(status));
+  g_launches.clear();
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -113,6 +152,21 @@ int check_mask_args(int mask_kind, const flexattn_params* prm, int B, int Sq, in
 
 }  // namespace
 
+namespace fa {
+
+void note_launch(const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char line[192];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  if (!g_launches.empty()) g_launches += "; ";
+  g_launches += line;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int flexattn_version(void) { return FLEXATTN_VERSION; }
@@ -143,8 +197,8 @@ size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind) {
   return nb * nq * (1 + nk) * sizeof(int);
 }
 
-int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
-                              void* buf, size_t bytes, flexattn_block_mask* out, void* stream) {
+static int build_block_mask_body(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
+                                 void* buf, size_t bytes, flexattn_block_mask* out, void* stream) {
   const flexattn_params* prm = params ? params : &kDefaultParams;
   if (!buf || !out) return FLEXATTN_ERR_NULLPTR;
   int st = check_mask_args(mask_kind, prm, B, Sq, Skv);
@@ -193,6 +247,15 @@ int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int 
   out->q_offset = key.q_offset;
   out->prefix = key.prefix;
   return FLEXATTN_OK;
+}
+
+int flexattn_build_block_mask(int mask_kind, const flexattn_params* params, int B, int Sq, int Skv,
+                              void* buf, size_t bytes, flexattn_block_mask* out, void* stream) {
+  log_begin();
+  const int st = build_block_mask_body(mask_kind, params, B, Sq, Skv, buf, bytes, out, stream);
+  log_end("flexattn_build_block_mask", st, "mask=0x%x B=%d Sq=%d Skv=%d bytes=%zu stream=%p", mask_kind, B, Sq,
+          Skv, bytes, stream);
+  return st;
 }
 
 }  // extern "C"
@@ -268,10 +331,10 @@ void fill_variant(fa::VariantArgs& va, const flexattn_params* prm, float scale, 
 
 extern "C" {
 
-int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
-                 const flexattn_params* params, const flexattn_block_mask* block_mask,
-                 void* stream) {
+static int fwd_body(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                    const flexattn_params* params, const flexattn_block_mask* block_mask,
+                    void* stream) {
   const flexattn_params* prm = params ? params : &kDefaultParams;
   if (!q || !k || !v || !out) return FLEXATTN_ERR_NULLPTR;
   int st = check_attn_args(prm, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, block_mask);
@@ -322,6 +385,19 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   hipError_t e = fa::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return FLEXATTN_OK;
+}
+
+int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream) {
+  log_begin();
+  const int st = fwd_body(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params,
+                          block_mask, stream);
+  log_end("flexattn_fwd", st, "B=%d H=%d Hkv=%d Sq=%d Skv=%d D=%d %s scale=%g mask=0x%x mod=%d block_mask=%s lse=%s stream=%p",
+          B, H, Hkv, Sq, Skv, D, dtype_name(params), scale, mask_kind, mod_kind, block_mask ? "given" : "none",
+          lse ? "yes" : "no", stream);
+  return st;
 }
 
 size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits) {
@@ -472,23 +548,33 @@ int flexattn_decode(const void* q, const void* k, const void* v, void* out, floa
                     int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
                     const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params, block_mask,
-                     splits, workspace, workspace_bytes, false, stream);
+  log_begin();
+  const int st = decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params,
+                             block_mask, splits, workspace, workspace_bytes, false, stream);
+  log_end("flexattn_decode", st, "B=%d H=%d Hkv=%d Sq=%d Skv=%d D=%d %s scale=%g mask=0x%x mod=%d block_mask=%s splits=%d workspace_bytes=%zu stream=%p",
+          B, H, Hkv, Sq, Skv, D, dtype_name(params), scale, mask_kind, mod_kind, block_mask ? "given" : "none",
+          splits, workspace_bytes, stream);
+  return st;
 }
 
 int flexattn_decode_static(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                            int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
                            const flexattn_params* params, const flexattn_block_mask* block_mask, int splits,
                            void* stream) {
-  return decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params, block_mask,
-                     splits, nullptr, 0, true, stream);
+  log_begin();
+  const int st = decode_impl(q, k, v, out, lse, B, H, Hkv, Sq, Skv, D, scale, mask_kind, mod_kind, params,
+                             block_mask, splits, nullptr, 0, true, stream);
+  log_end("flexattn_decode_static", st, "B=%d H=%d Hkv=%d Sq=%d Skv=%d D=%d %s scale=%g mask=0x%x mod=%d block_mask=%s splits=%d stream=%p",
+          B, H, Hkv, Sq, Skv, D, dtype_name(params), scale, mask_kind, mod_kind, block_mask ? "given" : "none",
+          splits, stream);
+  return st;
 }
 
-int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
-                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
-                 const flexattn_params* params, const flexattn_block_mask* block_mask,
-                 void* stream) {
+static int bwd_body(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                    int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                    const flexattn_params* params, const flexattn_block_mask* block_mask,
+                    void* stream) {
   const flexattn_params* prm = params ? params : &kDefaultParams;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
     return FLEXATTN_ERR_NULLPTR;
@@ -549,6 +635,20 @@ int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, c
   hipError_t e = fa::launch_attn_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return FLEXATTN_OK;
+}
+
+int flexattn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                 int Hkv, int Sq, int Skv, int D, float scale, int mask_kind, int mod_kind,
+                 const flexattn_params* params, const flexattn_block_mask* block_mask,
+                 void* stream) {
+  log_begin();
+  const int st = bwd_body(q, k, v, out, lse, dout, dq, dk, dv, delta, B, H, Hkv, Sq, Skv, D, scale, mask_kind,
+                          mod_kind, params, block_mask, stream);
+  log_end("flexattn_bwd", st, "B=%d H=%d Hkv=%d Sq=%d Skv=%d D=%d %s scale=%g mask=0x%x mod=%d block_mask=%s stream=%p",
+          B, H, Hkv, Sq, Skv, D, dtype_name(params), scale, mask_kind, mod_kind, block_mask ? "given" : "none",
+          stream);
+  return st;
 }
 
 }  // extern "C"

@@ -1356,6 +1356,8 @@ hipError_t launch_t(const BwdLaunch& p, hipStream_t stream) {
   {
     const long long total = static_cast<long long>(p.B) * p.H * ((p.Sq + kRows - 1) / kRows);
     const long long per = (total + kXcds - 1) / kXcds;
+    note_launch("attn_bwd_dq_kernel<%d, %d, %s> grid %lld x %d", D, MOD, DOCS ? "true" : "false", per * kXcds,
+                kThreads);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
                        dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
     const hipError_t e = hipGetLastError();
@@ -1364,9 +1366,13 @@ hipError_t launch_t(const BwdLaunch& p, hipStream_t stream) {
   const long long total = static_cast<long long>(p.B) * p.Hkv * ((p.Skv + kRows - 1) / kRows);
   const long long per = (total + kXcds - 1) / kXcds;
   if constexpr (D <= 128) {
+    note_launch("attn_bwd_dkdv2_kernel<%d, %d, %s> grid %lld x %d", D, MOD, DOCS ? "true" : "false", per * kXcds,
+                kDkv2Threads);
     hipLaunchKernelGGL((attn_bwd_dkdv2_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
                        dim3(kDkv2Threads), 0, stream, p);
   } else {
+    note_launch("attn_bwd_dkdv_kernel<%d, %d, %s> grid %lld x %d", D, MOD, DOCS ? "true" : "false", per * kXcds,
+                kThreads);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MOD, DOCS>), dim3(static_cast<unsigned>(per * kXcds)),
                        dim3(kThreads), 0, stream, p);
   }

@@ -432,6 +432,8 @@ hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const long long total = static_cast<long long>(p.B) * p.H * nq;
   const long long per = (total + kXcds - 1) / kXcds;
   dim3 grid(static_cast<unsigned>(per * kXcds));
+  note_launch("attn_fwd_kernel<%d, %d, %s, %s> grid %lld x %d", D, MOD, F32 ? "true" : "false",
+              DOCS ? "true" : "false", per * kXcds, kThreads);
   hipLaunchKernelGGL((attn_fwd_kernel<D, MOD, F32, DOCS>), grid, dim3(kThreads), 0, stream, p,
                      p.kv_count, p.kv_list);
   return hipGetLastError();

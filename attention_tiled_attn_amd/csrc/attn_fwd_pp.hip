@@ -803,6 +803,8 @@ hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const long long total = (PACK ? static_cast<long long>(p.B) * p.Hkv
                                 : static_cast<long long>(p.B) * p.H * np) * p.splits;
   const long long per = (total + kXcds - 1) / kXcds;
+  note_launch("attn_fwd_pp_kernel<%d, %d, %s, %s> grid %lld x %d splits %d", D, MOD, DOCS ? "true" : "false",
+              PACK ? "true" : "false", per * kXcds, kThreads, p.splits);
   hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS, PACK>), dim3(static_cast<unsigned>(per * kXcds)),
                      dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
   return hipGetLastError();
@@ -900,6 +902,7 @@ hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
   hipError_t e = pack ? launch_dims<true>(p, stream) : launch_dims<false>(p, stream);
   if (e != hipSuccess || p.splits <= 1) return e;
   const long long n = static_cast<long long>(p.B) * p.Hkv * (p.H / p.Hkv) * p.Sq * (p.D / 4);
+  note_launch("attn_decode_merge_kernel grid %lld x 256", (n + 255) / 256);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();

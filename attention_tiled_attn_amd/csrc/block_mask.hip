@@ -283,6 +283,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 
 hipError_t launch_block_mask(const MaskLaunch& p, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(p.nq), static_cast<unsigned>(p.num_b));
+  note_launch("block_mask_kernel grid %d x %d x 64", p.nq, p.num_b);
   hipLaunchKernelGGL(block_mask_kernel, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }

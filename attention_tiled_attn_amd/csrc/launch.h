@@ -99,4 +99,9 @@ struct MaskLaunch {
 
 hipError_t launch_block_mask(const MaskLaunch& p, hipStream_t stream);
 
+// Dispatch log (FLEXATTN_LOG): the launch functions note each kernel they
+// launch (name, template arguments, grid), printf-style; the entry point
+// prints the notes of its call when it returns. No-op when the log is off.
+__attribute__((format(printf, 1, 2))) void note_launch(const char* fmt, ...);
+
 }  // namespace fa

@@ -182,6 +182,13 @@ const char* flexattn_strerror(int status);
 /* Detail text of the last FLEXATTN_ERR_HIP returned on this thread ("" if none). */
 const char* flexattn_last_error(void);
 
+/* Dispatch log: when the environment variable FLEXATTN_LOG is set to anything
+ * but "" or "0" (read once per process), flexattn_fwd, flexattn_decode,
+ * flexattn_decode_static, flexattn_bwd and flexattn_build_block_mask each
+ * print one line on stderr as they return: "[flexattn] <entry>(<arguments>)
+ * -> <kernels launched, with template arguments and grid, or 'no launch'>
+ * -> <status> (<flexattn_strerror text>)". */
+
 /* Bytes of device memory flexattn_build_block_mask needs for these sizes
  * (int32 counts and lists). Returns 0 for invalid sizes or mask kinds. */
 size_t flexattn_block_mask_bytes(int B, int Sq, int Skv, int mask_kind);
