@@ -13,7 +13,8 @@ attention library) on cuda:0 and reports, per unit:
   one wave issuing both;
 * interference: a wave multiplying while the other wave of its SIMD issues
   FMAs or exponentials; the extra matrix cycles per instruction of the other
-  wave;
+  wave, and the other way round, the vector wave's cycles per instruction
+  while every one of its instructions has a multiplying partner;
 * LDS: bytes per clock per CU read with ds_read_b128 (conflict-free rows) and
   with the transposing ds_read_b64_tr_b16;
 * HBM: read and copy bandwidth over 1 GiB.
@@ -88,7 +89,9 @@ def run() -> dict:
     lib = _lib()
     out = {"gpu": torch.cuda.get_device_name(0)}
 
-    # matrix cores
+    # matrix cores. Cycles per MFMA per SIMD over the launch (event time x
+    # clock): the two waves of a SIMD need not run over the same interval, so
+    # one wave's own span says nothing about the SIMD's rate then
     for wps in (1, 2):
         r, t = _units(lib, torch, MFMA, wps, 4000)
         cyc = st.median(c for c, _, _ in r)
@@ -96,10 +99,10 @@ def run() -> dict:
         clk = st.median(c / (w / REALTIME_HZ) for c, w, _ in r) / 1e9
         total = sum(o for _, _, o in r)
         out[f"mfma_{wps}w"] = {
-            "cycles_per_mfma_per_simd": cyc / (ops * wps),
+            "cycles_per_mfma_per_simd": t * clk * 1e9 / (ops * wps),
+            "wave_cycles_per_own_mfma": cyc / ops,
             "clock_ghz": clk,
             "tflops": total * MFMA_FLOP / t / 1e12,
-            "tflops_at_clock_limit": CUS * 4 * MFMA_FLOP / (cyc / (ops * wps)) * clk * 1e9 / 1e12,
             # the longest wave by the real-time counter against the launch's
             # event time: checks the counter's assumed 100 MHz
             "realtime_over_events": max(w for _, w, _ in r) / REALTIME_HZ / t,
@@ -126,7 +129,7 @@ def run() -> dict:
     # per partner instruction takes the partner's issue interval from its
     # one-wave run (an estimate: its interval while the MFMA wave runs is not
     # observed on its own).
-    base = out["mfma_1w"]["cycles_per_mfma_per_simd"]
+    base = out["mfma_1w"]["wave_cycles_per_own_mfma"]
     for kind, name, viters in ((MIX_FMA, "fma", 60000), (MIX_EXP, "exp", 30000)):
         r, _ = _units(lib, torch, kind, 2, 4000, viters)
         m_rows, v_rows = _wave_rows(r, 2, 0), _wave_rows(r, 2, 1)
@@ -139,6 +142,19 @@ def run() -> dict:
             "partner_instr_per_mfma": cpm / solo,
             "extra_mfma_cycles_per_partner_instr": (cpm - base) / (cpm / solo),
             "partner_outlasted_mfma_waves": st.median(c for c, _, _ in v_rows) >= mc,
+        }
+        # the vector wave's own rate beside the products: a vector loop a
+        # third as long as the MFMA loop (by the one-wave rates), so that it
+        # ends while its partner is still multiplying
+        short = max(1, int(mc / 3 / (solo * 16)))
+        r, _ = _units(lib, torch, kind, 2, 4000, short)
+        m_rows, v_rows = _wave_rows(r, 2, 0), _wave_rows(r, 2, 1)
+        vc = st.median(c for c, _, _ in v_rows)
+        out[f"{name}_beside_mfma"] = {
+            "cycles_per_instr": vc / v_rows[0][2],
+            "alone_cycles_per_instr": solo,
+            "slowdown": vc / v_rows[0][2] / solo,
+            "ended_before_mfma_waves": vc < st.median(c for c, _, _ in m_rows),
         }
     # LDS
     for wps in (1, 2):
