@@ -112,14 +112,22 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 // at D = 64 +29%, dense at D = 64 +6%). Not with the relative-bias table or in
 // decode mode, whose registers do not fit 128 without spilling (6% and 11%
 // slower measured).
-template <int D, int MOD, bool PACK>
+template <int D, int MOD, int PACK>
 constexpr int kWavesPerSimd = (D == 64 && !PACK && MOD != kModRelBias) ? 4 : 2;
 
-template <int D, int MOD, bool DOCS, bool PACK>
+// PACK: 0 the regular mapping; 1 decode mode; 2 decode mode with at most 32
+// packed rows (D <= 128), whose rows sit in wave 0 of both groups: each of
+// the two waves takes one 32-key half of every stage with a running softmax
+// of its own, and the two are merged once after the loop. Both waves share
+// SIMD 0, so one's products overlap the other's softmax, where with the rows
+// in one wave a stage costs that wave's matrix and vector work back to back.
+template <int D, int MOD, bool DOCS, int PACK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, MOD, PACK>, kWavesPerSimd<D, MOD, PACK>)))
 void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = PGeo<D>;
+  constexpr bool KS = PACK == 2;   // key halves split between the groups
+  static_assert(!KS || D <= 128, "key split needs 64-key stages");
   constexpr int DC = D / 16;   // 16-wide d chunks (k-steps of S^T)
   constexpr int DB = D / 32;   // 32-row d blocks of O^T
   constexpr int RB = G::kRowBytes;
@@ -199,7 +207,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const int b = PACK ? item / p.Hkv : slice / p.H;
   const int kvh = PACK ? item % p.Hkv : (slice % p.H) / rep;
   // this lane's row: packed index r (decode mode), its query head and row
-  const int r_lane = grp * kPairHalf + wq * 32 + l32;
+  const int r_lane = (KS ? 0 : grp * kPairHalf) + wq * 32 + l32;
   const int hl = PACK ? min(r_lane / p.Sq, rep - 1) : 0;
   const int h = PACK ? kvh * rep + hl : slice % p.H;   // lane-varying in decode mode
   const int q_row = PACK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
@@ -417,7 +425,10 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   const uint64_t qmask = __builtin_amdgcn_ballot_w64(q_ok);
   auto rows_any = [&](bool c) { return (__builtin_amdgcn_ballot_w64(c) & qmask) != 0; };
 
-  constexpr int KB = G::kKB, CH = G::kCH;
+  // a wave's keys of a stage: all, or (key split) its group's 32-key half
+  constexpr int KB = KS ? 1 : G::kKB, CH = KS ? 2 : G::kCH;
+  constexpr int kBW = KB * 32;
+  const int koff_w = KS ? 32 * grp : 0;
   bf16x8 pf[CH];
 
   // S^T(t) = K(t) Q^T: KB 32-key blocks, fragment reads 4 ahead of the MFMAs
@@ -429,7 +440,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     for (int c = 0; c < DC; ++c)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff_at(c) + kb * 32 * RB);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff_at(c) + (kb * 32 + koff_w) * RB);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
@@ -450,7 +461,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
-        const unsigned char* a0 = vb + voff_at(db) + (16 * ch) * RB;
+        const unsigned char* a0 = vb + voff_at(db) + (16 * ch + koff_w) * RB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * RB));
         const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -485,7 +496,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       const int qw = PACK ? p.va.q_offset : __builtin_amdgcn_readfirstlane(q_pos);
       const int span = PACK ? p.Sq - 1 : 31;
       const int R = p.va.rel_max;
-      const bool below = kv0 + kBN - 1 - qw < -R;   // largest distance below -R
+      const bool below = kv0 + kBW - 1 - qw < -R;   // largest distance below -R
       const bool above = kv0 - (qw + span) > R;     // smallest distance above R
       clipped = below || above;
       if (clipped) clip_add = sml.tab[below ? -R : R] * kLog2e;
@@ -507,7 +518,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       // The causal part (with its prefix), the window and the key range each
       // admit an interval of key positions for this row, so together they
       // admit keys kk0 + c for c in [lo, hi], where element (kb, i, e) of this
-      // lane is key kk0 + c with c = 32 kb + 8 i + e (0 <= c <= kBN - 5).
+      // lane is key kk0 + c with c = 32 kb + 8 i + e (0 <= c <= kBW - 5).
       // Bounds are formed in 64 bits and clamped to the stage.
       const bool causal = p.mask_kind & kMaskCausal;
       const bool window = p.mask_kind & kMaskWindow;
@@ -516,15 +527,15 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       long long hi = static_cast<long long>(p.Skv) - 1 - kk0;
       if (causal) hi = min(hi, max(d, static_cast<long long>(p.va.prefix) - 1 - kk0));
       const long long lo = window ? d - p.va.window + 1 : 0LL;
-      int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBN)));
-      int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBN)));
+      int hi_c = static_cast<int>(min(max(hi, -1LL), static_cast<long long>(kBW)));
+      int lo_c = static_cast<int>(min(max(lo, 0LL), static_cast<long long>(kBW)));
       // Documents: when the stage's keys all carry one label, a row's label
       // test has one answer for all of them and is folded into the interval
       // (a row of another document admits none); otherwise every element
       // compares its key's staged label with the row's.
       bool need_doc = false;
       if constexpr (DOCS) {
-        const int lk = labbuf[ring * kBN + (lane & (kBN - 1))];
+        const int lk = labbuf[ring * kBN + koff_w + (lane & (kBW - 1))];
         const int l0 = __builtin_amdgcn_readfirstlane(lk);
         if (wave_all(lk == l0)) {
           if (doc_q != l0) hi_c = -1;
@@ -537,9 +548,9 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       // the diagonal needs the upper bound alone, one on the window's far
       // edge the lower bound alone), as one compare and one select per element.
       const bool need_lo = !wave_all(lo_c <= 0);
-      const bool need_hi = !wave_all(hi_c >= kBN - 1);
+      const bool need_hi = !wave_all(hi_c >= kBW - 1);
       if (need_doc) {
-        const int* lab = labbuf + ring * kBN + 4 * g;
+        const int* lab = labbuf + ring * kBN + koff_w + 4 * g;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -696,7 +707,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
     // vector slot
     const int e_n2 = ent(u + 2);
-    if (do_s) softmax(s, stage_kv0(ord(u), __builtin_amdgcn_readfirstlane(e_cur)), ((ec >> 1) & 1) != 0, ring);
+    if (do_s)
+      softmax(s, stage_kv0(ord(u), __builtin_amdgcn_readfirstlane(e_cur)) + koff_w, ((ec >> 1) & 1) != 0, ring);
     if (u + 2 < T) {
       issue_copy(ord(u + 2), __builtin_amdgcn_readfirstlane(e_n2), ring_old);
       wait_prev_stage();   // this group's copies of stage u + 1 are complete
@@ -724,13 +736,47 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   }
   if (!kInPhase && grp == 0) __syncthreads();   // matches group 1's extra barrier
 
+  if constexpr (KS) {
+    // Merge the two key halves: wave 0 of group 1 hands its base, partial
+    // sums and O^T to wave 0 of group 0 through the idle K ring, register by
+    // register (64 lanes x 4 bytes contiguous). Each half's O and l are
+    // relative to its own base m_w; those of all the keys are the sums of
+    // 2^(m_w - M) O_w and 2^(m_w - M) l_w, M the larger base (a half that
+    // admitted no key has m_w = -inf and weighs 0).
+    float* const xch = reinterpret_cast<float*>(kbuf);
+    static_assert((2 + 16 * DB) * 64 * 4 <= kRing * G::kBufBytes, "exchange fits the K ring");
+    if (live && grp == 1) {
+      xch[lane] = m_run;
+      xch[64 + lane] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(2 + 16 * db + i) * 64 + lane] = o[db][i];
+    }
+    __syncthreads();
+    if (live && grp == 0) {
+      const float m1 = xch[lane], l1 = xch[64 + lane];
+      const float mm = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+      l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * xch[(2 + 16 * db + i) * 64 + lane];
+      m_run = mm;
+    }
+  }
+  // rows this wave writes (key split: group 0's copy of the rows)
+  const bool out_ok = q_ok && (!KS || grp == 0);
+
   // ---- epilogue: normalise, LSE, store
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (p.splits > 1) {
     // this split's normalised rows and LSE, merged by attn_decode_merge_kernel;
     // workspace rows [split][b][h][q_row] (in decode mode h = kvh rep + hl)
-    if (q_ok) {
+    if (out_ok) {
       const size_t wrow = ((static_cast<size_t>(split) * p.B + b) * p.H + h) * p.Sq + q_row;
       float* const wo = p.ws_o + wrow * D;
 #pragma unroll
@@ -780,7 +826,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     }
     if (p.lse && g == 0 && q_ok)
       p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-  } else if (q_ok) {
+  } else if (out_ok) {
     __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
     const size_t orow = static_cast<size_t>(q_row) * p.o_sr;
 #pragma unroll
@@ -797,20 +843,20 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   }
 }
 
-template <int D, int MOD, bool DOCS, bool PACK>
+template <int D, int MOD, bool DOCS, int PACK>
 hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const int np = (p.Sq + kBM - 1) / kBM;
   const long long total = (PACK ? static_cast<long long>(p.B) * p.Hkv
                                 : static_cast<long long>(p.B) * p.H * np) * p.splits;
   const long long per = (total + kXcds - 1) / kXcds;
-  note_launch("attn_fwd_pp_kernel<%d, %d, %s, %s> grid %lld x %d splits %d", D, MOD, DOCS ? "true" : "false",
-              PACK ? "true" : "false", per * kXcds, kThreads, p.splits);
+  note_launch("attn_fwd_pp_kernel<%d, %d, %s, %d> grid %lld x %d splits %d", D, MOD, DOCS ? "true" : "false",
+              PACK, per * kXcds, kThreads, p.splits);
   hipLaunchKernelGGL((attn_fwd_pp_kernel<D, MOD, DOCS, PACK>), dim3(static_cast<unsigned>(per * kXcds)),
                      dim3(kThreads), 0, stream, p, p.kv_count, p.kv_list);
   return hipGetLastError();
 }
 
-template <int D, bool DOCS, bool PACK>
+template <int D, bool DOCS, int PACK>
 hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
   switch (p.mod_kind) {
     case kModNone: return launch_t<D, kModNone, DOCS, PACK>(p, stream);
@@ -821,11 +867,14 @@ hipError_t launch_mod(const FwdLaunch& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <bool PACK>
+template <int PACK>
 hipError_t launch_dims(const FwdLaunch& p, hipStream_t stream) {
   if (p.splits < 1) return hipErrorInvalidValue;
   const bool docs = p.mask_kind & kMaskDocument;
-  if (p.D == 256) return docs ? launch_mod<256, true, PACK>(p, stream) : launch_mod<256, false, PACK>(p, stream);
+  if (p.D == 256) {
+    if constexpr (PACK == 2) return hipErrorInvalidValue;
+    else return docs ? launch_mod<256, true, PACK>(p, stream) : launch_mod<256, false, PACK>(p, stream);
+  }
   if (p.D == 128) return docs ? launch_mod<128, true, PACK>(p, stream) : launch_mod<128, false, PACK>(p, stream);
   if (p.D == 64) return docs ? launch_mod<64, true, PACK>(p, stream) : launch_mod<64, false, PACK>(p, stream);
   return hipErrorInvalidValue;
@@ -893,13 +942,17 @@ hipError_t static_scratch(int device, void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<false>(p, stream); }
+hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<0>(p, stream); }
 
 // Split-KV: a group's rows packed into one workgroup when they fit (decode
-// mode), else the regular mapping with every query tile's list split.
+// mode; with at most 32 rows and D <= 128, the key halves of every stage
+// split between the two groups), else the regular mapping with every query
+// tile's list split.
 hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
-  const bool pack = static_cast<long long>(p.H / p.Hkv) * p.Sq <= kBM;
-  hipError_t e = pack ? launch_dims<true>(p, stream) : launch_dims<false>(p, stream);
+  const long long packed_rows = static_cast<long long>(p.H / p.Hkv) * p.Sq;
+  hipError_t e = packed_rows <= 32 && p.D <= 128 ? launch_dims<2>(p, stream)
+                 : packed_rows <= kBM            ? launch_dims<1>(p, stream)
+                                                 : launch_dims<0>(p, stream);
   if (e != hipSuccess || p.splits <= 1) return e;
   const long long n = static_cast<long long>(p.B) * p.Hkv * (p.H / p.Hkv) * p.Sq * (p.D / 4);
   note_launch("attn_decode_merge_kernel grid %lld x 256", (n + 255) / 256);

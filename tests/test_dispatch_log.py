@@ -104,13 +104,13 @@ def test_log_names_launched_kernels():
     ok = "-> 0 (success)"
     fwd = [ln for ln in lines if ln.startswith("[flexattn] flexattn_fwd(")]
     assert len(fwd) == 2 and all(ln.endswith(ok) for ln in fwd)
-    assert "attn_fwd_pp_kernel<128, 0, false, false> grid 8 x 512 splits 1" in fwd[0]
+    assert "attn_fwd_pp_kernel<128, 0, false, 0> grid 8 x 512 splits 1" in fwd[0]
     assert "block_mask=none" in fwd[0] and "block_mask=given" in fwd[1]
     bm = [ln for ln in lines if ln.startswith("[flexattn] flexattn_build_block_mask(")]
     assert len(bm) == 2 and all("block_mask_kernel grid 1 x 1 x 64" in ln and ln.endswith(ok) for ln in bm)
     dec = [ln for ln in lines if ln.startswith("[flexattn] flexattn_decode(")]
     assert len(dec) == 1 and dec[0].endswith(ok)
-    assert re.search(r"attn_fwd_pp_kernel<128, 0, false, true> grid \d+ x 512 splits 4; "
+    assert re.search(r"attn_fwd_pp_kernel<128, 0, false, 2> grid \d+ x 512 splits 4; "
                      r"attn_decode_merge_kernel grid \d+ x 256", dec[0]), dec[0]
     bwd = [ln for ln in lines if ln.startswith("[flexattn] flexattn_bwd(")]
     assert len(bwd) == 1 and bwd[0].endswith(ok)
