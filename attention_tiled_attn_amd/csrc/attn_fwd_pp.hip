@@ -115,12 +115,13 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 template <int D, int MOD, int PACK>
 constexpr int kWavesPerSimd = (D == 64 && !PACK && MOD != kModRelBias) ? 4 : 2;
 
-// PACK: 0 the regular mapping; 1 decode mode; 2 decode mode with at most 32
-// packed rows (D <= 128), whose rows sit in wave 0 of both groups: each of
-// the two waves takes one 32-key half of every stage with a running softmax
-// of its own, and the two are merged once after the loop. Both waves share
-// SIMD 0, so one's products overlap the other's softmax, where with the rows
-// in one wave a stage costs that wave's matrix and vector work back to back.
+// PACK: 0 the regular mapping; 1 decode mode; 2 decode mode with at most 128
+// packed rows (D <= 128), which sit in the waves of both groups alike: wave
+// w of group 0 and wave w of group 1 (one SIMD) hold the same 32 rows and
+// each takes one 32-key half of every stage with a running softmax of its
+// own; the two are merged once after the loop. One wave's products then
+// overlap its partner's softmax, where with the rows in one group a stage
+// costs each wave's matrix and vector work back to back.
 template <int D, int MOD, bool DOCS, int PACK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, MOD, PACK>, kWavesPerSimd<D, MOD, PACK>)))
@@ -737,14 +738,16 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   if (!kInPhase && grp == 0) __syncthreads();   // matches group 1's extra barrier
 
   if constexpr (KS) {
-    // Merge the two key halves: wave 0 of group 1 hands its base, partial
-    // sums and O^T to wave 0 of group 0 through the idle K ring, register by
-    // register (64 lanes x 4 bytes contiguous). Each half's O and l are
-    // relative to its own base m_w; those of all the keys are the sums of
-    // 2^(m_w - M) O_w and 2^(m_w - M) l_w, M the larger base (a half that
-    // admitted no key has m_w = -inf and weighs 0).
-    float* const xch = reinterpret_cast<float*>(kbuf);
-    static_assert((2 + 16 * DB) * 64 * 4 <= kRing * G::kBufBytes, "exchange fits the K ring");
+    // Merge the two key halves: each wave of group 1 hands its base, partial
+    // sums and O^T to its partner in group 0 through the idle stage rings
+    // (waves 0, 1 in the K ring, 2, 3 in the V ring), register by register
+    // (64 lanes x 4 bytes contiguous). Each half's O and l are relative to
+    // its own base m_w; those of all the keys are the sums of 2^(m_w - M) O_w
+    // and 2^(m_w - M) l_w, M the larger base (a half that admitted no key
+    // has m_w = -inf and weighs 0).
+    constexpr int XW = (2 + 16 * DB) * 64;   // floats per wave
+    static_assert(2 * XW * 4 <= kRing * G::kBufBytes, "exchange fits the stage rings");
+    float* const xch = reinterpret_cast<float*>(wq < 2 ? kbuf : vbuf) + (wq & 1) * XW;
     if (live && grp == 1) {
       xch[lane] = m_run;
       xch[64 + lane] = l_run;
@@ -945,12 +948,12 @@ hipError_t static_scratch(int device, void** ptr) {
 hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<0>(p, stream); }
 
 // Split-KV: a group's rows packed into one workgroup when they fit (decode
-// mode; with at most 32 rows and D <= 128, the key halves of every stage
+// mode; with at most 128 rows and D <= 128, the key halves of every stage
 // split between the two groups), else the regular mapping with every query
 // tile's list split.
 hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
   const long long packed_rows = static_cast<long long>(p.H / p.Hkv) * p.Sq;
-  hipError_t e = packed_rows <= 32 && p.D <= 128 ? launch_dims<2>(p, stream)
+  hipError_t e = packed_rows <= kPairHalf && p.D <= 128 ? launch_dims<2>(p, stream)
                  : packed_rows <= kBM            ? launch_dims<1>(p, stream)
                                                  : launch_dims<0>(p, stream);
   if (e != hipSuccess || p.splits <= 1) return e;
