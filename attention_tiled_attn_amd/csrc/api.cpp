@@ -413,9 +413,18 @@ int flexattn_decode_splits(int B, int Hkv, int Skv) {
   if (B < 1 || Hkv < 1 || Skv < 1) return 1;
   const long long tiles = ceil_div(Skv, FLEXATTN_TILE);
   const long long groups = static_cast<long long>(B) * Hkv;
-  long long s = (2 * 256 + groups - 1) / groups;   // about two workgroups per CU
-  s = std::min<long long>(s, std::max<long long>(1, tiles / 4));
-  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, 64)));
+  const long long cap = std::max<long long>(1, std::min<long long>(tiles / 4, 64));
+  // A workgroup takes ~(2 tiles / s + 3) stage times (two 64-key stages per
+  // tile, ~3 stages of start and drain), and ceil(groups * s / 256) rounds
+  // of workgroups run one after another: minimise their product, the
+  // smallest s among equals.
+  auto cost = [&](long long s) {
+    return static_cast<double>((groups * s + 255) / 256) * (2.0 * static_cast<double>(tiles) / s + 3.0);
+  };
+  long long best = 1;
+  for (long long s = 2; s <= cap; ++s)
+    if (cost(s) < cost(best)) best = s;
+  return static_cast<int>(best);
 }
 
 int flexattn_split_count(int B, int H, int Hkv, int Sq, int Skv) {

@@ -257,9 +257,13 @@ int flexattn_fwd(const void* q, const void* k, const void* v, void* out, float* 
  * Results equal flexattn_fwd's up to float32 rounding in the merge. */
 size_t flexattn_decode_workspace_bytes(int B, int H, int Hkv, int Sq, int D, int splits);
 
-/* A split count for packed decoding (rep * Sq <= 256) that gives the chip at
- * least ~2 workgroups per CU while leaving each at least 4 key tiles (128
- * keys each). */
+/* A split count for packed decoding (rep * Sq <= 256): a decode-mode
+ * workgroup fills a CU, so B * Hkv * splits workgroups run in
+ * ceil(B * Hkv * splits / 256) rounds, each taking about 2 * tiles / splits
+ * + 3 stage times (tiles = ceil(Skv / 128), two stages per tile, ~3 stages
+ * of start and drain per workgroup). The count minimises that product (the
+ * fewest splits among equals), at most 64 and leaving each split at least
+ * 4 key tiles. */
 int flexattn_decode_splits(int B, int Hkv, int Skv);
 
 /* A split count for flexattn_decode in either organisation: the packed rule

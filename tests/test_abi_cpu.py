@@ -300,8 +300,11 @@ def test_decode_workspace_and_splits():
     assert fa.flexattn_decode_workspace_bytes(2, 8, 2, 3, 128, 1) == 0
     for bad in [(0, 8, 2, 1, 128, 2), (1, 8, 3, 1, 128, 2), (1, 8, 2, 1, 96, 2), (1, 8, 2, 1, 64, 65)]:
         assert fa.flexattn_decode_workspace_bytes(*bad) == 0
-    # about two workgroups per CU, at least 4 key tiles each, at most 64
-    assert fa.flexattn_decode_splits(16, 8, 32768) == 4
+    # rounds of 256 workgroups x (2 tiles / s + 3) stage times, minimised;
+    # at least 4 key tiles each, at most 64
+    assert fa.flexattn_decode_splits(16, 8, 32768) == 2       # 128 groups: one round of 256
+    assert fa.flexattn_decode_splits(100, 1, 65536) == 5      # 500 workgroups in 2 rounds
+    assert fa.flexattn_decode_splits(3, 1, 65536) == 64
     assert fa.flexattn_decode_splits(1, 1, 1 << 20) == 64
     assert fa.flexattn_decode_splits(1, 8, 1024) == 2
     assert fa.flexattn_decode_splits(64, 8, 8192) == 1
