@@ -182,7 +182,7 @@ template <int D> constexpr int kDqStage = 32;
 template <int D> constexpr int kDkvStage = D == 256 ? 32 : 64;
 // waves per SIMD; at D = 64 three dQ workgroups share a CU (registers under
 // 168 and 41-45 KB of LDS each): alibi_d64 backward +2.7%, doc_swa at D = 64
-// +6% against two (A/B on one box)
+// +6% against two (A/B on one machine)
 template <int D> constexpr int kDqWaves = D == 256 ? 1 : D == 64 ? 3 : 2;
 
 // dQ (and delta)

@@ -108,7 +108,7 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 // Waves per SIMD: 2 (one workgroup per CU), or 4 (two workgroups per CU) at
 // D = 64, where a wave fits 128 registers and a workgroup ~57 KB of LDS. There
 // the softmax outweighs the products, and the other workgroup's waves add
-// vector issue slots (A/B on one box: alibi_d64 +12%, softcap_d64 +18%, doc_swa
+// vector issue slots (A/B on one machine: alibi_d64 +12%, softcap_d64 +18%, doc_swa
 // at D = 64 +29%, dense at D = 64 +6%). Not with the relative-bias table or in
 // decode mode, whose registers do not fit 128 without spilling (6% and 11%
 // slower measured).
@@ -679,7 +679,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // Group 1 runs one slot behind (ping-pong), except at D = 256: its stages
   // hold 32 keys, so a wave's softmax is half as long as its matrix slot, and
   // the two waves of a SIMD do better taking the matrix cores back to back and
-  // exponentiating together (A/B on one box: 825 -> 952 TFLOPS on the causal
+  // exponentiating together (A/B on one machine: 825 -> 952 TFLOPS on the causal
   // GQA workload at D = 256; 14% slower at D = 64 and 128).
   constexpr bool kInPhase = D == 256;
   if (!kInPhase && grp == 1) __syncthreads();

@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -78,10 +79,16 @@ def admitted_pairs(wl, doc_ids) -> int:
 
 
 def kernel_sha() -> str:
+    """Hash of the forward kernel's sources with comments and blank lines
+    dropped, so that it changes with the code, not with its commentary."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
@@ -219,7 +226,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; sharding is design-only",
+        print(json.dumps({"error": "this library runs on one GPU only; sharding is design-only",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
