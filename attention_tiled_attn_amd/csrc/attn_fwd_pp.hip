@@ -113,21 +113,24 @@ __device__ inline int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1
 // decode mode, whose registers do not fit 128 without spilling (6% and 11%
 // slower measured).
 template <int D, int MOD, int PACK>
-constexpr int kWavesPerSimd = (D == 64 && !PACK && MOD != kModRelBias) ? 4 : 2;
+constexpr int kWavesPerSimd = (D == 64 && PACK == 0 && MOD != kModRelBias) ? 4 : 2;
 
 // PACK: 0 the regular mapping; 1 decode mode; 2 decode mode with at most 128
-// packed rows (D <= 128), which sit in the waves of both groups alike: wave
-// w of group 0 and wave w of group 1 (one SIMD) hold the same 32 rows and
-// each takes one 32-key half of every stage with a running softmax of its
-// own; the two are merged once after the loop. One wave's products then
-// overlap its partner's softmax, where with the rows in one group a stage
-// costs each wave's matrix and vector work back to back.
+// packed rows (D <= 128); 3 the regular mapping when Sq <= 128 (D <= 128).
+// In modes 2 and 3 (key split) the rows sit in the waves of both groups
+// alike: wave w of group 0 and wave w of group 1 (one SIMD) hold the same 32
+// rows and each takes one 32-key half of every stage with a running softmax
+// of its own; the two are merged once after the loop. One wave's products
+// then overlap its partner's softmax, where with the rows in one group a
+// stage costs each wave's matrix and vector work back to back (and, in the
+// regular mapping, the other group works on padding rows).
 template <int D, int MOD, bool DOCS, int PACK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, MOD, PACK>, kWavesPerSimd<D, MOD, PACK>)))
 void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int* __restrict__ kv_list) {
   using G = PGeo<D>;
-  constexpr bool KS = PACK == 2;   // key halves split between the groups
+  constexpr bool KS = PACK == 2 || PACK == 3;   // key halves split between the groups
+  constexpr bool PK = PACK == 1 || PACK == 2;   // packed rows (decode mode)
   static_assert(!KS || D <= 128, "key split needs 64-key stages");
   constexpr int DC = D / 16;   // 16-wide d chunks (k-steps of S^T)
   constexpr int DB = D / 32;   // 32-row d blocks of O^T
@@ -150,8 +153,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // ---- workgroup -> (b, h, 256-row tile[, split]): XCD-contiguous, heavy
   // tiles first; decode mode: (b, key/value head, split)
   const int rep = p.H / p.Hkv;
-  const int np = PACK ? 1 : (p.Sq + kBM - 1) / kBM;
-  const int total = (PACK ? p.B * p.Hkv : p.B * p.H * np) * p.splits;
+  const int np = PK ? 1 : (p.Sq + kBM - 1) / kBM;
+  const int total = (PK ? p.B * p.Hkv : p.B * p.H * np) * p.splits;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int wg = blockIdx.x;
   const int lin = (wg % kXcds) * per_xcd + wg / kXcds;
@@ -159,12 +162,12 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // split-KV (p.splits > 1): the splits of one item are consecutive
   const int split = lin % p.splits;
   const int item = lin / p.splits;
-  int qp = PACK ? 0 : np - 1 - (item % np);
+  int qp = PK ? 0 : np - 1 - (item % np);
   int slice = item / np;   // (b, h) of the regular kernel
   // length and first entry of the item's key-tile list when the mapping
   // below has fetched them (n_head < 0: not fetched)
   int n_head = -1, e_head = 0;
-  if constexpr (DOCS && !PACK) {
+  if constexpr (DOCS && !PK) {
     // Document masks make the work of a slice's query tiles uneven. When the
     // slices split evenly over the XCDs, each XCD takes its slices' items
     // longest first (most key tiles; ties: the later tile), rank-major over
@@ -205,27 +208,28 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       __syncthreads();   // the keys are read before the list overwrites them
     }
   }
-  const int b = PACK ? item / p.Hkv : slice / p.H;
-  const int kvh = PACK ? item % p.Hkv : (slice % p.H) / rep;
+  const int b = PK ? item / p.Hkv : slice / p.H;
+  const int kvh = PK ? item % p.Hkv : (slice % p.H) / rep;
   // this lane's row: packed index r (decode mode), its query head and row
   const int r_lane = (KS ? 0 : grp * kPairHalf) + wq * 32 + l32;
-  const int hl = PACK ? min(r_lane / p.Sq, rep - 1) : 0;
-  const int h = PACK ? kvh * rep + hl : slice % p.H;   // lane-varying in decode mode
-  const int q_row = PACK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
-  const bool q_ok = PACK ? r_lane < rep * p.Sq : q_row < p.Sq;
+  const int hl = PK ? min(r_lane / p.Sq, rep - 1) : 0;
+  const int h = PK ? kvh * rep + hl : slice % p.H;   // lane-varying in decode mode
+  const int q_row = PK ? r_lane - hl * p.Sq : qp * kBM + r_lane;
+  const bool q_ok = PK ? r_lane < rep * p.Sq : q_row < p.Sq;
   // decode mode: a wave whose 32 rows all lie past the packed rows only
   // copies and keeps the barriers (wave-uniform, fixed for the whole loop)
-  const bool live = !PACK || __builtin_amdgcn_readfirstlane(r_lane - l32) < rep * p.Sq;
+  const bool live = PACK == 3 ? __builtin_amdgcn_readfirstlane(q_row - l32) < p.Sq
+                               : !PK || __builtin_amdgcn_readfirstlane(r_lane - l32) < rep * p.Sq;
   const size_t q_head = (static_cast<size_t>(b) * p.H + h) * p.Sq;   // LSE rows
   // row strides in bytes; a (batch, head) slice spans rows 0 .. S - 1, so
   // rows past the end read as zero (decode mode: the slices of the group's
   // heads, from its first head)
   const unsigned qrb = static_cast<unsigned>(p.q_sr) * 2u;
   const unsigned grb = static_cast<unsigned>(grp ? p.v_sr : p.k_sr) * 2u;   // this group's K or V
-  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.q_sb + (PACK ? kvh * rep : h) * p.q_sh;
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.q_sb + (PK ? kvh * rep : h) * p.q_sh;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.v_sb + kvh * p.v_sh;
-  const unsigned q_bytes = PACK ? static_cast<unsigned>((rep - 1) * p.q_sh * 2 + (p.Sq - 1) * qrb + RB)
+  const unsigned q_bytes = PK ? static_cast<unsigned>((rep - 1) * p.q_sh * 2 + (p.Sq - 1) * qrb + RB)
                                 : static_cast<unsigned>(p.Sq - 1) * qrb + RB;
   const rsrc_t rq = make_rsrc(qbase, q_bytes);
   const unsigned kv_bytes = static_cast<unsigned>(p.Skv - 1) * grb + RB;
@@ -250,7 +254,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   constexpr bool kDesc = MOD == kModAlibi;
   // the whole list, from its head: the first copies start before it is
   // staged (ascending order only: the descending order starts at its tail)
-  const bool early = !PACK && p.splits == 1 && !kDesc;
+  const bool early = !PK && p.splits == 1 && !kDesc;
   if (!early || n_head < 0) {
     if (kv_count) n_entries = kv_count[bm_b * p.nq + qp];
     if (early && list) {
@@ -270,7 +274,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   // Q^T fragments (B operand of S^T): rows past Sq (and, in decode mode,
   // packed rows past the group) read as zero
   const unsigned q_off = !q_ok ? 0x80000000u
-                         : PACK ? static_cast<unsigned>(hl * p.q_sh * 2) + static_cast<unsigned>(q_row) * qrb
+                         : PK ? static_cast<unsigned>(hl * p.q_sh * 2) + static_cast<unsigned>(q_row) * qrb
                                 : static_cast<unsigned>(q_row) * qrb;
   bf16x8 qf[DC];
 #pragma unroll
@@ -359,7 +363,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     e_first = static_cast<int>(static_cast<long long>(n_all) * split / p.splits);
     n_entries = static_cast<int>(static_cast<long long>(n_all) * (split + 1) / p.splits) - e_first;
   }
-  if constexpr (PACK) {
+  if constexpr (PK) {
     // every packed row lies in query tile 0, so a tile is visited when
     // either half admits a pair, and skips the per-element mask only when
     // both halves are full (half 1 has no rows when Sq <= 128)
@@ -381,8 +385,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
   if constexpr (MOD == kModRelBias) {
     // decode mode: the tables of all rep heads of the group, one after another
     const int n_tab = 2 * p.va.rel_max + 1;
-    const int h0 = PACK ? kvh * rep : __builtin_amdgcn_readfirstlane(h);
-    for (int j = 0; j < (PACK ? rep : 1); ++j)
+    const int h0 = PK ? kvh * rep : __builtin_amdgcn_readfirstlane(h);
+    for (int j = 0; j < (PK ? rep : 1); ++j)
       stage_rel_table(p.va, h0 + j, (lds_f32*)(rtab) + j * n_tab, tid, kThreads);
   }
   __syncthreads();
@@ -494,8 +498,8 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
     if constexpr (MOD == kModRelBias) {
       // the wave's rows lie in [qw, qw + span]: lane 0 holds the first of 32
       // consecutive rows; in decode mode any row of query tile 0
-      const int qw = PACK ? p.va.q_offset : __builtin_amdgcn_readfirstlane(q_pos);
-      const int span = PACK ? p.Sq - 1 : 31;
+      const int qw = PK ? p.va.q_offset : __builtin_amdgcn_readfirstlane(q_pos);
+      const int span = PK ? p.Sq - 1 : 31;
       const int R = p.va.rel_max;
       const bool below = kv0 + kBW - 1 - qw < -R;   // largest distance below -R
       const bool above = kv0 - (qw + span) > R;     // smallest distance above R
@@ -686,7 +690,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 
   int e_prev = 0, e_cur = ent(0), e_next = ent(1);
   int ring = 0;   // ring slot of stage u (u % 3); stage u - 1 and u + 2 share slot (u + 2) % 3
-  const int sh = 2 * grp;
+  const int sh = PACK == 3 ? 0 : 2 * grp;   // mode 3: every row lies in half 0
   for (int u = 0; u < T; ++u) {
     const int ring_old = ring == 0 ? kRing - 1 : ring - 1;
     const int ec = __builtin_amdgcn_readfirstlane(e_cur) >> sh;
@@ -769,6 +773,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * xch[(2 + 16 * db + i) * 64 + lane];
       m_run = mm;
     }
+    __syncthreads();   // the exchange is read before the epilogue reuses the rings
   }
   // rows this wave writes (key split: group 0's copy of the rows)
   const bool out_ok = q_ok && (!KS || grp == 0);
@@ -793,7 +798,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
         }
       if (g == 0) p.ws_lse[wrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
-  } else if constexpr (!PACK) {
+  } else if constexpr (!PK) {
     // O through LDS: each wave writes its 32 rows row-major into the idle
     // stage buffers (16-byte chunks XOR-permuted by row, so neither side has
     // bank conflicts) and stores whole rows, 16 bytes per lane. A store then
@@ -822,12 +827,12 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
       for (int j = 0; j < 32 / RPI; ++j) {
         const int r = j * RPI + lane / CPP, c = lane % CPP;
         const u32x4 w = *reinterpret_cast<const u32x4*>(stg + r * DP * 2 + ((c ^ (r % CPP)) * 16));
-        if (row0 + r < p.Sq)
+        if (row0 + r < p.Sq && (!KS || grp == 0))
           *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(row0 + r) * p.o_sr + ps * DP + c * 8) = w;
       }
       if (ps + 1 < D / DP) __syncthreads();   // read back before the next pass overwrites
     }
-    if (p.lse && g == 0 && q_ok)
+    if (p.lse && g == 0 && out_ok)
       p.lse[q_head + q_row] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
   } else if (out_ok) {
     __bf16* const obase = static_cast<__bf16*>(p.out) + b * p.o_sb + h * p.o_sh;
@@ -849,7 +854,7 @@ void attn_fwd_pp_kernel(FwdLaunch p, const int* __restrict__ kv_count, const int
 template <int D, int MOD, bool DOCS, int PACK>
 hipError_t launch_t(const FwdLaunch& p, hipStream_t stream) {
   const int np = (p.Sq + kBM - 1) / kBM;
-  const long long total = (PACK ? static_cast<long long>(p.B) * p.Hkv
+  const long long total = ((PACK == 1 || PACK == 2) ? static_cast<long long>(p.B) * p.Hkv
                                 : static_cast<long long>(p.B) * p.H * np) * p.splits;
   const long long per = (total + kXcds - 1) / kXcds;
   note_launch("attn_fwd_pp_kernel<%d, %d, %s, %d> grid %lld x %d splits %d", D, MOD, DOCS ? "true" : "false",
@@ -875,7 +880,7 @@ hipError_t launch_dims(const FwdLaunch& p, hipStream_t stream) {
   if (p.splits < 1) return hipErrorInvalidValue;
   const bool docs = p.mask_kind & kMaskDocument;
   if (p.D == 256) {
-    if constexpr (PACK == 2) return hipErrorInvalidValue;
+    if constexpr (PACK >= 2) return hipErrorInvalidValue;
     else return docs ? launch_mod<256, true, PACK>(p, stream) : launch_mod<256, false, PACK>(p, stream);
   }
   if (p.D == 128) return docs ? launch_mod<128, true, PACK>(p, stream) : launch_mod<128, false, PACK>(p, stream);
@@ -945,7 +950,11 @@ hipError_t static_scratch(int device, void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) { return launch_dims<0>(p, stream); }
+// Sq <= 128 (every row in the first half of the one query tile) and D <= 128
+// take the key split
+hipError_t launch_attn_fwd_pp(const FwdLaunch& p, hipStream_t stream) {
+  return p.Sq <= kPairHalf && p.D <= 128 ? launch_dims<3>(p, stream) : launch_dims<0>(p, stream);
+}
 
 // Split-KV: a group's rows packed into one workgroup when they fit (decode
 // mode; with at most 128 rows and D <= 128, the key halves of every stage
@@ -955,7 +964,7 @@ hipError_t launch_attn_decode(const FwdLaunch& p, hipStream_t stream) {
   const long long packed_rows = static_cast<long long>(p.H / p.Hkv) * p.Sq;
   hipError_t e = packed_rows <= kPairHalf && p.D <= 128 ? launch_dims<2>(p, stream)
                  : packed_rows <= kBM            ? launch_dims<1>(p, stream)
-                                                 : launch_dims<0>(p, stream);
+                                                 : launch_attn_fwd_pp(p, stream);
   if (e != hipSuccess || p.splits <= 1) return e;
   const long long n = static_cast<long long>(p.B) * p.Hkv * (p.H / p.Hkv) * p.Sq * (p.D / 4);
   note_launch("attn_decode_merge_kernel grid %lld x 256", (n + 255) / 256);
