@@ -113,6 +113,9 @@ TILE_SPLIT_CASES = [
     dict(B=1, H=2, S=600, causal=True, prefix=200, mod="relbias", rel_max=50),
     dict(B=1, H=2, S=520, D=256, causal=True),
     dict(B=1, H=2, S=400, D=128),
+    # Sq <= 128 with rep * Sq > 256: the split lists of the key-split mapping
+    dict(B=1, H=8, Hkv=2, Sq=100, Skv=1500, q_offset=1400, causal=True, D=128),
+    dict(B=2, H=4, Hkv=1, Sq=128, Skv=900, q_offset=772, causal=True, documents=True, mod="alibi"),
 ]
 
 
